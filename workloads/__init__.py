@@ -1,0 +1,16 @@
+"""Seeded synthetic inputs for paged MLA decode.
+
+This package only draws random numbers and lays them out in the cache formats
+(page pool, block table, sequence lengths, BF16 rows, 656-byte FP8 records).
+It holds none of the attention arithmetic: both the CPU oracle (test side)
+and the HIP library consume what it produces.
+"""
+from .gen import (  # noqa: F401
+    Workload,
+    WORKLOAD_SPECS,
+    make_workload,
+    named_workload,
+    poison_unused,
+    permute_pages,
+    quantize_fp8_records,
+)
