@@ -1,0 +1,226 @@
+"""Paged MLA decode for MI355X (gfx950): thin Python binding over libmla.so.
+
+Two calls, named after the C ABI in include/mla.h:
+
+    tile_metadata, num_splits = mla_get_metadata(cache_seqlens, s_q * h_q // h_kv, h_kv)
+    o, lse = mla_decode_kvcache(q, kvcache, block_table, cache_seqlens, dv,
+                                tile_metadata, num_splits, causal=True)
+
+(the call pattern of FlashMLA's get_mla_metadata / flash_mla_with_kvcache:
+"功能 1" on the kdjingpai.com post). PyTorch supplies device memory and the
+current stream; every step of the computation runs in the HIP library. If the
+library is not built, importing the calls raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import D_QK, D_V, FP8_RECORD_BYTES, META_INTS, PAGE_TOKENS, MlaDecodeArgs, MlaError
+
+__all__ = [
+    "mla_get_metadata", "mla_decode_kvcache", "mla_workspace_bytes", "mla_num_parts", "MlaDecoder",
+    "MlaError", "kv_format_of", "library_path",
+]
+
+_FORMATS = {"bf16": _lib.MLA_KV_BF16, "fp8": _lib.MLA_KV_FP8_E4M3}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _fmt_code(kv_format) -> int:
+    if isinstance(kv_format, int):
+        return kv_format
+    try:
+        return _FORMATS[kv_format]
+    except KeyError:
+        raise ValueError(f"kv_format must be 'bf16' or 'fp8', got {kv_format!r}") from None
+
+
+def kv_format_of(kvcache: torch.Tensor) -> str:
+    if kvcache.dtype == torch.bfloat16 and kvcache.shape[-1] == D_QK:
+        return "bf16"
+    if kvcache.dtype == torch.uint8 and kvcache.shape[-1] == FP8_RECORD_BYTES:
+        return "fp8"
+    raise ValueError(f"kvcache must be bf16 [..., {D_QK}] or uint8 FP8 records [..., {FP8_RECORD_BYTES}], "
+                     f"got {kvcache.dtype} {tuple(kvcache.shape)}")
+
+
+def mla_num_parts(batch: int, heads_per_kv: int, h_kv: int = 1, kv_format="bf16", num_cus: int = 0) -> int:
+    lib = _lib.load()
+    n = lib.mla_num_parts(int(batch), int(heads_per_kv), int(h_kv), _fmt_code(kv_format), int(num_cus))
+    if n < 0:
+        raise ValueError(_lib.last_error())
+    return n
+
+
+def mla_workspace_bytes(batch: int, num_parts: int, heads_per_kv: int, h_kv: int = 1) -> int:
+    return int(_lib.load().mla_workspace_bytes(int(batch), int(num_parts), int(heads_per_kv), int(h_kv)))
+
+
+def _i32p(t: torch.Tensor):
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_int32))
+
+
+def mla_get_metadata_host(cache_seqlens_host: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *,
+                          kv_format="bf16", num_parts: int = 0, num_cus: int = 0,
+                          pin: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Host tile scheduler: int32 CPU tensors (tile_metadata [P, 8], num_splits [B + 1])."""
+    lib = _lib.load()
+    L = cache_seqlens_host
+    if L.device.type != "cpu":
+        L = L.cpu()
+    L = L.to(torch.int32).contiguous()
+    if L.dim() != 1:
+        raise ValueError("cache_seqlens must be 1-D [batch]")
+    B = int(L.shape[0])
+    fmt = _fmt_code(kv_format)
+    parts = int(num_parts)
+    if parts == 0:
+        parts = lib.mla_num_parts(B, int(heads_per_kv), int(h_kv), fmt, int(num_cus))
+        if parts < 0:
+            raise ValueError(_lib.last_error())
+    meta = torch.empty((parts, META_INTS), dtype=torch.int32, pin_memory=pin)
+    splits = torch.empty((B + 1,), dtype=torch.int32, pin_memory=pin)
+    got = ctypes.c_int(0)
+    _lib.check(lib.mla_get_metadata(_i32p(L), B, int(heads_per_kv), int(h_kv), fmt, int(num_cus), parts,
+                                    _i32p(meta), _i32p(splits), ctypes.byref(got)))
+    return meta, splits
+
+
+def mla_get_metadata(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *, kv_format="bf16",
+                     num_parts: int = 0, num_cus: int = 0,
+                     device: Optional[torch.device] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tile-scheduler metadata for one decode step, on `device` (default: the device of
+    cache_seqlens, or the current CUDA device for a CPU tensor). Reuse it for every layer.
+    A device-resident cache_seqlens is read back to the host (a synchronising copy)."""
+    if device is None:
+        device = cache_seqlens.device if cache_seqlens.device.type != "cpu" else torch.device("cuda")
+    pin = torch.device(device).type == "cuda"
+    meta, splits = mla_get_metadata_host(cache_seqlens, heads_per_kv, h_kv, kv_format=kv_format,
+                                         num_parts=num_parts, num_cus=num_cus, pin=pin)
+    return meta.to(device, non_blocking=True), splits.to(device, non_blocking=True)
+
+
+def _check_tensor(name, t, dtype, ndim, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+class MlaDecoder:
+    """A decode call with its argument block marshalled once.
+
+    Holds references to every tensor it points at; `run()` launches on the
+    current (or given) stream. Use it when the same buffers are decoded
+    repeatedly (one per layer of a decode step, or a benchmark loop)."""
+
+    def __init__(self, q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal=False,
+                 softmax_scale=None, *, out=None, lse=None, workspace=None, events=None):
+        dev = q.device
+        if dev.type != "cuda":
+            raise ValueError("q must be a CUDA (HIP) tensor")
+        fmt = kv_format_of(kvcache)
+        _check_tensor("q", q, torch.bfloat16, 4, dev)
+        _check_tensor("kvcache", kvcache, kvcache.dtype, 4, dev)
+        _check_tensor("block_table", block_table, torch.int32, 2, dev)
+        _check_tensor("cache_seqlens", cache_seqlens, torch.int32, 1, dev)
+        _check_tensor("tile_metadata", tile_metadata, torch.int32, 2, dev)
+        _check_tensor("num_splits", num_splits, torch.int32, 1, dev)
+        if q.stride(-1) != 1 or kvcache.stride(-1) != 1 or block_table.stride(-1) != 1:
+            raise ValueError("q, kvcache and block_table need a contiguous last dimension")
+        if not (cache_seqlens.is_contiguous() and tile_metadata.is_contiguous() and num_splits.is_contiguous()):
+            raise ValueError("cache_seqlens, tile_metadata and num_splits must be contiguous")
+        if tile_metadata.shape[1] != META_INTS:
+            raise ValueError(f"tile_metadata must be [num_parts, {META_INTS}]")
+        B, S, H, D = q.shape
+        Hk = int(kvcache.shape[2])
+        if kvcache.shape[1] != PAGE_TOKENS:
+            raise ValueError(f"kvcache pages must hold {PAGE_TOKENS} tokens")
+        if num_splits.shape[0] != B + 1 or cache_seqlens.shape[0] != B or block_table.shape[0] != B:
+            raise ValueError("cache_seqlens [batch], block_table [batch, n] and num_splits [batch + 1] must agree with q")
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(D)
+        rows = S * H // max(Hk, 1)
+        parts = int(tile_metadata.shape[0])
+        if out is None:
+            out = torch.empty((B, S, H, int(dv)), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        _check_tensor("out", out, torch.bfloat16, 4, dev)
+        _check_tensor("lse", lse, torch.float32, 3, dev)
+        if not (out.is_contiguous() and lse.is_contiguous()):
+            raise ValueError("out and lse must be contiguous")
+        if tuple(out.shape) != (B, S, H, int(dv)) or tuple(lse.shape) != (B, H, S):
+            raise ValueError("out must be [batch, s_q, h_q, dv] and lse [batch, h_q, s_q]")
+        need = mla_workspace_bytes(B, parts, rows, Hk) if H % max(Hk, 1) == 0 else 0
+        if workspace is None:
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+        self.tensors = (q, kvcache, block_table, cache_seqlens, tile_metadata, num_splits, out, lse, workspace)
+        self.out, self.lse, self.workspace = out, lse, workspace
+        a = MlaDecodeArgs()
+        a.q = q.data_ptr()
+        a.q_stride[:] = [q.stride(0), q.stride(1), q.stride(2)]
+        a.kvcache = kvcache.data_ptr()
+        a.kv_stride[:] = [kvcache.stride(0), kvcache.stride(1), kvcache.stride(2)]
+        a.kv_format = _FORMATS[fmt]
+        a.num_pages = int(kvcache.shape[0])
+        a.block_table = block_table.data_ptr()
+        a.bt_stride = block_table.stride(0)
+        a.max_blocks_per_seq = int(block_table.shape[1])
+        a.cache_seqlens = cache_seqlens.data_ptr()
+        a.tile_metadata = tile_metadata.data_ptr()
+        a.num_parts = parts
+        a.num_splits = num_splits.data_ptr()
+        a.batch, a.s_q, a.h_q, a.h_kv = B, S, H, Hk
+        a.d_qk, a.dv = int(D), int(dv)
+        a.causal = 1 if causal else 0
+        a.softmax_scale = float(softmax_scale)
+        a.o = out.data_ptr()
+        a.lse = lse.data_ptr()
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+        self.args = a
+        if events is not None:
+            self.set_events(events)
+        self._args_ref = ctypes.byref(a)
+        self._lib = _lib.load()
+        self.device = dev
+
+    def set_events(self, events: Sequence) -> None:
+        """Timing hooks: three raw hipEvent_t handles (ints) or None."""
+        for i in range(3):
+            e = events[i] if i < len(events) else None
+            self.args.events[i] = None if e is None else int(e)
+
+    def run(self, stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        _lib.check(self._lib.mla_decode_kvcache(self._args_ref, ctypes.c_void_p(s.cuda_stream)))
+        return self.out, self.lse
+
+
+def mla_decode_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                       dv: int, tile_metadata: torch.Tensor, num_splits: torch.Tensor, causal: bool = False,
+                       softmax_scale: Optional[float] = None, *, out=None, lse=None,
+                       workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """o [batch, s_q, h_q, dv] bf16 and lse [batch, h_q, s_q] fp32 for one layer.
+
+    q bf16 [batch, s_q, h_q, 576]; kvcache bf16 [pages, 64, h_kv, 576] or uint8
+    FP8 records [pages, 64, h_kv, 656]; block_table int32 [batch, max_blocks];
+    cache_seqlens int32 [batch]; tile_metadata / num_splits from mla_get_metadata
+    for these lengths. causal: query token s of s_q reads keys t <= L - s_q + s.
+    softmax_scale defaults to 1/sqrt(576)."""
+    dec = MlaDecoder(q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal, softmax_scale,
+                     out=out, lse=lse, workspace=workspace)
+    return dec.run()

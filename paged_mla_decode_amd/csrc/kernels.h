@@ -1,0 +1,39 @@
+// kernels.h -- the validated argument block the HIP kernels receive.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace mla {
+
+struct DecodeParams {
+  const uint16_t* q;          // bf16 bits
+  int64_t q_sb, q_ss, q_sh;   // element strides: batch, query token, head
+  const uint8_t* kv;          // cache base (bytes)
+  int64_t kv_sp, kv_st, kv_sh;  // byte strides: page, token, head
+  int num_pages;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int max_blocks;
+  const int32_t* seqlens;
+  const int32_t* meta;
+  int num_parts;
+  const int32_t* num_splits;
+  int batch, s_q, h_q, h_kv, group, rows;  // group = h_q / h_kv, rows = s_q * group
+  int causal;
+  float scale_log2;           // softmax_scale * log2(e)
+  uint16_t* o;                // bf16 bits [batch, s_q, h_q, 512]
+  float* lse;                 // [batch, h_q, s_q]
+  float* part_o;              // [slots, h_kv, rows, 512]
+  float* part_lse;            // [slots, h_kv, rows]
+  int max_slots;
+  int grid_wgs;               // real workgroups of the split kernel (the grid is padded to a multiple of 8)
+};
+
+hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
+                         void* const events[3]);
+
+}  // namespace mla

@@ -1,0 +1,68 @@
+// plan.h -- launch plan shared by the host scheduler and the kernel launcher.
+//
+// The split-KV kernel runs 4 wavefronts per workgroup. Each wavefront owns a
+// block of 16 query rows (rows = s_q * h_q / h_kv per KV head, the head fold of
+// the deepseekonline.chat day-1 post, "Dynamische Sequenzoptimierung") and a
+// group of the 64 tokens of every page it visits:
+//   rb = 16-row blocks per workgroup, tg = token groups per page, rb * tg = 4.
+// Few rows (memory-bound decode) split each page's tokens over the waves; many
+// rows give each wave 16 rows and the whole page.
+#pragma once
+
+#include <cstdint>
+
+namespace mla {
+
+constexpr int kPage = 64;
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kFp8Record = 656;
+constexpr int kMetaInts = 8;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+struct Plan {
+  int rb;          // 16-row blocks per workgroup
+  int tg;          // token groups per page (rb * tg == kWaves)
+  int m_tile;      // rows per workgroup
+  int m_tiles;     // workgroups per (range, KV head) along the rows
+  int wgs_per_cu;  // resident workgroups per CU the part count assumes
+  int split_cost;  // scheduler: fixed cost of one piece of a sequence, in pages
+  int min_pages;   // scheduler: smallest piece worth cutting off a sequence
+};
+
+inline Plan make_plan(int heads_per_kv, int kv_format) {
+  (void)kv_format;
+  Plan p{};
+  if (heads_per_kv <= 16) {
+    p.rb = 1; p.tg = 4;
+  } else if (heads_per_kv <= 32) {
+    p.rb = 2; p.tg = 2;
+  } else {
+    p.rb = 4; p.tg = 1;
+  }
+  p.m_tile = 16 * p.rb;
+  p.m_tiles = (heads_per_kv + p.m_tile - 1) / p.m_tile;
+  p.wgs_per_cu = 2;
+  p.split_cost = 1;
+  p.min_pages = 1;
+  return p;
+}
+
+// Ranges the scheduler makes by default: enough workgroups to fill every CU
+// `wgs_per_cu` deep once the row tiles and KV heads are counted.
+inline int default_parts(const Plan& p, int h_kv, int num_cus) {
+  long slots = static_cast<long>(num_cus) * p.wgs_per_cu;
+  long per_range = static_cast<long>(p.m_tiles) * h_kv;
+  long parts = slots / (per_range > 0 ? per_range : 1);
+  if (parts < 1) parts = 1;
+  if (parts > (1 << 20)) parts = 1 << 20;
+  return static_cast<int>(parts);
+}
+
+// Host scheduler (scheduler.cpp). Lengths must be >= 0; num_parts >= 1.
+// Returns the total number of pieces (num_splits[batch]).
+int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, int min_pages,
+             int32_t* meta, int32_t* num_splits);
+
+}  // namespace mla
