@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark: paged MLA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole decode path over one batch: the host tile
+scheduler (mla_get_metadata) with its upload, then mla_decode_kvcache (split-KV
+kernel + combine kernel). Inputs are resident in HBM before timing starts. The
+KV pool is replicated R times and steps rotate through the copies so that the
+working set exceeds the 256 MB Infinity Cache and the numbers are HBM numbers.
+
+Prints one JSON line. `value` is achieved algorithmic HBM GB/s of the whole
+step; TFLOPS and roofline fractions ride along. `roofline` is measured on the
+split-KV kernel alone with HIP events on the decode stream. `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def algorithmic_work(w):
+    """Bytes the method must move and FLOPs it must do (no partials, no re-reads).
+
+    bytes = sum_b h_kv*L_b*bpt + q + o + lse + block-table entries + lengths,
+    flops = 2*(576 + 512) * h_q * sum_b sum_s n_allowed(b, s)."""
+    L = [int(x) for x in w.cache_seqlens.tolist()]
+    B, S, H, Hk = w.batch, w.s_q, w.h_q, w.h_kv
+    bpt = 1152 if w.kv_format == "bf16" else 656
+    kv = sum(Hk * l * bpt for l in L)
+    q = B * S * H * 576 * 2
+    o = B * S * H * 512 * 2
+    lse = B * S * H * 4
+    bt = sum((l + 63) // 64 for l in L) * 4
+    byts = kv + q + o + lse + bt + B * 4
+    n_allowed = 0
+    for l in L:
+        for s in range(S):
+            n_allowed += max(0, min(l, (l - S + 1 + s) if w.causal else l))
+    flops = 2 * (576 + 512) * H * n_allowed
+    return byts, flops, kv
+
+
+class HipEvents:
+    """Minimal HIP event API through ctypes (events on the decode stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """Time the oracle on the first sequences of the workload (bounded sample)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    a = w.as_numpy()
+    done, t_total, n = [], 0.0, 0
+    order = list(range(w.batch))
+    while n < len(order) and t_total < target_s:
+        b = order[n]
+        t0 = time.perf_counter()
+        oracle.mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
+                          dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
+        t_total += time.perf_counter() - t0
+        done.append(b)
+        n += 1
+    L = [int(a["cache_seqlens"][b]) for b in done]
+    bpt = 1152 if w.kv_format == "bf16" else 656
+    S, H = w.s_q, w.h_q
+    byts = sum(w.h_kv * l * bpt for l in L) + len(done) * S * H * (576 * 2 + 512 * 2 + 4) \
+        + sum((l + 63) // 64 for l in L) * 4 + 4 * len(done)
+    return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {w.batch} sequences (first in batch order, {sum(L)} cached tokens), "
+                      f"{t_total:.2f} s, numpy float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="compute_heavy")
+    ap.add_argument("--copies", type=int, default=0, help="KV pool replicas to rotate through (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_mla_decode_amd as mla
+    from workloads import WORKLOAD_SPECS, named_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = named_workload(args.workload)
+    byts, flops, kv_bytes = algorithmic_work(w)
+    pool_bytes = w.kvcache.numel() * w.kvcache.element_size()
+    copies = args.copies or max(1, math.ceil(2 * INFINITY_CACHE_BYTES / max(pool_bytes, 1)))
+    print(f"[bench] {w.name}: {WORKLOAD_SPECS[w.name]['text']}; pool {pool_bytes / 1e6:.1f} MB x {copies} copies",
+          file=sys.stderr, flush=True)
+
+    q = w.q.to(dev)
+    bt = w.block_table.to(dev)
+    L_dev = w.cache_seqlens.to(dev)
+    L_host = w.cache_seqlens.clone().pin_memory()
+    kvs = [w.kvcache.to(dev) for _ in range(copies)]
+    M = w.heads_per_kv
+    parts = mla.mla_num_parts(w.batch, M, w.h_kv, w.kv_format)
+    meta_dev = torch.empty((parts, 8), dtype=torch.int32, device=dev)
+    splits_dev = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.h_q, w.s_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((mla.mla_workspace_bytes(w.batch, parts, M, w.h_kv),), dtype=torch.uint8, device=dev)
+    decoders = [mla.MlaDecoder(q, kv, bt, L_dev, w.dv, meta_dev, splits_dev, w.causal, w.softmax_scale,
+                               out=out, lse=lse, workspace=ws) for kv in kvs]
+    stream = torch.cuda.current_stream(dev)
+    hip = HipEvents()
+
+    def step(i, ev=None):
+        # a1: host tile scheduler for this step's lengths, uploaded on the decode stream
+        m_h, s_h = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts, pin=True)
+        meta_dev.copy_(m_h, non_blocking=True)
+        splits_dev.copy_(s_h, non_blocking=True)
+        d = decoders[i % copies]
+        d.set_events(ev if ev is not None else (None, None, None))
+        d.run(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(hip.create(), hip.create(), hip.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    split_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    comb_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+    split_avg = sum(split_ms) / len(split_ms)
+    comb_avg = sum(comb_ms) / len(comb_ms)
+
+    gbs = byts / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    split_gbs = byts / (split_avg * 1e-3) / 1e9
+    split_tflops = flops / (split_avg * 1e-3) / 1e12
+    intensity = flops / byts
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if intensity < ridge else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(split_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(split_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    result = {
+        "metric": "paged MLA decode achieved HBM GB/s and TFLOPS (+% of roofline), 1 MI355X",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "d_qk": 576, "d_v": 512, "page": 64, "kv_format": w.kv_format, "causal": w.causal,
+                   "total_kv_tokens": int(w.cache_seqlens.sum()), "num_parts": parts, "kv_copies": copies},
+        "tflops": round(tflops, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "split_kernel_ms": round(split_avg, 5),
+        "combine_kernel_ms": round(comb_avg, 5),
+        "algorithmic_bytes": byts,
+        "algorithmic_flops": flops,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

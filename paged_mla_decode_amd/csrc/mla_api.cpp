@@ -174,6 +174,9 @@ mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: a kv stride is smaller than one cached row (%lld bytes)",
                 static_cast<long long>(row_bytes));
   if (!aligned16(a->kvcache)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: kvcache must be 16-byte aligned");
+  if (kvb[1] * mla::kPage >= (int64_t{1} << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: a 64-token page must span less than 2 GiB (token stride %lld bytes)",
+                static_cast<long long>(kvb[1]));
   if ((reinterpret_cast<uintptr_t>(a->o) & 7u) || (reinterpret_cast<uintptr_t>(a->lse) & 3u))
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: o must be 8-byte and lse 4-byte aligned");
 

@@ -8,24 +8,26 @@
 // softmax (same page, "跷跷板调度算法突破寄存器资源限制"); the decomposition
 // below is designed for CDNA4, not taken from the Hopper design.
 //
-// Split kernel, one workgroup = 4 wavefronts per (KV range, 16*rb-row tile,
-// KV head). For each page of the range:
-//   1. all 256 threads gather the page (64 tokens x 1152 B, or 64 x 656-B FP8
-//      records dequantised to bf16) with 16-byte loads into LDS; the loads
-//      for page i+1 are in flight while page i is computed;
-//   2. each wave computes S^T = K Q^T for its 16 rows and its token group on
-//      MFMA 16x16x32 bf16: A = 16 tokens x 32 dims of K read from LDS (one
-//      16-byte read per lane), B = Q^T held in VGPRs for the whole range;
-//   3. the online softmax runs in registers: every lane holds one query row
-//      (lane % 16) and 4 tokens, so the row max needs two cross-lane steps and
-//      the rescale of the O accumulator is lane-local;
-//   4. O^T += V^T P^T on MFMA: P^T is the bf16 softmax tile exactly as the
-//      S^T MFMA left it in registers (the token order inside a 32-token chunk
-//      is permuted identically on both operands), V^T is read from the same
-//      LDS page.
-// Waves that split a page's tokens merge (m, l, O) through LDS at the end of
-// each sequence piece. A piece that is a whole sequence writes bf16 O and LSE
-// directly; otherwise it writes fp32 O / l and its LSE to its partial slot.
+// Split kernel: one workgroup = 4 wavefronts per (KV range, row tile, KV head).
+//   * Pages stream into a two-slot LDS ring with global_load_lds_dwordx4:
+//     64 lanes x 16 B land in 1 KB of LDS per instruction, so no VGPRs hold
+//     in-flight data and page i+1 loads while page i is computed. The 16-byte
+//     chunks of a 1152-byte token row are XOR-swizzled (chunk ^ f(token)) so
+//     both the K reads and the transposed V reads below hit distinct banks.
+//   * FP8 pages (656-byte records) stream raw into the ring; one LDS pass turns
+//     the e4m3 codes into bf16 (exact: 4 significant bits fit in 8) and copies
+//     RoPE and the per-128-dim scales. The scales are applied in fp32 on the
+//     logits (per scale group) and folded into P for the PV product, so K and V
+//     enter the MFMA without rounding.
+//   * Each wave owns 16 query rows (lane % 16) and a token group of every page:
+//     S^T = K Q^T on MFMA 16x16x32 bf16 (A = 16 tokens x 32 dims of K from LDS,
+//     one 16-byte read; B = Q^T kept in VGPRs), online softmax in registers
+//     (two cross-lane steps for the row max; the O rescale is lane-local), then
+//     O^T += V^T P^T on MFMA with P^T straight from the S^T registers and V^T
+//     from LDS through ds_read_b64_tr_b16 (the transposing LDS read of gfx950).
+//   * Waves that split a page's tokens merge (m, l, O) through LDS at the end of
+//     a sequence piece. A piece that is the whole sequence writes bf16 O and LSE;
+//     otherwise fp32 O / l and its LSE go to the piece's partial slot.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -36,18 +38,29 @@ namespace mla {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kLdsRow = 584;                   // bf16 per token row in LDS: 576 + 8 pad (1168 B)
-constexpr int kLdsPage = kPage * kLdsRow;      // 37376 bf16 = 74752 B
-constexpr int kFmtBf16 = 0;
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
+
+constexpr int kRowBytes = kDqk * 2;                  // 1152: one bf16 token row
+constexpr int kPageBytes = kPage * kRowBytes;        // 73728 = 72 x 1 KB
+constexpr int kRawPageBytes = kPage * kFp8Record;    // 41984 = 41 x 1 KB
+constexpr int kBf16Loads = kPageBytes / 1024;        // 72 direct-load instructions per page
+constexpr int kFp8Loads = kRawPageBytes / 1024;      // 41
 constexpr int kFmtFp8 = 1;
+constexpr int kFmtBf16 = 0;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 
+// LDS budget (bytes): bf16 -- two page slots; fp8 -- two raw slots, one bf16
+// page, per-token scales.
+constexpr int kLdsBf16 = 2 * kPageBytes;                                   // 147456
+constexpr int kLdsFp8 = 2 * kRawPageBytes + kPageBytes + kPage * 4 * 4;    // 158720
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));   // round to nearest even
@@ -55,139 +68,332 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// OCP E4M3FN code (low 8 bits of c) -> float; S.1111.111 -> NaN.
-__device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
+// Swizzle of the 16-byte chunk index inside a token row (stays inside its
+// aligned group of 8 chunks): K reads (8 consecutive tokens, one chunk) and
+// transposed V reads (4 consecutive tokens, 2 chunks) both spread over 8 groups.
+__device__ __forceinline__ int swz(int token) { return ((token & 3) << 1) | ((token >> 2) & 1); }
+
+__device__ __forceinline__ int chunk_off(int token, int chunk) { return token * kRowBytes + 16 * (chunk ^ swz(token)); }
+
+// OCP E4M3FN code (low 8 bits of c) -> bf16 bits, exactly. Codes 0x7F/0xFF -> NaN.
+__device__ __forceinline__ uint32_t e4m3fn_to_bf16_bits(uint32_t c) {
   const uint32_t mag = c & 0x7Fu;
-  const uint32_t e = mag >> 3, m = mag & 7u;
-  float v = (e == 0) ? static_cast<float>(m) * 0.001953125f                 // m * 2^-9
-                     : __uint_as_float(((e + 120u) << 23) | (m << 20));     // 2^(e-7) * (1 + m/8)
-  v = (mag == 0x7Fu) ? __builtin_nanf("") : v;
-  return (c & 0x80u) ? -v : v;
+  uint32_t v;
+  if (mag >= 8u) {
+    v = (mag << 4) + 0x3C00u;                      // exponent e - 7 + 127, mantissa m << 4
+  } else {
+    v = __float_as_uint(static_cast<float>(mag) * 0.001953125f) >> 16;   // m * 2^-9, exact in bf16
+  }
+  v = (mag == 0x7Fu) ? 0x7FC0u : v;
+  return v | ((c & 0x80u) << 8);
 }
 
-// ----------------------------------------------------------------------------
-// Page loaders: global -> registers (prefetch), registers -> LDS.
-// ----------------------------------------------------------------------------
+// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt fields left at "no wait"),
+// so the compiler's own wait-count tracking sees it.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int FMT>
-struct PageLoader;
-
-template <>
-struct PageLoader<kFmtBf16> {
-  static constexpr int kChunks = kPage * (kDqk * 2 / 16) / kThreads;   // 4608 / 256 = 18
-  u32x4 v[kChunks];
-
-  __device__ __forceinline__ void clear() {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) v[j] = u32x4{0u, 0u, 0u, 0u};
-  }
-  // base: start of (page, token 0, kv head); token stride st in bytes.
-  __device__ __forceinline__ void load(const uint8_t* base, int64_t st, int tid) {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int c = j * kThreads + tid;
-      const int tok = c / 72, col = c - tok * 72;
-      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + tok * st + col * 16));
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int c = j * kThreads + tid;
-      const int tok = c / 72, col = c - tok * 72;
-      *reinterpret_cast<u32x4*>(lds + tok * kLdsRow + col * 8) = v[j];
-    }
-  }
-};
-
-// FP8 record: [0,512) e4m3 codes, [512,528) 4 fp32 scales, [528,656) 64 bf16 RoPE.
-// Thread t dequantises latent chunk (t % 32) -- 16 codes, dims 16*(t%32).. --
-// of tokens t/32 + 8k, k < 8, and copies RoPE chunk t % 8 of tokens t/8 + 32k, k < 2.
-template <>
-struct PageLoader<kFmtFp8> {
-  u32x4 lat[8];
-  float sc[8];
-  u32x4 rope[2];
-
-  __device__ __forceinline__ void clear() {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) { lat[k] = u32x4{0u, 0u, 0u, 0u}; sc[k] = 0.f; }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) rope[k] = u32x4{0u, 0u, 0u, 0u};
-  }
-  __device__ __forceinline__ void load(const uint8_t* base, int64_t st, int tid) {
-    const int ch = tid & 31;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint8_t* rec = base + (tid / 32 + 8 * k) * st;
-      lat[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + ch * 16));
-      sc[k] = *reinterpret_cast<const float*>(rec + 512 + 4 * (ch / 8));
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint8_t* rec = base + (tid / 8 + 32 * k) * st;
-      rope[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 528 + (tid & 7) * 16));
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const int ch = tid & 31;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int tok = tid / 32 + 8 * k;
-      const uint32_t w[4] = {lat[k][0], lat[k][1], lat[k][2], lat[k][3]};
-      uint32_t out[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float lo = e4m3fn_to_f32(w[i] >> (16 * h)) * sc[k];
-          const float hi = e4m3fn_to_f32(w[i] >> (16 * h + 8)) * sc[k];
-          out[2 * i + h] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-        }
-      }
-      u32x4* dst = reinterpret_cast<u32x4*>(lds + tok * kLdsRow + ch * 16);
-      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int tok = tid / 8 + 32 * k;
-      *reinterpret_cast<u32x4*>(lds + tok * kLdsRow + 512 + (tid & 7) * 8) = rope[k];
-    }
-  }
-};
-
-__device__ __forceinline__ float wave_max16(float v) {
-  // reduce over the 4 lanes that share lane % 16
+__device__ __forceinline__ float max4lanes(float v) {   // over the 4 lanes sharing lane % 16
   v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  return fmaxf(v, __shfl_xor(v, 32));
 }
 
-__device__ __forceinline__ float wave_sum16(float v) {
+__device__ __forceinline__ float sum4lanes(float v) {
   v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  return v + __shfl_xor(v, 32);
+}
+
+// ----------------------------------------------------------------------------
+// Page iteration over one KV range: sequences begin_b..end_b, pages [pg0, pg1)
+// of each, in order. Zero-page sequences still get their epilogue.
+// ----------------------------------------------------------------------------
+struct Range {
+  int begin_b, begin_page, end_b, end_page, split0;
+};
+
+__device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1) {
+  const int max_len = p.max_blocks * kPage;
+  int len = p.seqlens[b];
+  len = len < 0 ? 0 : (len > max_len ? max_len : len);
+  L = len;
+  const int np = (len + kPage - 1) / kPage;
+  pg0 = (b == r.begin_b) ? max(r.begin_page, 0) : 0;
+  pg1 = (b == r.end_b) ? min(r.end_page, np) : np;
+  if (pg0 > pg1) pg0 = pg1;
+}
+
+// First (sequence, page) at or after sequence b that has a page in the range; nb = end_b + 1 if none.
+__device__ __forceinline__ void next_with_pages(const DecodeParams& p, const Range& r, int b, int& nb, int& npg) {
+  for (; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    seq_pages(p, r, b, L, pg0, pg1);
+    if (pg0 < pg1) {
+      nb = b;
+      npg = pg0;
+      return;
+    }
+  }
+  nb = r.end_b + 1;
+  npg = 0;
 }
 
 // ----------------------------------------------------------------------------
 // Split-KV kernel
 // ----------------------------------------------------------------------------
 
+// Barrier that orders LDS only: unlike __syncthreads it does not wait for the
+// page loads still in flight into the other ring slot.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Lane-constant indices of one wavefront.
+struct Lane {
+  int tid, lane, wave, tg, r16, q4;
+  int sw_k;              // swizzle of K rows read by this lane (token 16*tile + r16)
+  int tr_tok, sw_v;      // V^T transposed reads: token tb + tr_tok (+16), its swizzle
+  int tr_half, tr_hh;    // 8-byte half and chunk parity of the transposed read
+};
+
+// Exact online-softmax rescale is deferred until the running max grows by
+// more than this (log2 units): P stays <= 2^8, far from fp32/bf16 limits, and
+// O / l and LSE = m + log2 l are unchanged.
+constexpr float kRescaleSlack = 8.f;
+
+// One page of the pipeline. `cur` holds the page (bf16 rows, or raw FP8
+// records), `nxt` is the other ring slot and receives the next page, `conv`
+// (FP8 only) holds the converted bf16 page and its scales. The three regions
+// are disjoint; the restrict qualifiers let the compiler see that the reads
+// of this page never touch the loads in flight into `nxt`.
+template <int TG, int FMT>
+__device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
+                                          uint8_t* __restrict__ conv, const uint8_t* next_src,
+                                          const uint32_t* ld_off, const Lane& ln, int L, int last_allowed,
+                                          int pi, bool this_ok, float scale_log2, const bf16x8 (&qf)[18],
+                                          f32x4 (&acc)[32], float& m_run, float& l_run) {
+  constexpr int NT = 4 / TG;
+  constexpr bool kFp8 = (FMT == kFmtFp8);
+  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
+  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
+  constexpr int NG = kFp8 ? 4 : 1;    // scale groups folded into P
+  const int tid = ln.tid, tg = ln.tg, r16 = ln.r16, q4 = ln.q4;
+
+  const int valid = min(L - pi * kPage, kPage);      // tokens of this page inside the sequence
+  const uint8_t* page;
+  const float* scale_tab = nullptr;
+  if constexpr (kFp8) {
+    // raw records -> bf16 page (codes exact), RoPE copy, scales; tail tokens and a bad page -> 0
+    float* scales = reinterpret_cast<float*>(conv + kPageBytes);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int item = tid + kThreads * j;
+      const int t = item >> 5, ch = item & 31;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 16 * ch);
+      const bool keep = this_ok && t < valid;
+      u32x4 lo, hi;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t a = w[i], c = w[i + 2];
+        lo[2 * i] = e4m3fn_to_bf16_bits(a) | (e4m3fn_to_bf16_bits(a >> 8) << 16);
+        lo[2 * i + 1] = e4m3fn_to_bf16_bits(a >> 16) | (e4m3fn_to_bf16_bits(a >> 24) << 16);
+        hi[2 * i] = e4m3fn_to_bf16_bits(c) | (e4m3fn_to_bf16_bits(c >> 8) << 16);
+        hi[2 * i + 1] = e4m3fn_to_bf16_bits(c >> 16) | (e4m3fn_to_bf16_bits(c >> 24) << 16);
+      }
+      if (!keep) {
+        lo = u32x4{0u, 0u, 0u, 0u};
+        hi = lo;
+      }
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch)) = lo;
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch + 1)) = hi;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int item = tid + kThreads * j;
+      const int t = item >> 3, rr = item & 7;
+      u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 528 + 16 * rr);
+      if (!(this_ok && t < valid)) w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 64 + rr)) = w;
+    }
+    {
+      const int t = tid >> 2, c = tid & 3;
+      const float sv = *reinterpret_cast<const float*>(cur + t * kFp8Record + 512 + 4 * c);
+      scales[tid] = (this_ok && t < valid) ? sv : 0.f;
+    }
+    lds_barrier();
+    page = conv;
+    scale_tab = scales;
+  } else {
+    if (valid < kPage || !this_ok) {
+      // zero the rows past the sequence end (all rows of a bad page) so that
+      // stale bytes never meet a zero weight in P V (0 * NaN = NaN)
+      const int z0 = this_ok ? valid : 0;
+      for (int x = z0 * kRowBytes + 16 * tid; x < kPageBytes; x += 16 * kThreads)
+        *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
+      lds_barrier();
+    }
+    page = cur;
+  }
+
+  // next page -> nxt (direct to LDS; lands while this page is computed)
+  if (next_src != nullptr) {
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const int k = ln.wave + kWaves * j;
+      if (k < kLoads)
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(next_src + ld_off[j]), LDS_PTR(void, nxt + 1024 * k), 16, 0, 0);
+    }
+  }
+
+  // ---- S^T tiles: rows = tokens, columns = query rows --------------------------
+  f32x4 s[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint8_t* krow = page + (16 * (tg * NT + t) + r16) * kRowBytes;
+    if constexpr (kFp8) {
+      f32x4 grp[5];
+#pragma unroll
+      for (int g = 0; g < 5; ++g) grp[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ((4 * c + q4) ^ ln.sw_k));
+        const int g = (c < 16) ? (c >> 2) : 4;
+        grp[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], grp[g], 0, 0, 0);
+      }
+      // logits of tokens 16*tile + 4*q4 + i: RoPE part + scale-weighted latent groups
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(scale_tab + 4 * (16 * (tg * NT + t) + 4 * q4 + i));
+        s[t][i] = grp[4][i] + sc[0] * grp[0][i] + sc[1] * grp[1][i] + sc[2] * grp[2][i] + sc[3] * grp[3][i];
+      }
+    } else {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ((4 * c + q4) ^ ln.sw_k));
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- mask, online softmax ----------------------------------------------------
+  const int tok_base = pi * kPage + 16 * tg * NT + 4 * q4;
+  float mx = kNegInf;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok_base + 16 * t + i;
+      const bool ok = tok < L && tok <= last_allowed;
+      const float v = ok ? s[t][i] * scale_log2 : kNegInf;
+      s[t][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  }
+  mx = max4lanes(mx);
+  if (mx > m_run + kRescaleSlack) {          // the 4 lanes of a row agree on this
+    const float alpha = fast_exp2(m_run - mx);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[d] *= alpha;
+    m_run = mx;
+  }
+  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(s[t][i] - m_use);
+      s[t][i] = e;
+      psum += e;
+    }
+  }
+  l_run += psum;
+
+  // ---- O^T += V^T P^T ------------------------------------------------------------
+  if constexpr (NT >= 2) {
+#pragma unroll
+    for (int u = 0; u < NT / 2; ++u) {
+      const int tb = 16 * (tg * NT + 2 * u);
+      const uint8_t* v0 = page + (tb + ln.tr_tok) * kRowBytes + 8 * ln.tr_half;
+      const uint8_t* v1 = v0 + 16 * kRowBytes;
+      // P^T operand; k-slot j < 4 is token tb + 4*q4 + j, j >= 4 is token tb + 16 + 4*q4 + j - 4
+      bf16x8 pb[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = s[2 * u][j], x1 = s[2 * u + 1][j];
+          if constexpr (kFp8) {
+            x0 *= scale_tab[4 * (tb + 4 * q4 + j) + g];
+            x1 *= scale_tab[4 * (tb + 16 + 4 * q4 + j) + g];
+          }
+          pb[g][j] = static_cast<__bf16>(x0);
+          pb[g][4 + j] = static_cast<__bf16>(x1);
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < 32; ++d) {
+        const int off = 16 * ((2 * d + ln.tr_hh) ^ ln.sw_v);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + off));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v1 + off));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kFp8 ? (d >> 3) : 0], acc[d], 0, 0, 0);
+      }
+    }
+  } else {
+    const int tb = 16 * tg;
+    const uint8_t* v0 = page + (tb + ln.tr_tok) * kRowBytes + 8 * ln.tr_half;
+    s16x4 pb[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = s[0][j];
+        if constexpr (kFp8) x *= scale_tab[4 * (tb + 4 * q4 + j) + g];
+        pb[g][j] = static_cast<short>(f32_to_bf16(x));
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 32; ++d) {
+      const int off = 16 * ((2 * d + ln.tr_hh) ^ ln.sw_v);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + off));
+      acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, lo), pb[kFp8 ? (d >> 3) : 0],
+                                                         acc[d], 0, 0, 0);
+    }
+  }
+}
+
 template <int RB, int TG, int FMT>
 __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   static_assert(RB * TG == kWaves, "4 waves per workgroup");
-  constexpr int NT = 4 / TG;          // 16-token tiles per wave per page
   constexpr int M_TILE = 16 * RB;
+  constexpr bool kFp8 = (FMT == kFmtFp8);
+  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
+  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
+  constexpr int kSlotBytes = kFp8 ? kRawPageBytes : kPageBytes;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsPage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kFp8 ? kLdsFp8 : kLdsBf16];
   __shared__ float red_m[kWaves][16];
   __shared__ float red_l[kWaves][16];
+  uint8_t* const ring = smem;                                        // two load slots
+  uint8_t* const conv = smem + 2 * kRawPageBytes;                    // fp8: converted page + scales
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int rb = wave % RB, tg = wave / RB;
-  const int r16 = lane & 15, q4 = lane >> 4;
+  Lane ln;
+  ln.tid = threadIdx.x;
+  ln.lane = ln.tid & 63;
+  ln.wave = ln.tid >> 6;
+  const int rb = ln.wave % RB;
+  ln.tg = ln.wave / RB;
+  ln.r16 = ln.lane & 15;
+  ln.q4 = ln.lane >> 4;
+  ln.sw_k = swz(ln.r16);
+  ln.tr_tok = 4 * ln.q4 + (ln.r16 >> 2);
+  ln.sw_v = swz(ln.tr_tok);
+  ln.tr_half = ln.r16 & 1;
+  ln.tr_hh = (ln.r16 & 3) >> 1;
+  const int lane = ln.lane, wave = ln.wave, tg = ln.tg, r16 = ln.r16, q4 = ln.q4;
 
   // Workgroup i runs on XCD i % 8: give each XCD a contiguous block of
   // logical ids so the row tiles of one KV range share that XCD's L2.
@@ -199,33 +405,75 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   const int kvh = (logical / m_tiles) % p.h_kv;
   const int part = logical / (m_tiles * p.h_kv);
 
-  const int32_t* meta = p.meta + part * kMetaInts;
-  const int begin_b = meta[0];
-  if (begin_b < 0 || begin_b >= p.batch) return;
-  const int begin_page = meta[1];
-  const int end_b = min(meta[2], p.batch - 1);
-  const int end_page = meta[3];
-  const int split0 = meta[4];
+  Range r;
+  {
+    const int32_t* meta = p.meta + part * kMetaInts;
+    r.begin_b = meta[0];
+    r.begin_page = meta[1];
+    r.end_b = min(meta[2], p.batch - 1);
+    r.end_page = meta[3];
+    r.split0 = meta[4];
+  }
+  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
 
   const int row = mt * M_TILE + rb * 16 + r16;   // this lane's query row within the KV head
   const bool row_ok = row < p.rows;
   const int s_idx = row_ok ? row / p.group : 0;
   const int head = kvh * p.group + (row_ok ? row % p.group : 0);
 
-  const int max_len = p.max_blocks * kPage;
-  PageLoader<FMT> ld;
+  // Per-lane byte offsets (within a page of this KV head) of the direct loads.
+  uint32_t ld_off[kLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) {
+    const int k = wave + kWaves * j;
+    const int x = 1024 * k + 16 * lane;            // byte in the LDS slot
+    if constexpr (kFp8) {
+      const int t = x / kFp8Record;
+      ld_off[j] = static_cast<uint32_t>(t * p.kv_st + (x - t * kFp8Record));
+    } else {
+      const int pc = x / 16;
+      const int t = pc / 72;
+      const int lc = (pc - 72 * t) ^ swz(t);
+      ld_off[j] = static_cast<uint32_t>(t * p.kv_st + 16 * lc);
+    }
+  }
+  const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
 
-  for (int b = begin_b; b <= end_b; ++b) {
-    int L = p.seqlens[b];
-    L = L < 0 ? 0 : (L > max_len ? max_len : L);
-    const int np = (L + kPage - 1) / kPage;
-    const int pg0 = (b == begin_b) ? max(begin_page, 0) : 0;
-    const int pg1 = (b == end_b) ? min(end_page, np) : np;
-    const int split_idx = (b == begin_b) ? split0 : 0;
+  // Global address of page `pi` of sequence `b`; nullptr for a block-table
+  // entry outside the pool (never dereferenced).
+  auto page_src = [&](int b, int pi) -> const uint8_t* {
+    const int pg = p.block_table[static_cast<int64_t>(b) * p.bt_stride + pi];
+    if (pg < 0 || pg >= p.num_pages) return nullptr;
+    return kv_head + static_cast<int64_t>(pg) * p.kv_sp;
+  };
+
+  // ---- pipeline: the page in flight always targets ring slot `slot` ------------
+  int slot = 0;
+  bool load_ok = true;
+  {
+    int nb, npi;
+    next_with_pages(p, r, r.begin_b, nb, npi);
+    if (nb <= r.end_b) {
+      const uint8_t* src = page_src(nb, npi);
+      load_ok = src != nullptr;
+      if (load_ok) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+          const int k = wave + kWaves * j;
+          if (k < kLoads)
+            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src + ld_off[j]), LDS_PTR(void, ring + 1024 * k), 16, 0, 0);
+        }
+      }
+    }
+  }
+
+  for (int b = r.begin_b; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    seq_pages(p, r, b, L, pg0, pg1);
+    const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = p.num_splits[b];
     const int nsplit = p.num_splits[b + 1] - slot0;
-    const int last_allowed_base = p.causal ? (L - p.s_q) : (L - 1);   // + s_idx if causal
-    const int last_allowed = p.causal ? last_allowed_base + s_idx : last_allowed_base;
+    const int last_allowed = p.causal ? (L - p.s_q + s_idx) : (L - 1);
 
     // Q^T operand: 18 chunks of 8 dims (dims 32c + 8*q4 .. +8) of this lane's row.
     bf16x8 qf[18];
@@ -236,6 +484,9 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
         u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
         qf[c] = __builtin_bit_cast(bf16x8, v);
       }
+      // Q must be in registers before the page loop: otherwise the first MFMA
+      // would wait on every load in flight, the next page's included.
+      wait_vm_all();
     }
 
     float m_run = kNegInf, l_run = 0.f;
@@ -244,125 +495,36 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     for (int d = 0; d < 32; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool bad = false;
 
-    const uint8_t* kv_head = p.kv + kvh * p.kv_sh;
-    auto page_ptr = [&](int pi, bool& ok) -> const uint8_t* {
-      const int pg = p.block_table[static_cast<int64_t>(b) * p.bt_stride + pi];
-      ok = (pg >= 0 && pg < p.num_pages);
-      return kv_head + static_cast<int64_t>(ok ? pg : 0) * p.kv_sp;
-    };
-
-    if (pg0 < pg1) {
-      bool ok;
-      const uint8_t* ptr = page_ptr(pg0, ok);
-      if (ok) ld.load(ptr, p.kv_st, tid); else { ld.clear(); bad = true; }
-    }
-
     for (int pi = pg0; pi < pg1; ++pi) {
-      __syncthreads();                 // every wave is done with the previous page
-      ld.store(lds, tid);
-      __syncthreads();
-      if (pi + 1 < pg1) {
-        bool ok;
-        const uint8_t* ptr = page_ptr(pi + 1, ok);
-        if (ok) ld.load(ptr, p.kv_st, tid); else { ld.clear(); bad = true; }
-      }
-
-      // ---- S^T tiles: rows = tokens, columns = query rows --------------------
-      f32x4 s[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = lds + (16 * (tg * NT + t) + r16) * kLdsRow + 8 * q4;
-#pragma unroll
-        for (int c = 0; c < 18; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * c);
-          s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[t], 0, 0, 0);
+      // page (b, pi) is in flight into `slot`
+      const bool this_ok = load_ok;
+      bad |= !this_ok;
+      wait_vm_all();
+      lds_barrier();                   // its bytes are in LDS; every wave is done with slot ^ 1
+      const uint8_t* next_src = nullptr;
+      {
+        int nb = b, npi = pi + 1;
+        if (npi >= pg1) next_with_pages(p, r, b + 1, nb, npi);
+        if (nb <= r.end_b) {
+          next_src = page_src(nb, npi);
+          load_ok = next_src != nullptr;
         }
       }
-
-      // ---- mask, online softmax ----------------------------------------------
-      const int tok_base = pi * kPage + 16 * tg * NT + 4 * q4;
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = tok_base + 16 * t + i;
-          const bool ok = tok < L && tok <= last_allowed;
-          const float v = ok ? s[t][i] * p.scale_log2 : kNegInf;
-          s[t][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = wave_max16(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(s[t][i] - m_use);
-          s[t][i] = e;
-          psum += e;
-        }
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < 32; ++d) acc[d] *= alpha;
-
-      // ---- O^T += V^T P^T ----------------------------------------------------
-      if constexpr (NT >= 2) {
-#pragma unroll
-        for (int u = 0; u < NT / 2; ++u) {
-          bf16x8 pb;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pb[j] = static_cast<__bf16>(s[2 * u][j]);
-            pb[4 + j] = static_cast<__bf16>(s[2 * u + 1][j]);
-          }
-          const int tok0 = 16 * (tg * NT + 2 * u) + 4 * q4;   // k-slots j<4: tok0+j ; j>=4: tok0+16+j-4
-          const __bf16* vb = reinterpret_cast<const __bf16*>(lds);
-#pragma unroll
-          for (int d = 0; d < 32; ++d) {
-            const int dim = 16 * d + r16;
-            bf16x8 a;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              a[j] = vb[(tok0 + j) * kLdsRow + dim];
-              a[4 + j] = vb[(tok0 + 16 + j) * kLdsRow + dim];
-            }
-            acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[d], 0, 0, 0);
-          }
-        }
-      } else {
-        s16x4 pb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pb[j] = static_cast<short>(f32_to_bf16(s[0][j]));
-        const int tok0 = 16 * tg + 4 * q4;
-#pragma unroll
-        for (int d = 0; d < 32; ++d) {
-          const int dim = 16 * d + r16;
-          s16x4 a;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) a[j] = static_cast<short>(lds[(tok0 + j) * kLdsRow + dim]);
-          acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[d], 0, 0, 0);
-        }
-      }
+      page_step<TG, FMT>(ring + slot * kSlotBytes, ring + (slot ^ 1) * kSlotBytes, conv, next_src, ld_off, ln, L,
+                         last_allowed, pi, this_ok, p.scale_log2, qf, acc, m_run, l_run);
+      slot ^= 1;
     }
 
-    // ---- merge the token groups, then write -----------------------------------
-    float l_row = wave_sum16(l_run);
+    // ---- merge the token groups, then write -------------------------------------------
+    float l_row = sum4lanes(l_run);
     float m_fin = m_run;
     if constexpr (TG > 1) {
-      __syncthreads();                 // all waves done with the LDS page
+      lds_barrier();                   // all waves done with the LDS page
       if (lane < 16) {
         red_m[wave][r16] = m_run;
         red_l[wave][r16] = l_row;
       }
-      __syncthreads();
+      lds_barrier();
       float M = kNegInf;
 #pragma unroll
       for (int k = 0; k < TG; ++k) M = fmaxf(M, red_m[rb + RB * k][r16]);
@@ -375,67 +537,72 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       for (int d = 0; d < 32; ++d) acc[d] *= f;
       l_row = ltot;
       m_fin = M;
-      // Sum the TG accumulators of each row block through LDS (fp32 [16 rows][512]).
-      float* red = reinterpret_cast<float*>(lds);
-      auto slot_ptr = [&](int slot) { return red + slot * (16 * 512); };
-      auto put = [&](float* base) {
+      // Sum the TG accumulators of each row block through LDS (fp32 [16 rows][512]),
+      // in the slot not receiving a page (bf16) or the converted page (fp8).
+      float* red = reinterpret_cast<float*>(kFp8 ? conv : ring + (slot ^ 1) * kSlotBytes);
+      auto put = [&](int sl) {
 #pragma unroll
         for (int d = 0; d < 32; ++d)
-          *reinterpret_cast<f32x4*>(base + r16 * 512 + 16 * d + 4 * q4) = acc[d];
+          *reinterpret_cast<f32x4*>(red + sl * (16 * 512) + r16 * 512 + 16 * d + 4 * q4) = acc[d];
       };
-      auto add = [&](const float* base) {
+      auto add = [&](int sl) {
 #pragma unroll
-        for (int d = 0; d < 32; ++d) acc[d] += *reinterpret_cast<const f32x4*>(base + r16 * 512 + 16 * d + 4 * q4);
+        for (int d = 0; d < 32; ++d)
+          acc[d] += *reinterpret_cast<const f32x4*>(red + sl * (16 * 512) + r16 * 512 + 16 * d + 4 * q4);
       };
       if constexpr (TG == 4) {                 // RB == 1: waves 0..3 hold the same rows
-        if (wave >= 2) put(slot_ptr(wave - 2));
-        __syncthreads();
-        if (wave < 2) add(slot_ptr(wave));
-        __syncthreads();
-        if (wave == 1) put(slot_ptr(0));
-        __syncthreads();
-        if (wave == 0) add(slot_ptr(0));
+        if (wave >= 2) put(wave - 2);
+        lds_barrier();
+        if (wave < 2) add(wave);
+        lds_barrier();
+        if (wave == 1) put(0);
+        lds_barrier();
+        if (wave == 0) add(0);
       } else {                                  // TG == 2, RB == 2
-        if (tg == 1) put(slot_ptr(rb));
-        __syncthreads();
-        if (tg == 0) add(slot_ptr(rb));
+        if (tg == 1) put(rb);
+        lds_barrier();
+        if (tg == 0) add(rb);
       }
+      lds_barrier();                            // scratch free again before the next page lands
     }
 
     if (tg == 0 && row_ok) {
-      const bool valid = !bad;
+      const bool ok = !bad;
       const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
       float lse = (l_row > 0.f) ? (m_fin + __log2f(l_row)) * kLn2 : kNegInf;
-      if (!valid) lse = __builtin_nanf("");
+      if (!ok) lse = __builtin_nanf("");
       if (nsplit == 1) {
         uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + 4 * q4;
+        const float nan = __builtin_nanf("");
 #pragma unroll
         for (int d = 0; d < 32; ++d) {
           u32x2 w;
-          const float x0 = valid ? acc[d][0] * inv : __builtin_nanf("");
-          const float x1 = valid ? acc[d][1] * inv : __builtin_nanf("");
-          const float x2 = valid ? acc[d][2] * inv : __builtin_nanf("");
-          const float x3 = valid ? acc[d][3] * inv : __builtin_nanf("");
+          const float x0 = ok ? acc[d][0] * inv : nan;
+          const float x1 = ok ? acc[d][1] * inv : nan;
+          const float x2 = ok ? acc[d][2] * inv : nan;
+          const float x3 = ok ? acc[d][3] * inv : nan;
           w[0] = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
           w[1] = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
           *reinterpret_cast<u32x2*>(orow + 16 * d) = w;
         }
         if (q4 == 0) p.lse[(static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx] = lse;
       } else {
-        const int slot = slot0 + split_idx;
-        if (slot >= 0 && slot < p.max_slots && split_idx < nsplit) {
-          float* prow = p.part_o + ((static_cast<int64_t>(slot) * p.h_kv + kvh) * p.rows + row) * kDv + 4 * q4;
+        const int pslot = slot0 + split_idx;
+        if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
+          float* prow = p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv + 4 * q4;
+          const float nan = __builtin_nanf("");
 #pragma unroll
           for (int d = 0; d < 32; ++d) {
             f32x4 v = acc[d] * inv;
-            if (!valid) v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            if (!ok) v = f32x4{nan, nan, nan, nan};
             *reinterpret_cast<f32x4*>(prow + 16 * d) = v;
           }
-          if (q4 == 0) p.part_lse[(static_cast<int64_t>(slot) * p.h_kv + kvh) * p.rows + row] = lse;
+          if (q4 == 0) p.part_lse[(static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row] = lse;
         }
       }
     }
   }
+  wait_vm_all();   // nothing may still be landing in LDS when the workgroup ends
 }
 
 // ----------------------------------------------------------------------------
