@@ -90,9 +90,8 @@ def cpu_baseline(w, target_s: float = 15.0):
         threads = len(os.sched_getaffinity(0))
     a = w.as_numpy()
     done, t_total, n = [], 0.0, 0
-    order = list(range(w.batch))
-    while n < len(order) and t_total < target_s:
-        b = order[n]
+    while t_total < target_s and n < 64 * w.batch:      # cycle through the batch until the time target
+        b = n % w.batch
         t0 = time.perf_counter()
         oracle.mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
                           dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
@@ -105,8 +104,8 @@ def cpu_baseline(w, target_s: float = 15.0):
     byts = sum(w.h_kv * l * bpt for l in L) + len(done) * S * H * (576 * 2 + 512 * 2 + 4) \
         + sum((l + 63) // 64 for l in L) * 4 + 4 * len(done)
     return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} sequences (first in batch order, {sum(L)} cached tokens), "
-                      f"{t_total:.2f} s, numpy float64"}
+            "sample": f"{len(done)} sequence decodes cycling through the {w.batch} sequences in batch order "
+                      f"({sum(L)} cached tokens), {t_total:.2f} s, numpy float64"}
 
 
 def main():

@@ -246,19 +246,28 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
   }
 
   // ---- S^T tiles: rows = tokens, columns = query rows --------------------------
+  // K chunk 4c + q4 of token row T sits at 16 * ((4c + q4) ^ swz(T)); with
+  // c = 2k + h that is 128k + 16 * ((4h + q4) ^ swz): two lane bases plus an
+  // immediate offset per read.
+  const int kb0 = 16 * ((q4) ^ ln.sw_k), kb1 = 16 * ((4 + q4) ^ ln.sw_k);
   f32x4 s[NT];
+  if constexpr (kFp8) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint8_t* krow = page + (16 * (tg * NT + t) + r16) * kRowBytes;
-    if constexpr (kFp8) {
+    for (int t = 0; t < NT; ++t) {
+      const uint8_t* krow = page + (16 * (tg * NT + t) + r16) * kRowBytes;
       f32x4 grp[5];
 #pragma unroll
       for (int g = 0; g < 5; ++g) grp[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // round-robin over the scale groups so consecutive MFMAs are independent
 #pragma unroll
-      for (int c = 0; c < 18; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ((4 * c + q4) ^ ln.sw_k));
-        const int g = (c < 16) ? (c >> 2) : 4;
-        grp[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], grp[g], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+          if (g == 4 && j >= 2) continue;
+          const int c = (g < 4) ? 4 * g + j : 16 + j;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 128 * (c >> 1) + ((c & 1) ? kb1 : kb0));
+          grp[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], grp[g], 0, 0, 0);
+        }
       }
       // logits of tokens 16*tile + 4*q4 + i: RoPE part + scale-weighted latent groups
 #pragma unroll
@@ -266,13 +275,45 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
         const f32x4 sc = *reinterpret_cast<const f32x4*>(scale_tab + 4 * (16 * (tg * NT + t) + 4 * q4 + i));
         s[t][i] = grp[4][i] + sc[0] * grp[0][i] + sc[1] * grp[1][i] + sc[2] * grp[2][i] + sc[3] * grp[3][i];
       }
-    } else {
-      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  } else {
+    // NT tiles x CH partial chains = 4 independent accumulations in flight;
+    // the K operands of chunk c + 1 are read while chunk c multiplies.
+    constexpr int CH = (NT >= 4) ? 1 : 4 / NT;
+    f32x4 part[NT][CH];
 #pragma unroll
-      for (int c = 0; c < 18; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ((4 * c + q4) ^ ln.sw_k));
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[t], 0, 0, 0);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < CH; ++h) part[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* krow0 = page + (16 * tg * NT + r16) * kRowBytes;
+    auto kload = [&](int c, int t) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(krow0 + 16 * t * kRowBytes + 128 * (c >> 1) + ((c & 1) ? kb1 : kb0));
+    };
+    // three-slot rotation: reads run two chunks ahead of the MFMAs
+    constexpr int kDepth = 3;
+    bf16x8 kbuf[kDepth][NT];
+#pragma unroll
+    for (int c = 0; c < kDepth - 1; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) kbuf[c][t] = kload(c, t);
+    __builtin_amdgcn_sched_group_barrier(0x100, (kDepth - 1) * NT, 0);
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+      if (c + kDepth - 1 < 18) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) kbuf[(c + kDepth - 1) % kDepth][t] = kload(c + kDepth - 1, t);
       }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        part[t][c % CH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c % kDepth][t], qf[c], part[t][c % CH], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);     // MFMAs of chunk c ...
+      if (c + kDepth - 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);   // ... then reads of chunk c + 2
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s[t] = part[t][0];
+#pragma unroll
+      for (int h = 1; h < CH; ++h) s[t] += part[t][h];
     }
   }
 
@@ -312,12 +353,16 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
   l_run += psum;
 
   // ---- O^T += V^T P^T ------------------------------------------------------------
+  // Transposed read of dims 16d.. : 16 * ((2d + hh) ^ sw_v) = 128 * (d / 4) + vb[d % 4].
+  int vb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vb[r] = 16 * ((2 * r + ln.tr_hh) ^ ln.sw_v) + 8 * ln.tr_half;
+  constexpr int kAhead = 4;                  // transposed reads issued ahead of their MFMA
   if constexpr (NT >= 2) {
 #pragma unroll
     for (int u = 0; u < NT / 2; ++u) {
       const int tb = 16 * (tg * NT + 2 * u);
-      const uint8_t* v0 = page + (tb + ln.tr_tok) * kRowBytes + 8 * ln.tr_half;
-      const uint8_t* v1 = v0 + 16 * kRowBytes;
+      const uint8_t* v0 = page + (tb + ln.tr_tok) * kRowBytes;
       // P^T operand; k-slot j < 4 is token tb + 4*q4 + j, j >= 4 is token tb + 16 + 4*q4 + j - 4
       bf16x8 pb[NG];
 #pragma unroll
@@ -333,18 +378,25 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
           pb[g][4 + j] = static_cast<__bf16>(x1);
         }
       }
+      auto vload = [&](int d) -> bf16x8 {
+        const uint8_t* a0 = v0 + 128 * (d >> 2) + vb[d & 3];
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 va[kAhead];
+#pragma unroll
+      for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
 #pragma unroll
       for (int d = 0; d < 32; ++d) {
-        const int off = 16 * ((2 * d + ln.tr_hh) ^ ln.sw_v);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + off));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v1 + off));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = va[d % kAhead];
+        if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
         acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kFp8 ? (d >> 3) : 0], acc[d], 0, 0, 0);
       }
     }
   } else {
     const int tb = 16 * tg;
-    const uint8_t* v0 = page + (tb + ln.tr_tok) * kRowBytes + 8 * ln.tr_half;
+    const uint8_t* v0 = page + (tb + ln.tr_tok) * kRowBytes;
     s16x4 pb[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -355,12 +407,18 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
         pb[g][j] = static_cast<short>(f32_to_bf16(x));
       }
     }
+    auto vload = [&](int d) -> s16x4 {
+      return __builtin_bit_cast(
+          s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + 128 * (d >> 2) + vb[d & 3])));
+    };
+    s16x4 va[kAhead];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
 #pragma unroll
     for (int d = 0; d < 32; ++d) {
-      const int off = 16 * ((2 * d + ln.tr_hh) ^ ln.sw_v);
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + off));
-      acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, lo), pb[kFp8 ? (d >> 3) : 0],
-                                                         acc[d], 0, 0, 0);
+      const s16x4 a = va[d % kAhead];
+      if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
+      acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[kFp8 ? (d >> 3) : 0], acc[d], 0, 0, 0);
     }
   }
 }
@@ -607,63 +665,96 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
 
 // ----------------------------------------------------------------------------
 // Combine: LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i
-// One wave per (sequence, row, KV head); lane l owns dims 8l .. 8l+7.
+// One workgroup per (sequence, row, KV head, 128-dim quarter). Thread t takes
+// splits i = t / 16 (mod 16) and dims 8 * (t % 16) .. +8 of the quarter, so 16
+// splits are read at once; the 16 partial sums are reduced through LDS.
 // ----------------------------------------------------------------------------
 
+constexpr int kCombDims = 128;                  // dims per workgroup
+constexpr int kCombGroups = kThreads / (kCombDims / 8);   // 16 split lanes
+
 __global__ void __launch_bounds__(kThreads) combine_kernel(DecodeParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x, kvh = blockIdx.z;
-  const int row = blockIdx.y * kWaves + wave;
-  if (row >= p.rows) return;
+  __shared__ float red[kCombGroups][kCombDims + 4];
+  __shared__ float stat[2][kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int row = blockIdx.y;
+  const int kvh = blockIdx.z / (kDv / kCombDims);
+  const int quarter = blockIdx.z % (kDv / kCombDims);
   const int slot0 = p.num_splits[b];
   const int n = p.num_splits[b + 1] - slot0;
-  if (n <= 1) return;
+  if (n <= 1 || row >= p.rows) return;
   const int s_idx = row / p.group;
   const int head = kvh * p.group + row % p.group;
-  uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + 8 * lane;
+  const int sub = tid / (kCombDims / 8), dl = tid % (kCombDims / 8);
+  const int dim0 = quarter * kCombDims + 8 * dl;
+  uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
   float* lse_out = p.lse + (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
   if (slot0 < 0 || slot0 + n > p.max_slots) {
-    const u32x4 nan4 = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    *reinterpret_cast<u32x4*>(orow) = nan4;
-    if (lane == 0) *lse_out = __builtin_nanf("");
+    if (sub == 0) *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    if (tid == 0 && quarter == 0) *lse_out = __builtin_nanf("");
     return;
   }
   const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;             // slots apart
   const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   const float* o_in = p.part_o + (static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row) * kDv
-                      + 8 * lane;
+                      + dim0;
 
+  // LSE over all splits (block-wide max, then sum)
   float mx = kNegInf;
-  for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_in[i * stride]);
+  for (int i = tid; i < n; i += kThreads) mx = fmaxf(mx, lse_in[i * stride]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) stat[0][wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(stat[0][0], stat[0][1]), fmaxf(stat[0][2], stat[0][3]));
   const bool any = mx != kNegInf;
   const float mxu = any ? mx : 0.f;
   float sum = 0.f;
-  for (int i = lane; i < n; i += 64) sum += __expf(lse_in[i * stride] - mxu);
+  for (int i = tid; i < n; i += kThreads) sum += __expf(lse_in[i * stride] - mxu);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) stat[1][wave] = sum;
+  __syncthreads();
+  sum = stat[1][0] + stat[1][1] + stat[1][2] + stat[1][3];
   const float lse = any ? mxu + __logf(sum) : kNegInf;
 
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
   if (any) {
-    for (int i = 0; i < n; ++i) {
+#pragma unroll 4
+    for (int i = sub; i < n; i += kCombGroups) {
       const float w = __expf(lse_in[i * stride] - lse);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
-      if (w != 0.f) {
-        acc[0] += w * a[0]; acc[1] += w * a[1]; acc[2] += w * a[2]; acc[3] += w * a[3];
-        acc[4] += w * c[0]; acc[5] += w * c[1]; acc[6] += w * c[2]; acc[7] += w * c[3];
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
+      if (w != 0.f) {          // a split with no allowed key has w = 0 and O = 0
+        a0 += w * x0;
+        a1 += w * x1;
       }
     }
   }
-  u32x4 outw;
-  outw[0] = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-  outw[1] = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-  outw[2] = static_cast<uint32_t>(f32_to_bf16(acc[4])) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-  outw[3] = static_cast<uint32_t>(f32_to_bf16(acc[6])) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-  *reinterpret_cast<u32x4*>(orow) = outw;
-  if (lane == 0) *lse_out = lse;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    red[sub][8 * dl + j] = a0[j];
+    red[sub][8 * dl + 4 + j] = a1[j];
+  }
+  __syncthreads();
+  if (tid < kCombDims / 8) {
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int g = 0; g < kCombGroups; ++g) acc += red[g][8 * tid + j];
+      o[j] = acc;
+    }
+    u32x4 outw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      outw[j] = static_cast<uint32_t>(f32_to_bf16(o[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(o[2 * j + 1])) << 16);
+    *reinterpret_cast<u32x4*>(p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv +
+                              quarter * kCombDims + 8 * tid) = outw;
+    if (tid == 0 && quarter == 0) *lse_out = lse;
+  }
 }
 
 template <int RB, int TG>
@@ -693,7 +784,7 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
     err = hipEventRecord(static_cast<hipEvent_t>(events[1]), stream);
     if (err != hipSuccess) return err;
   }
-  const dim3 cgrid(p.batch, (p.rows + kWaves - 1) / kWaves, p.h_kv);
+  const dim3 cgrid(p.batch, p.rows, p.h_kv * (kDv / kCombDims));
   hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -43,7 +43,7 @@ inline Plan make_plan(int heads_per_kv, int kv_format) {
   }
   p.m_tile = 16 * p.rb;
   p.m_tiles = (heads_per_kv + p.m_tile - 1) / p.m_tile;
-  p.wgs_per_cu = 2;
+  p.wgs_per_cu = 1;      // the two-page LDS ring (144-155 KB) leaves room for one workgroup per CU
   p.split_cost = 1;
   p.min_pages = 1;
   return p;
