@@ -148,8 +148,10 @@ def main():
     out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.h_q, w.s_q), dtype=torch.float32, device=dev)
     ws = torch.empty((mla.mla_workspace_bytes(w.batch, parts, M, w.h_kv),), dtype=torch.uint8, device=dev)
+    _, s_host = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts)
+    max_splits = mla.max_splits_of(s_host)
     decoders = [mla.MlaDecoder(q, kv, bt, L_dev, w.dv, meta_dev, splits_dev, w.causal, w.softmax_scale,
-                               out=out, lse=lse, workspace=ws) for kv in kvs]
+                               out=out, lse=lse, workspace=ws, max_splits=max_splits) for kv in kvs]
     stream = torch.cuda.current_stream(dev)
     hip = HipEvents()
 

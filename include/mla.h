@@ -162,6 +162,11 @@ typedef struct mla_decode_args {
   void* workspace;            /* >= mla_workspace_bytes(batch, num_parts, s_q*h_q/h_kv, h_kv) bytes, 256-B aligned */
   size_t workspace_bytes;
 
+  /* Optional hint: 0 = unknown, else the largest number of pieces of any
+     sequence (max_b num_splits[b+1] - num_splits[b]); it only selects the
+     shape of the combine kernel (results do not depend on it). */
+  int max_splits;
+
   /* Optional timing hooks (hipEvent_t or NULL): recorded on the stream before
      the split-KV kernel, after it, and after the combine kernel. */
   void* events[3];

@@ -105,7 +105,16 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int =
     pin = torch.device(device).type == "cuda"
     meta, splits = mla_get_metadata_host(cache_seqlens, heads_per_kv, h_kv, kv_format=kv_format,
                                          num_parts=num_parts, num_cus=num_cus, pin=pin)
-    return meta.to(device, non_blocking=True), splits.to(device, non_blocking=True)
+    meta_d, splits_d = meta.to(device, non_blocking=True), splits.to(device, non_blocking=True)
+    # host-side fact carried along for the decode call's combine-shape hint
+    splits_d._mla_max_splits = max_splits_of(splits)
+    return meta_d, splits_d
+
+
+def max_splits_of(num_splits_host: torch.Tensor) -> int:
+    """Largest number of pieces of any sequence, from host num_splits [batch + 1]."""
+    d = num_splits_host[1:] - num_splits_host[:-1]
+    return int(d.max()) if d.numel() else 0
 
 
 def _check_tensor(name, t, dtype, ndim, device):
@@ -127,7 +136,7 @@ class MlaDecoder:
     repeatedly (one per layer of a decode step, or a benchmark loop)."""
 
     def __init__(self, q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal=False,
-                 softmax_scale=None, *, out=None, lse=None, workspace=None, events=None):
+                 softmax_scale=None, *, out=None, lse=None, workspace=None, events=None, max_splits=None):
         dev = q.device
         if dev.type != "cuda":
             raise ValueError("q must be a CUDA (HIP) tensor")
@@ -191,6 +200,9 @@ class MlaDecoder:
         a.lse = lse.data_ptr()
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+        if max_splits is None:
+            max_splits = getattr(num_splits, "_mla_max_splits", 0)
+        a.max_splits = int(max_splits)
         self.args = a
         if events is not None:
             self.set_events(events)

@@ -55,6 +55,7 @@ class MlaDecodeArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("max_splits", ctypes.c_int),
         ("events", ctypes.c_void_p * 3),
     ]
 

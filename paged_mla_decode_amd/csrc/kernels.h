@@ -30,6 +30,7 @@ struct DecodeParams {
   float* part_o;              // [slots, h_kv, rows, 512]
   float* part_lse;            // [slots, h_kv, rows]
   int max_slots;
+  int max_splits;             // hint: largest piece count of any sequence (0 = unknown)
   int grid_wgs;               // real workgroups of the split kernel (the grid is padded to a multiple of 8)
 };
 

@@ -223,6 +223,7 @@ mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
   p.part_o = static_cast<float*>(a->workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + partial_o_bytes(slots, rows, a->h_kv));
   p.max_slots = slots;
+  p.max_splits = a->max_splits > 0 ? a->max_splits : 0;
   p.grid_wgs = static_cast<int>(wgs);
 
   hipError_t err = mla::launch_decode(p, plan, a->kv_format, static_cast<hipStream_t>(hip_stream), a->events);

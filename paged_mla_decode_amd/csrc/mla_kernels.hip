@@ -663,6 +663,429 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   wait_vm_all();   // nothing may still be landing in LDS when the workgroup ends
 }
 
+// Per-lane byte offset, within one page of one KV head, of the j-th direct
+// load of wave `wave` (LDS slot byte x = 1024 * (wave + 4j) + 16 * lane),
+// computed when issued instead of being held in registers.
+template <int FMT>
+struct LoadOffsets {
+  int wave, lane, st;
+  __device__ __forceinline__ uint32_t operator[](int j) const {
+    const int x = 1024 * (wave + kWaves * j) + 16 * lane;
+    if constexpr (FMT == kFmtFp8) {
+      const int t = x / kFp8Record;
+      return static_cast<uint32_t>(t * st + (x - t * kFp8Record));
+    } else {
+      const int pc = x >> 4;
+      const int t = pc / 72;
+      return static_cast<uint32_t>(t * st + 16 * ((pc - 72 * t) ^ swz(t)));
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------
+// Wide-row variant (more than 64 rows per KV head): 4 waves x 32 rows = 128
+// rows per workgroup. Each wave holds two 16-row blocks that share every K and
+// V operand read, which halves LDS traffic per FLOP against 16 rows per wave;
+// a page is processed as two halves of 32 tokens to keep the register budget
+// (O accumulators 256 AGPRs, Q^T 144 VGPRs) within one wave per SIMD.
+// ----------------------------------------------------------------------------
+
+template <int FMT>
+__device__ __forceinline__ void page_step_wide(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
+                                               uint8_t* __restrict__ conv, const uint8_t* next_src,
+                                               const LoadOffsets<FMT>& ld_off, const Lane& ln, int L, const int (&last_ok)[2],
+                                               int pi, bool this_ok, float scale_log2, const bf16x8 (&qf)[2][18],
+                                               f32x4 (&acc)[2][32], float (&m_run)[2], float (&l_run)[2]) {
+  constexpr bool kFp8 = (FMT == kFmtFp8);
+  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
+  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
+  const int tid = ln.tid, r16 = ln.r16, q4 = ln.q4;
+
+  const int valid = min(L - pi * kPage, kPage);
+  const uint8_t* page;
+  const float* scale_tab = nullptr;
+  if constexpr (kFp8) {
+    float* scales = reinterpret_cast<float*>(conv + kPageBytes);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int item = tid + kThreads * j;
+      const int t = item >> 5, ch = item & 31;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 16 * ch);
+      const bool keep = this_ok && t < valid;
+      u32x4 lo, hi;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t a = w[i], c = w[i + 2];
+        lo[2 * i] = e4m3fn_to_bf16_bits(a) | (e4m3fn_to_bf16_bits(a >> 8) << 16);
+        lo[2 * i + 1] = e4m3fn_to_bf16_bits(a >> 16) | (e4m3fn_to_bf16_bits(a >> 24) << 16);
+        hi[2 * i] = e4m3fn_to_bf16_bits(c) | (e4m3fn_to_bf16_bits(c >> 8) << 16);
+        hi[2 * i + 1] = e4m3fn_to_bf16_bits(c >> 16) | (e4m3fn_to_bf16_bits(c >> 24) << 16);
+      }
+      if (!keep) {
+        lo = u32x4{0u, 0u, 0u, 0u};
+        hi = lo;
+      }
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch)) = lo;
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch + 1)) = hi;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int item = tid + kThreads * j;
+      const int t = item >> 3, rr = item & 7;
+      u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 528 + 16 * rr);
+      if (!(this_ok && t < valid)) w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 64 + rr)) = w;
+    }
+    {
+      const int t = tid >> 2, c = tid & 3;
+      const float sv = *reinterpret_cast<const float*>(cur + t * kFp8Record + 512 + 4 * c);
+      scales[tid] = (this_ok && t < valid) ? sv : 0.f;
+    }
+    lds_barrier();
+    page = conv;
+    scale_tab = scales;
+  } else {
+    if (valid < kPage || !this_ok) {
+      const int z0 = this_ok ? valid : 0;
+      for (int x = z0 * kRowBytes + 16 * tid; x < kPageBytes; x += 16 * kThreads)
+        *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
+      lds_barrier();
+    }
+    page = cur;
+  }
+
+  if (next_src != nullptr) {
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const int k = ln.wave + kWaves * j;
+      if (k < kLoads)
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(next_src + ld_off[j]), LDS_PTR(void, nxt + 1024 * k), 16, 0, 0);
+    }
+  }
+
+  const int kb0 = 16 * ((q4) ^ ln.sw_k), kb1 = 16 * ((4 + q4) ^ ln.sw_k);
+  int vb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vb[r] = 16 * ((2 * r + ln.tr_hh) ^ ln.sw_v) + 8 * ln.tr_half;
+
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {             // two halves of 32 tokens: tiles 2u, 2u + 1
+    f32x4 s[2][2];                          // [tile][row block]
+    const uint8_t* krow0 = page + (32 * u + r16) * kRowBytes;
+    auto kload = [&](int c, int tt) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(krow0 + 16 * tt * kRowBytes + 128 * (c >> 1) + ((c & 1) ? kb1 : kb0));
+    };
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 grp[2][5];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int g = 0; g < 5; ++g) grp[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int g = 0; g < 5; ++g) {
+            if (g == 4 && j >= 2) continue;
+            const int c = (g < 4) ? 4 * g + j : 16 + j;
+            const bf16x8 a = kload(c, tt);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              grp[rb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rb][c], grp[rb][g], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(scale_tab + 4 * (32 * u + 16 * tt + 4 * q4 + i));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            s[tt][rb][i] = grp[rb][4][i] + sc[0] * grp[rb][0][i] + sc[1] * grp[rb][1][i] + sc[2] * grp[rb][2][i] +
+                           sc[3] * grp[rb][3][i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      constexpr int kDepth = 2;
+      bf16x8 kbuf[kDepth][2];
+#pragma unroll
+      for (int c = 0; c < kDepth - 1; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) kbuf[c][tt] = kload(c, tt);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kDepth - 1), 0);
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        if (c + kDepth - 1 < 18) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) kbuf[(c + kDepth - 1) % kDepth][tt] = kload(c + kDepth - 1, tt);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            s[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c % kDepth][tt], qf[rb][c], s[tt][rb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (c + kDepth - 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+
+    // mask + online softmax, per row block
+    const int tok_base = pi * kPage + 32 * u + 4 * q4;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tok_base + 16 * tt + i;
+          const bool ok = tok < L && tok <= last_ok[rb];
+          const float v = ok ? s[tt][rb][i] * scale_log2 : kNegInf;
+          s[tt][rb][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = max4lanes(mx);
+      if (mx > m_run[rb] + kRescaleSlack) {
+        const float alpha = fast_exp2(m_run[rb] - mx);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 32; ++d) acc[rb][d] *= alpha;
+        m_run[rb] = mx;
+      }
+      const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
+      float psum = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(s[tt][rb][i] - m_use);
+          s[tt][rb][i] = e;
+          psum += e;
+        }
+      }
+      l_run[rb] += psum;
+    }
+
+    // O^T += V^T P^T for both row blocks; one pair of transposed reads feeds two MFMAs
+    const uint8_t* v0 = page + (32 * u + ln.tr_tok) * kRowBytes;
+    auto vload = [&](int d) -> bf16x8 {
+      const uint8_t* a0 = v0 + 128 * (d >> 2) + vb[d & 3];
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    constexpr int NG = kFp8 ? 4 : 1;         // scale groups (8 dim blocks each for fp8)
+    constexpr int DPG = 32 / NG;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = s[0][rb][j], x1 = s[1][rb][j];
+          if constexpr (kFp8) {
+            x0 *= scale_tab[4 * (32 * u + 4 * q4 + j) + g];
+            x1 *= scale_tab[4 * (32 * u + 16 + 4 * q4 + j) + g];
+          }
+          pb[rb][j] = static_cast<__bf16>(x0);
+          pb[rb][4 + j] = static_cast<__bf16>(x1);
+        }
+      }
+      constexpr int kAhead = 2;
+      bf16x8 va[kAhead];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) va[k] = vload(g * DPG + k);
+#pragma unroll
+      for (int k = 0; k < DPG; ++k) {
+        const int d = g * DPG + k;
+        const bf16x8 a = va[k % kAhead];
+        if (k + kAhead < DPG) va[k % kAhead] = vload(d + kAhead);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb], acc[rb][d], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) splitkv_wide_kernel(DecodeParams p) {
+  constexpr int M_TILE = 128;
+  constexpr bool kFp8 = (FMT == kFmtFp8);
+  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
+  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
+  constexpr int kSlotBytes = kFp8 ? kRawPageBytes : kPageBytes;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kFp8 ? kLdsFp8 : kLdsBf16];
+  uint8_t* const ring = smem;
+  uint8_t* const conv = smem + 2 * kRawPageBytes;
+
+  Lane ln;
+  ln.tid = threadIdx.x;
+  ln.lane = ln.tid & 63;
+  ln.wave = ln.tid >> 6;
+  ln.tg = 0;
+  ln.r16 = ln.lane & 15;
+  ln.q4 = ln.lane >> 4;
+  ln.sw_k = swz(ln.r16);
+  ln.tr_tok = 4 * ln.q4 + (ln.r16 >> 2);
+  ln.sw_v = swz(ln.tr_tok);
+  ln.tr_half = ln.r16 & 1;
+  ln.tr_hh = (ln.r16 & 3) >> 1;
+  const int lane = ln.lane, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+
+  const int per_xcd = gridDim.x / 8;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= p.grid_wgs) return;
+  const int m_tiles = (p.rows + M_TILE - 1) / M_TILE;
+  const int mt = logical % m_tiles;
+  const int kvh = (logical / m_tiles) % p.h_kv;
+  const int part = logical / (m_tiles * p.h_kv);
+
+  Range r;
+  {
+    const int32_t* meta = p.meta + part * kMetaInts;
+    r.begin_b = meta[0];
+    r.begin_page = meta[1];
+    r.end_b = min(meta[2], p.batch - 1);
+    r.end_page = meta[3];
+    r.split0 = meta[4];
+  }
+  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
+
+  int row[2], s_idx[2], head[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    row[rb] = mt * M_TILE + 32 * wave + 16 * rb + r16;
+    row_ok[rb] = row[rb] < p.rows;
+    s_idx[rb] = row_ok[rb] ? row[rb] / p.group : 0;
+    head[rb] = kvh * p.group + (row_ok[rb] ? row[rb] % p.group : 0);
+  }
+
+  const LoadOffsets<FMT> ld_off{wave, lane, static_cast<int>(p.kv_st)};
+  const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
+  auto page_src = [&](int b, int pi) -> const uint8_t* {
+    const int pg = p.block_table[static_cast<int64_t>(b) * p.bt_stride + pi];
+    if (pg < 0 || pg >= p.num_pages) return nullptr;
+    return kv_head + static_cast<int64_t>(pg) * p.kv_sp;
+  };
+
+  int slot = 0;
+  bool load_ok = true;
+  {
+    int nb, npi;
+    next_with_pages(p, r, r.begin_b, nb, npi);
+    if (nb <= r.end_b) {
+      const uint8_t* src = page_src(nb, npi);
+      load_ok = src != nullptr;
+      if (load_ok) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+          const int k = wave + kWaves * j;
+          if (k < kLoads)
+            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src + ld_off[j]), LDS_PTR(void, ring + 1024 * k), 16, 0, 0);
+        }
+      }
+    }
+  }
+
+  for (int b = r.begin_b; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    seq_pages(p, r, b, L, pg0, pg1);
+    const int split_idx = (b == r.begin_b) ? r.split0 : 0;
+    const int slot0 = p.num_splits[b];
+    const int nsplit = p.num_splits[b + 1] - slot0;
+    int last_ok[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) last_ok[rb] = p.causal ? (L - p.s_q + s_idx[rb]) : (L - 1);
+
+    bf16x8 qf[2][18];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const uint16_t* qrow = p.q + b * p.q_sb + s_idx[rb] * p.q_ss + head[rb] * p.q_sh;
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        u32x4 v = row_ok[rb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+        qf[rb][c] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    wait_vm_all();
+
+    float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+    f32x4 acc[2][32];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int d = 0; d < 32; ++d) acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+
+    for (int pi = pg0; pi < pg1; ++pi) {
+      const bool this_ok = load_ok;
+      bad |= !this_ok;
+      wait_vm_all();
+      lds_barrier();
+      const uint8_t* next_src = nullptr;
+      {
+        int nb = b, npi = pi + 1;
+        if (npi >= pg1) next_with_pages(p, r, b + 1, nb, npi);
+        if (nb <= r.end_b) {
+          next_src = page_src(nb, npi);
+          load_ok = next_src != nullptr;
+        }
+      }
+      page_step_wide<FMT>(ring + slot * kSlotBytes, ring + (slot ^ 1) * kSlotBytes, conv, next_src, ld_off, ln, L,
+                          last_ok, pi, this_ok, p.scale_log2, qf, acc, m_run, l_run);
+      slot ^= 1;
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float l_row = sum4lanes(l_run[rb]);
+      if (!row_ok[rb]) continue;
+      const bool ok = !bad;
+      const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
+      float lse = (l_row > 0.f) ? (m_run[rb] + __log2f(l_row)) * kLn2 : kNegInf;
+      if (!ok) lse = __builtin_nanf("");
+      const float nan = __builtin_nanf("");
+      if (nsplit == 1) {
+        uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx[rb]) * p.h_q + head[rb]) * kDv + 4 * q4;
+#pragma unroll
+        for (int d = 0; d < 32; ++d) {
+          u32x2 w;
+          const float x0 = ok ? acc[rb][d][0] * inv : nan;
+          const float x1 = ok ? acc[rb][d][1] * inv : nan;
+          const float x2 = ok ? acc[rb][d][2] * inv : nan;
+          const float x3 = ok ? acc[rb][d][3] * inv : nan;
+          w[0] = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
+          w[1] = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
+          *reinterpret_cast<u32x2*>(orow + 16 * d) = w;
+        }
+        if (q4 == 0) p.lse[(static_cast<int64_t>(b) * p.h_q + head[rb]) * p.s_q + s_idx[rb]] = lse;
+      } else {
+        const int pslot = slot0 + split_idx;
+        if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
+          float* prow =
+              p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row[rb]) * kDv + 4 * q4;
+#pragma unroll
+          for (int d = 0; d < 32; ++d) {
+            f32x4 v = acc[rb][d] * inv;
+            if (!ok) v = f32x4{nan, nan, nan, nan};
+            *reinterpret_cast<f32x4*>(prow + 16 * d) = v;
+          }
+          if (q4 == 0) p.part_lse[(static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row[rb]] = lse;
+        }
+      }
+    }
+  }
+  wait_vm_all();
+}
+
 // ----------------------------------------------------------------------------
 // Combine: LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i
 // One workgroup per (sequence, row, KV head, 128-dim quarter). Thread t takes
@@ -757,6 +1180,69 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(DecodeParams p) {
   }
 }
 
+// Narrow combine, for sequences cut into few pieces: one workgroup per
+// (sequence, 16 rows, KV head, 128-dim quarter); 16 lanes per row, 8 dims per
+// lane, the pieces walked in a loop with independent loads.
+__global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) {
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int row = blockIdx.y * 16 + tid / 16;
+  const int l16 = tid & 15;
+  const int kvh = blockIdx.z / (kDv / kCombDims);
+  const int quarter = blockIdx.z % (kDv / kCombDims);
+  const int slot0 = p.num_splits[b];
+  const int n = p.num_splits[b + 1] - slot0;
+  if (n <= 1 || row >= p.rows) return;
+  const int s_idx = row / p.group;
+  const int head = kvh * p.group + row % p.group;
+  const int dim0 = quarter * kCombDims + 8 * l16;
+  uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
+  float* lse_out = p.lse + (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
+  if (slot0 < 0 || slot0 + n > p.max_slots) {
+    *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    if (l16 == 0 && quarter == 0) *lse_out = __builtin_nanf("");
+    return;
+  }
+  const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;
+  const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
+  const float* o_in = p.part_o + (static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row) * kDv
+                      + dim0;
+  float mx = kNegInf;
+  for (int i = l16; i < n; i += 16) mx = fmaxf(mx, lse_in[i * stride]);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const bool any = mx != kNegInf;
+  const float mxu = any ? mx : 0.f;
+  float sum = 0.f;
+  for (int i = l16; i < n; i += 16) sum += __expf(lse_in[i * stride] - mxu);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  const float lse = any ? mxu + __logf(sum) : kNegInf;
+  f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  if (any) {
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) {
+      const float w = __expf(lse_in[i * stride] - lse);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
+      if (w != 0.f) {
+        a0 += w * x0;
+        a1 += w * x1;
+      }
+    }
+  }
+  u32x4 outw;
+  outw[0] = static_cast<uint32_t>(f32_to_bf16(a0[0])) | (static_cast<uint32_t>(f32_to_bf16(a0[1])) << 16);
+  outw[1] = static_cast<uint32_t>(f32_to_bf16(a0[2])) | (static_cast<uint32_t>(f32_to_bf16(a0[3])) << 16);
+  outw[2] = static_cast<uint32_t>(f32_to_bf16(a1[0])) | (static_cast<uint32_t>(f32_to_bf16(a1[1])) << 16);
+  outw[3] = static_cast<uint32_t>(f32_to_bf16(a1[2])) | (static_cast<uint32_t>(f32_to_bf16(a1[3])) << 16);
+  *reinterpret_cast<u32x4*>(orow) = outw;
+  if (l16 == 0 && quarter == 0) *lse_out = lse;
+}
+
+// Pieces per sequence up to which the narrow combine is used.
+constexpr int kNarrowCombineMax = 8;
+
 template <int RB, int TG>
 hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStream_t stream) {
   if (kv_format == kFmtFp8)
@@ -776,16 +1262,31 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
     err = hipEventRecord(static_cast<hipEvent_t>(events[0]), stream);
     if (err != hipSuccess) return err;
   }
-  if (plan.rb == 1) err = launch_split<1, 4>(p, kv_format, grid, stream);
-  else if (plan.rb == 2) err = launch_split<2, 2>(p, kv_format, grid, stream);
-  else err = launch_split<4, 1>(p, kv_format, grid, stream);
+  if (plan.wide) {
+    if (kv_format == kFmtFp8)
+      hipLaunchKernelGGL(splitkv_wide_kernel<kFmtFp8>, dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(splitkv_wide_kernel<kFmtBf16>, dim3(grid), dim3(kThreads), 0, stream, p);
+    err = hipGetLastError();
+  } else if (plan.rb == 1) {
+    err = launch_split<1, 4>(p, kv_format, grid, stream);
+  } else if (plan.rb == 2) {
+    err = launch_split<2, 2>(p, kv_format, grid, stream);
+  } else {
+    err = launch_split<4, 1>(p, kv_format, grid, stream);
+  }
   if (err != hipSuccess) return err;
   if (events && events[1]) {
     err = hipEventRecord(static_cast<hipEvent_t>(events[1]), stream);
     if (err != hipSuccess) return err;
   }
-  const dim3 cgrid(p.batch, p.rows, p.h_kv * (kDv / kCombDims));
-  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, stream, p);
+  if (p.max_splits > 0 && p.max_splits <= kNarrowCombineMax) {
+    const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
+    hipLaunchKernelGGL(combine_rows_kernel, cgrid, dim3(kThreads), 0, stream, p);
+  } else {
+    const dim3 cgrid(p.batch, p.rows, p.h_kv * (kDv / kCombDims));
+    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, stream, p);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (events && events[2]) {

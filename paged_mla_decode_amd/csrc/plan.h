@@ -22,6 +22,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
 struct Plan {
+  int wide;        // 1: 4 waves x 32 rows (128-row tiles), for more than 64 rows
   int rb;          // 16-row blocks per workgroup
   int tg;          // token groups per page (rb * tg == kWaves)
   int m_tile;      // rows per workgroup
