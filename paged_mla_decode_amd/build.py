@@ -7,16 +7,29 @@ paged_mla_decode_amd/libmla.so, which the binding loads.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.cpp", "scheduler.cpp", "mla_kernels.hip"]
+SOURCES = ["mla_api.cpp", "scheduler.cpp", "mla_kernels.hip", "mla_kernels_x.hip"]
+# Per-file flags. The 128-row kernel keeps 256 fp32 accumulators per lane next
+# to its Q operands; selecting the VGPR form of MFMA lets the register
+# allocator place accumulators in either register file, which removes the
+# spills the all-AGPR form causes there.
+FILE_FLAGS = {"mla_kernels_x.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms stay off: plain float code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
 
 
 def hipcc_path() -> str:
@@ -26,29 +39,43 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm under /opt/rocm)")
 
 
-def compile_command(out: str = LIB_PATH, extra=()) -> list:
-    return [
-        hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU forms stay off: plain float code only
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-command-line-argument",
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", out, *extra,
-    ]
+def compile_commands(objdir: str, out: str = LIB_PATH) -> tuple:
+    """One compile command per source (object files in objdir) and the link command."""
+    hipcc = hipcc_path()
+    compiles, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        compiles.append([hipcc, *COMMON_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+    return compiles, link
+
+
+def _run(cmd: list) -> tuple:
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    return proc.returncode, out
 
 
 def build(verbose: bool = False) -> str:
     """Compile the library (always; a stale .so is replaced atomically)."""
     tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+    with tempfile.TemporaryDirectory(prefix="mla_build_") as objdir:
+        compiles, link = compile_commands(objdir, tmp)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(compiles)) as pool:
+            results = list(pool.map(_run, compiles))
+        for cmd, (rc, out) in zip(compiles, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+                if out.strip():
+                    print(out)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}) on {cmd[-3]}:\n{out}")
+        rc, out = _run(link)
+        if verbose:
+            print(" ".join(link), flush=True)
+        if rc != 0:
+            raise RuntimeError(f"hipcc link failed ({rc}):\n{out}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

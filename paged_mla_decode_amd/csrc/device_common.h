@@ -1,0 +1,157 @@
+// device_common.h -- device helpers shared by the split-KV kernels: vector
+// types, the swizzled LDS row layout, FP8 code conversion, lane reductions,
+// iteration over a KV range, and the LDS-only barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace mla {
+namespace dev {
+
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
+
+constexpr int kRowBytes = kDqk * 2;                  // 1152: one bf16 token row
+constexpr int kPageBytes = kPage * kRowBytes;        // 73728 = 72 x 1 KB
+constexpr int kRawPageBytes = kPage * kFp8Record;    // 41984 = 41 x 1 KB
+constexpr int kBf16Loads = kPageBytes / 1024;        // 72 direct-load instructions per page
+constexpr int kFp8Loads = kRawPageBytes / 1024;      // 41
+constexpr int kFmtFp8 = 1;
+constexpr int kFmtBf16 = 0;
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+
+// LDS budget (bytes): bf16 -- two page slots; fp8 -- two raw slots, one bf16
+// page, per-token scales.
+constexpr int kLdsBf16 = 2 * kPageBytes;                                   // 147456
+constexpr int kLdsFp8 = 2 * kRawPageBytes + kPageBytes + kPage * 4 * 4;    // 158720
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));   // round to nearest even
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Swizzle of the 16-byte chunk index inside a token row (stays inside its
+// aligned group of 8 chunks): K reads (8 consecutive tokens, one chunk) and
+// transposed V reads (4 consecutive tokens, 2 chunks) both spread over 8 groups.
+__device__ __forceinline__ int swz(int token) { return ((token & 3) << 1) | ((token >> 2) & 1); }
+
+__device__ __forceinline__ int chunk_off(int token, int chunk) { return token * kRowBytes + 16 * (chunk ^ swz(token)); }
+
+// OCP E4M3FN code (low 8 bits of c) -> bf16 bits, exactly. Codes 0x7F/0xFF -> NaN.
+__device__ __forceinline__ uint32_t e4m3fn_to_bf16_bits(uint32_t c) {
+  const uint32_t mag = c & 0x7Fu;
+  uint32_t v;
+  if (mag >= 8u) {
+    v = (mag << 4) + 0x3C00u;                      // exponent e - 7 + 127, mantissa m << 4
+  } else {
+    v = __float_as_uint(static_cast<float>(mag) * 0.001953125f) >> 16;   // m * 2^-9, exact in bf16
+  }
+  v = (mag == 0x7Fu) ? 0x7FC0u : v;
+  return v | ((c & 0x80u) << 8);
+}
+
+// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt fields left at "no wait"),
+// so the compiler's own wait-count tracking sees it.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ float max4lanes(float v) {   // over the 4 lanes sharing lane % 16
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float sum4lanes(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// ----------------------------------------------------------------------------
+// Page iteration over one KV range: sequences begin_b..end_b, pages [pg0, pg1)
+// of each, in order. Zero-page sequences still get their epilogue.
+// ----------------------------------------------------------------------------
+// Read of launch-invariant metadata (sequence lengths, block table, ranges,
+// piece counts) through the constant address space: with a wave-uniform index
+// this becomes a scalar load, waited on with lgkmcnt, so it never waits for
+// the page loads in flight (a vector load would need vmcnt(0)).
+__device__ __forceinline__ int ld_meta(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)(ptr);
+}
+
+struct Range {
+  int begin_b, begin_page, end_b, end_page, split0;
+};
+
+__device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1) {
+  const int max_len = p.max_blocks * kPage;
+  int len = ld_meta(p.seqlens + b);
+  len = len < 0 ? 0 : (len > max_len ? max_len : len);
+  L = len;
+  const int np = (len + kPage - 1) / kPage;
+  pg0 = (b == r.begin_b) ? max(r.begin_page, 0) : 0;
+  pg1 = (b == r.end_b) ? min(r.end_page, np) : np;
+  if (pg0 > pg1) pg0 = pg1;
+}
+
+// First (sequence, page) at or after sequence b that has a page in the range; nb = end_b + 1 if none.
+__device__ __forceinline__ void next_with_pages(const DecodeParams& p, const Range& r, int b, int& nb, int& npg) {
+  for (; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    seq_pages(p, r, b, L, pg0, pg1);
+    if (pg0 < pg1) {
+      nb = b;
+      npg = pg0;
+      return;
+    }
+  }
+  nb = r.end_b + 1;
+  npg = 0;
+}
+
+// Barrier that orders LDS only: unlike __syncthreads it does not wait for the
+// page loads still in flight into the other ring slot.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier for LDS exchanges made while direct page loads are in
+// flight. A release fence on LDS also waits for those loads (they write LDS),
+// so this one waits for this wave's own LDS accesses only (lgkmcnt(0);
+// vmcnt and expcnt fields at their no-wait maxima); the asm memory clobber
+// keeps the compiler from moving memory accesses across it. The caller
+// orders the direct loads itself (s_waitcnt vmcnt before the barrier that
+// publishes them).
+__device__ __forceinline__ void lds_barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Lane-constant indices of one wavefront.
+struct Lane {
+  int tid, lane, wave, tg, r16, q4;
+  int sw_k;              // swizzle of K rows read by this lane (token 16*tile + r16)
+  int tr_tok, sw_v;      // V^T transposed reads: token tb + tr_tok (+16), its swizzle
+  int tr_half, tr_hh;    // 8-byte half and chunk parity of the transposed read
+};
+
+// Exact online-softmax rescale is deferred until the running max grows by
+// more than this (log2 units): P stays <= 2^8, far from fp32/bf16 limits, and
+// O / l and LSE = m + log2 l are unchanged.
+constexpr float kRescaleSlack = 8.f;
+
+}  // namespace dev
+}  // namespace mla

@@ -34,6 +34,9 @@ struct DecodeParams {
   int grid_wgs;               // real workgroups of the split kernel (the grid is padded to a multiple of 8)
 };
 
+// The 128-row split kernel (mla_kernels_x.hip; bf16 pages, grid padded to a multiple of 8).
+hipError_t launch_split_x(const DecodeParams& p, int grid, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]);
 

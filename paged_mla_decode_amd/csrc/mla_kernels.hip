@@ -32,134 +32,17 @@
 
 #include <cstdint>
 
+#include "device_common.h"
 #include "kernels.h"
 
 namespace mla {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-#define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
-
-constexpr int kRowBytes = kDqk * 2;                  // 1152: one bf16 token row
-constexpr int kPageBytes = kPage * kRowBytes;        // 73728 = 72 x 1 KB
-constexpr int kRawPageBytes = kPage * kFp8Record;    // 41984 = 41 x 1 KB
-constexpr int kBf16Loads = kPageBytes / 1024;        // 72 direct-load instructions per page
-constexpr int kFp8Loads = kRawPageBytes / 1024;      // 41
-constexpr int kFmtFp8 = 1;
-constexpr int kFmtBf16 = 0;
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.693147180559945309f;
-
-// LDS budget (bytes): bf16 -- two page slots; fp8 -- two raw slots, one bf16
-// page, per-token scales.
-constexpr int kLdsBf16 = 2 * kPageBytes;                                   // 147456
-constexpr int kLdsFp8 = 2 * kRawPageBytes + kPageBytes + kPage * 4 * 4;    // 158720
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));   // round to nearest even
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Swizzle of the 16-byte chunk index inside a token row (stays inside its
-// aligned group of 8 chunks): K reads (8 consecutive tokens, one chunk) and
-// transposed V reads (4 consecutive tokens, 2 chunks) both spread over 8 groups.
-__device__ __forceinline__ int swz(int token) { return ((token & 3) << 1) | ((token >> 2) & 1); }
-
-__device__ __forceinline__ int chunk_off(int token, int chunk) { return token * kRowBytes + 16 * (chunk ^ swz(token)); }
-
-// OCP E4M3FN code (low 8 bits of c) -> bf16 bits, exactly. Codes 0x7F/0xFF -> NaN.
-__device__ __forceinline__ uint32_t e4m3fn_to_bf16_bits(uint32_t c) {
-  const uint32_t mag = c & 0x7Fu;
-  uint32_t v;
-  if (mag >= 8u) {
-    v = (mag << 4) + 0x3C00u;                      // exponent e - 7 + 127, mantissa m << 4
-  } else {
-    v = __float_as_uint(static_cast<float>(mag) * 0.001953125f) >> 16;   // m * 2^-9, exact in bf16
-  }
-  v = (mag == 0x7Fu) ? 0x7FC0u : v;
-  return v | ((c & 0x80u) << 8);
-}
-
-// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt fields left at "no wait"),
-// so the compiler's own wait-count tracking sees it.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-__device__ __forceinline__ float max4lanes(float v) {   // over the 4 lanes sharing lane % 16
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-
-__device__ __forceinline__ float sum4lanes(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
-
-// ----------------------------------------------------------------------------
-// Page iteration over one KV range: sequences begin_b..end_b, pages [pg0, pg1)
-// of each, in order. Zero-page sequences still get their epilogue.
-// ----------------------------------------------------------------------------
-struct Range {
-  int begin_b, begin_page, end_b, end_page, split0;
-};
-
-__device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1) {
-  const int max_len = p.max_blocks * kPage;
-  int len = p.seqlens[b];
-  len = len < 0 ? 0 : (len > max_len ? max_len : len);
-  L = len;
-  const int np = (len + kPage - 1) / kPage;
-  pg0 = (b == r.begin_b) ? max(r.begin_page, 0) : 0;
-  pg1 = (b == r.end_b) ? min(r.end_page, np) : np;
-  if (pg0 > pg1) pg0 = pg1;
-}
-
-// First (sequence, page) at or after sequence b that has a page in the range; nb = end_b + 1 if none.
-__device__ __forceinline__ void next_with_pages(const DecodeParams& p, const Range& r, int b, int& nb, int& npg) {
-  for (; b <= r.end_b; ++b) {
-    int L, pg0, pg1;
-    seq_pages(p, r, b, L, pg0, pg1);
-    if (pg0 < pg1) {
-      nb = b;
-      npg = pg0;
-      return;
-    }
-  }
-  nb = r.end_b + 1;
-  npg = 0;
-}
+using namespace dev;
 
 // ----------------------------------------------------------------------------
 // Split-KV kernel
 // ----------------------------------------------------------------------------
-
-// Barrier that orders LDS only: unlike __syncthreads it does not wait for the
-// page loads still in flight into the other ring slot.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Lane-constant indices of one wavefront.
-struct Lane {
-  int tid, lane, wave, tg, r16, q4;
-  int sw_k;              // swizzle of K rows read by this lane (token 16*tile + r16)
-  int tr_tok, sw_v;      // V^T transposed reads: token tb + tr_tok (+16), its swizzle
-  int tr_half, tr_hh;    // 8-byte half and chunk parity of the transposed read
-};
-
-// Exact online-softmax rescale is deferred until the running max grows by
-// more than this (log2 units): P stays <= 2^8, far from fp32/bf16 limits, and
-// O / l and LSE = m + log2 l are unchanged.
-constexpr float kRescaleSlack = 8.f;
 
 // One page of the pipeline. `cur` holds the page (bf16 rows, or raw FP8
 // records), `nxt` is the other ring slot and receives the next page, `conv`
@@ -466,11 +349,11 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   Range r;
   {
     const int32_t* meta = p.meta + part * kMetaInts;
-    r.begin_b = meta[0];
-    r.begin_page = meta[1];
-    r.end_b = min(meta[2], p.batch - 1);
-    r.end_page = meta[3];
-    r.split0 = meta[4];
+    r.begin_b = ld_meta(meta + 0);
+    r.begin_page = ld_meta(meta + 1);
+    r.end_b = min(ld_meta(meta + 2), p.batch - 1);
+    r.end_page = ld_meta(meta + 3);
+    r.split0 = ld_meta(meta + 4);
   }
   if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
 
@@ -500,7 +383,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   // Global address of page `pi` of sequence `b`; nullptr for a block-table
   // entry outside the pool (never dereferenced).
   auto page_src = [&](int b, int pi) -> const uint8_t* {
-    const int pg = p.block_table[static_cast<int64_t>(b) * p.bt_stride + pi];
+    const int pg = ld_meta(p.block_table + static_cast<int64_t>(b) * p.bt_stride + pi);
     if (pg < 0 || pg >= p.num_pages) return nullptr;
     return kv_head + static_cast<int64_t>(pg) * p.kv_sp;
   };
@@ -529,8 +412,8 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     int L, pg0, pg1;
     seq_pages(p, r, b, L, pg0, pg1);
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
-    const int slot0 = p.num_splits[b];
-    const int nsplit = p.num_splits[b + 1] - slot0;
+    const int slot0 = ld_meta(p.num_splits + b);
+    const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
     const int last_allowed = p.causal ? (L - p.s_q + s_idx) : (L - 1);
 
     // Q^T operand: 18 chunks of 8 dims (dims 32c + 8*q4 .. +8) of this lane's row.
@@ -663,429 +546,6 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   wait_vm_all();   // nothing may still be landing in LDS when the workgroup ends
 }
 
-// Per-lane byte offset, within one page of one KV head, of the j-th direct
-// load of wave `wave` (LDS slot byte x = 1024 * (wave + 4j) + 16 * lane),
-// computed when issued instead of being held in registers.
-template <int FMT>
-struct LoadOffsets {
-  int wave, lane, st;
-  __device__ __forceinline__ uint32_t operator[](int j) const {
-    const int x = 1024 * (wave + kWaves * j) + 16 * lane;
-    if constexpr (FMT == kFmtFp8) {
-      const int t = x / kFp8Record;
-      return static_cast<uint32_t>(t * st + (x - t * kFp8Record));
-    } else {
-      const int pc = x >> 4;
-      const int t = pc / 72;
-      return static_cast<uint32_t>(t * st + 16 * ((pc - 72 * t) ^ swz(t)));
-    }
-  }
-};
-
-// ----------------------------------------------------------------------------
-// Wide-row variant (more than 64 rows per KV head): 4 waves x 32 rows = 128
-// rows per workgroup. Each wave holds two 16-row blocks that share every K and
-// V operand read, which halves LDS traffic per FLOP against 16 rows per wave;
-// a page is processed as two halves of 32 tokens to keep the register budget
-// (O accumulators 256 AGPRs, Q^T 144 VGPRs) within one wave per SIMD.
-// ----------------------------------------------------------------------------
-
-template <int FMT>
-__device__ __forceinline__ void page_step_wide(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
-                                               uint8_t* __restrict__ conv, const uint8_t* next_src,
-                                               const LoadOffsets<FMT>& ld_off, const Lane& ln, int L, const int (&last_ok)[2],
-                                               int pi, bool this_ok, float scale_log2, const bf16x8 (&qf)[2][18],
-                                               f32x4 (&acc)[2][32], float (&m_run)[2], float (&l_run)[2]) {
-  constexpr bool kFp8 = (FMT == kFmtFp8);
-  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
-  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
-  const int tid = ln.tid, r16 = ln.r16, q4 = ln.q4;
-
-  const int valid = min(L - pi * kPage, kPage);
-  const uint8_t* page;
-  const float* scale_tab = nullptr;
-  if constexpr (kFp8) {
-    float* scales = reinterpret_cast<float*>(conv + kPageBytes);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int item = tid + kThreads * j;
-      const int t = item >> 5, ch = item & 31;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 16 * ch);
-      const bool keep = this_ok && t < valid;
-      u32x4 lo, hi;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t a = w[i], c = w[i + 2];
-        lo[2 * i] = e4m3fn_to_bf16_bits(a) | (e4m3fn_to_bf16_bits(a >> 8) << 16);
-        lo[2 * i + 1] = e4m3fn_to_bf16_bits(a >> 16) | (e4m3fn_to_bf16_bits(a >> 24) << 16);
-        hi[2 * i] = e4m3fn_to_bf16_bits(c) | (e4m3fn_to_bf16_bits(c >> 8) << 16);
-        hi[2 * i + 1] = e4m3fn_to_bf16_bits(c >> 16) | (e4m3fn_to_bf16_bits(c >> 24) << 16);
-      }
-      if (!keep) {
-        lo = u32x4{0u, 0u, 0u, 0u};
-        hi = lo;
-      }
-      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch)) = lo;
-      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch + 1)) = hi;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int item = tid + kThreads * j;
-      const int t = item >> 3, rr = item & 7;
-      u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 528 + 16 * rr);
-      if (!(this_ok && t < valid)) w = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 64 + rr)) = w;
-    }
-    {
-      const int t = tid >> 2, c = tid & 3;
-      const float sv = *reinterpret_cast<const float*>(cur + t * kFp8Record + 512 + 4 * c);
-      scales[tid] = (this_ok && t < valid) ? sv : 0.f;
-    }
-    lds_barrier();
-    page = conv;
-    scale_tab = scales;
-  } else {
-    if (valid < kPage || !this_ok) {
-      const int z0 = this_ok ? valid : 0;
-      for (int x = z0 * kRowBytes + 16 * tid; x < kPageBytes; x += 16 * kThreads)
-        *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
-      lds_barrier();
-    }
-    page = cur;
-  }
-
-  if (next_src != nullptr) {
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int k = ln.wave + kWaves * j;
-      if (k < kLoads)
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(next_src + ld_off[j]), LDS_PTR(void, nxt + 1024 * k), 16, 0, 0);
-    }
-  }
-
-  const int kb0 = 16 * ((q4) ^ ln.sw_k), kb1 = 16 * ((4 + q4) ^ ln.sw_k);
-  int vb[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) vb[r] = 16 * ((2 * r + ln.tr_hh) ^ ln.sw_v) + 8 * ln.tr_half;
-
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {             // two halves of 32 tokens: tiles 2u, 2u + 1
-    f32x4 s[2][2];                          // [tile][row block]
-    const uint8_t* krow0 = page + (32 * u + r16) * kRowBytes;
-    auto kload = [&](int c, int tt) -> bf16x8 {
-      return *reinterpret_cast<const bf16x8*>(krow0 + 16 * tt * kRowBytes + 128 * (c >> 1) + ((c & 1) ? kb1 : kb0));
-    };
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        f32x4 grp[2][5];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int g = 0; g < 5; ++g) grp[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int g = 0; g < 5; ++g) {
-            if (g == 4 && j >= 2) continue;
-            const int c = (g < 4) ? 4 * g + j : 16 + j;
-            const bf16x8 a = kload(c, tt);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              grp[rb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rb][c], grp[rb][g], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(scale_tab + 4 * (32 * u + 16 * tt + 4 * q4 + i));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            s[tt][rb][i] = grp[rb][4][i] + sc[0] * grp[rb][0][i] + sc[1] * grp[rb][1][i] + sc[2] * grp[rb][2][i] +
-                           sc[3] * grp[rb][3][i];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int kDepth = 2;
-      bf16x8 kbuf[kDepth][2];
-#pragma unroll
-      for (int c = 0; c < kDepth - 1; ++c)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) kbuf[c][tt] = kload(c, tt);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kDepth - 1), 0);
-#pragma unroll
-      for (int c = 0; c < 18; ++c) {
-        if (c + kDepth - 1 < 18) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) kbuf[(c + kDepth - 1) % kDepth][tt] = kload(c + kDepth - 1, tt);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            s[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c % kDepth][tt], qf[rb][c], s[tt][rb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        if (c + kDepth - 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-
-    // mask + online softmax, per row block
-    const int tok_base = pi * kPage + 32 * u + 4 * q4;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = tok_base + 16 * tt + i;
-          const bool ok = tok < L && tok <= last_ok[rb];
-          const float v = ok ? s[tt][rb][i] * scale_log2 : kNegInf;
-          s[tt][rb][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = max4lanes(mx);
-      if (mx > m_run[rb] + kRescaleSlack) {
-        const float alpha = fast_exp2(m_run[rb] - mx);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < 32; ++d) acc[rb][d] *= alpha;
-        m_run[rb] = mx;
-      }
-      const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-      float psum = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(s[tt][rb][i] - m_use);
-          s[tt][rb][i] = e;
-          psum += e;
-        }
-      }
-      l_run[rb] += psum;
-    }
-
-    // O^T += V^T P^T for both row blocks; one pair of transposed reads feeds two MFMAs
-    const uint8_t* v0 = page + (32 * u + ln.tr_tok) * kRowBytes;
-    auto vload = [&](int d) -> bf16x8 {
-      const uint8_t* a0 = v0 + 128 * (d >> 2) + vb[d & 3];
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    constexpr int NG = kFp8 ? 4 : 1;         // scale groups (8 dim blocks each for fp8)
-    constexpr int DPG = 32 / NG;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      bf16x8 pb[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float x0 = s[0][rb][j], x1 = s[1][rb][j];
-          if constexpr (kFp8) {
-            x0 *= scale_tab[4 * (32 * u + 4 * q4 + j) + g];
-            x1 *= scale_tab[4 * (32 * u + 16 + 4 * q4 + j) + g];
-          }
-          pb[rb][j] = static_cast<__bf16>(x0);
-          pb[rb][4 + j] = static_cast<__bf16>(x1);
-        }
-      }
-      constexpr int kAhead = 2;
-      bf16x8 va[kAhead];
-#pragma unroll
-      for (int k = 0; k < kAhead; ++k) va[k] = vload(g * DPG + k);
-#pragma unroll
-      for (int k = 0; k < DPG; ++k) {
-        const int d = g * DPG + k;
-        const bf16x8 a = va[k % kAhead];
-        if (k + kAhead < DPG) va[k % kAhead] = vload(d + kAhead);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb], acc[rb][d], 0, 0, 0);
-      }
-    }
-  }
-}
-
-template <int FMT>
-__global__ void __launch_bounds__(kThreads) splitkv_wide_kernel(DecodeParams p) {
-  constexpr int M_TILE = 128;
-  constexpr bool kFp8 = (FMT == kFmtFp8);
-  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
-  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
-  constexpr int kSlotBytes = kFp8 ? kRawPageBytes : kPageBytes;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kFp8 ? kLdsFp8 : kLdsBf16];
-  uint8_t* const ring = smem;
-  uint8_t* const conv = smem + 2 * kRawPageBytes;
-
-  Lane ln;
-  ln.tid = threadIdx.x;
-  ln.lane = ln.tid & 63;
-  ln.wave = ln.tid >> 6;
-  ln.tg = 0;
-  ln.r16 = ln.lane & 15;
-  ln.q4 = ln.lane >> 4;
-  ln.sw_k = swz(ln.r16);
-  ln.tr_tok = 4 * ln.q4 + (ln.r16 >> 2);
-  ln.sw_v = swz(ln.tr_tok);
-  ln.tr_half = ln.r16 & 1;
-  ln.tr_hh = (ln.r16 & 3) >> 1;
-  const int lane = ln.lane, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
-
-  const int per_xcd = gridDim.x / 8;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (logical >= p.grid_wgs) return;
-  const int m_tiles = (p.rows + M_TILE - 1) / M_TILE;
-  const int mt = logical % m_tiles;
-  const int kvh = (logical / m_tiles) % p.h_kv;
-  const int part = logical / (m_tiles * p.h_kv);
-
-  Range r;
-  {
-    const int32_t* meta = p.meta + part * kMetaInts;
-    r.begin_b = meta[0];
-    r.begin_page = meta[1];
-    r.end_b = min(meta[2], p.batch - 1);
-    r.end_page = meta[3];
-    r.split0 = meta[4];
-  }
-  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
-
-  int row[2], s_idx[2], head[2];
-  bool row_ok[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    row[rb] = mt * M_TILE + 32 * wave + 16 * rb + r16;
-    row_ok[rb] = row[rb] < p.rows;
-    s_idx[rb] = row_ok[rb] ? row[rb] / p.group : 0;
-    head[rb] = kvh * p.group + (row_ok[rb] ? row[rb] % p.group : 0);
-  }
-
-  const LoadOffsets<FMT> ld_off{wave, lane, static_cast<int>(p.kv_st)};
-  const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
-  auto page_src = [&](int b, int pi) -> const uint8_t* {
-    const int pg = p.block_table[static_cast<int64_t>(b) * p.bt_stride + pi];
-    if (pg < 0 || pg >= p.num_pages) return nullptr;
-    return kv_head + static_cast<int64_t>(pg) * p.kv_sp;
-  };
-
-  int slot = 0;
-  bool load_ok = true;
-  {
-    int nb, npi;
-    next_with_pages(p, r, r.begin_b, nb, npi);
-    if (nb <= r.end_b) {
-      const uint8_t* src = page_src(nb, npi);
-      load_ok = src != nullptr;
-      if (load_ok) {
-#pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j) {
-          const int k = wave + kWaves * j;
-          if (k < kLoads)
-            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src + ld_off[j]), LDS_PTR(void, ring + 1024 * k), 16, 0, 0);
-        }
-      }
-    }
-  }
-
-  for (int b = r.begin_b; b <= r.end_b; ++b) {
-    int L, pg0, pg1;
-    seq_pages(p, r, b, L, pg0, pg1);
-    const int split_idx = (b == r.begin_b) ? r.split0 : 0;
-    const int slot0 = p.num_splits[b];
-    const int nsplit = p.num_splits[b + 1] - slot0;
-    int last_ok[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) last_ok[rb] = p.causal ? (L - p.s_q + s_idx[rb]) : (L - 1);
-
-    bf16x8 qf[2][18];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const uint16_t* qrow = p.q + b * p.q_sb + s_idx[rb] * p.q_ss + head[rb] * p.q_sh;
-#pragma unroll
-      for (int c = 0; c < 18; ++c) {
-        u32x4 v = row_ok[rb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
-        qf[rb][c] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-    wait_vm_all();
-
-    float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-    f32x4 acc[2][32];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int d = 0; d < 32; ++d) acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
-
-    for (int pi = pg0; pi < pg1; ++pi) {
-      const bool this_ok = load_ok;
-      bad |= !this_ok;
-      wait_vm_all();
-      lds_barrier();
-      const uint8_t* next_src = nullptr;
-      {
-        int nb = b, npi = pi + 1;
-        if (npi >= pg1) next_with_pages(p, r, b + 1, nb, npi);
-        if (nb <= r.end_b) {
-          next_src = page_src(nb, npi);
-          load_ok = next_src != nullptr;
-        }
-      }
-      page_step_wide<FMT>(ring + slot * kSlotBytes, ring + (slot ^ 1) * kSlotBytes, conv, next_src, ld_off, ln, L,
-                          last_ok, pi, this_ok, p.scale_log2, qf, acc, m_run, l_run);
-      slot ^= 1;
-    }
-
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float l_row = sum4lanes(l_run[rb]);
-      if (!row_ok[rb]) continue;
-      const bool ok = !bad;
-      const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
-      float lse = (l_row > 0.f) ? (m_run[rb] + __log2f(l_row)) * kLn2 : kNegInf;
-      if (!ok) lse = __builtin_nanf("");
-      const float nan = __builtin_nanf("");
-      if (nsplit == 1) {
-        uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx[rb]) * p.h_q + head[rb]) * kDv + 4 * q4;
-#pragma unroll
-        for (int d = 0; d < 32; ++d) {
-          u32x2 w;
-          const float x0 = ok ? acc[rb][d][0] * inv : nan;
-          const float x1 = ok ? acc[rb][d][1] * inv : nan;
-          const float x2 = ok ? acc[rb][d][2] * inv : nan;
-          const float x3 = ok ? acc[rb][d][3] * inv : nan;
-          w[0] = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
-          w[1] = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
-          *reinterpret_cast<u32x2*>(orow + 16 * d) = w;
-        }
-        if (q4 == 0) p.lse[(static_cast<int64_t>(b) * p.h_q + head[rb]) * p.s_q + s_idx[rb]] = lse;
-      } else {
-        const int pslot = slot0 + split_idx;
-        if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
-          float* prow =
-              p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row[rb]) * kDv + 4 * q4;
-#pragma unroll
-          for (int d = 0; d < 32; ++d) {
-            f32x4 v = acc[rb][d] * inv;
-            if (!ok) v = f32x4{nan, nan, nan, nan};
-            *reinterpret_cast<f32x4*>(prow + 16 * d) = v;
-          }
-          if (q4 == 0) p.part_lse[(static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row[rb]] = lse;
-        }
-      }
-    }
-  }
-  wait_vm_all();
-}
-
 // ----------------------------------------------------------------------------
 // Combine: LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i
 // One workgroup per (sequence, row, KV head, 128-dim quarter). Thread t takes
@@ -1104,8 +564,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(DecodeParams p) {
   const int row = blockIdx.y;
   const int kvh = blockIdx.z / (kDv / kCombDims);
   const int quarter = blockIdx.z % (kDv / kCombDims);
-  const int slot0 = p.num_splits[b];
-  const int n = p.num_splits[b + 1] - slot0;
+  const int slot0 = ld_meta(p.num_splits + b);
+  const int n = ld_meta(p.num_splits + b + 1) - slot0;
   if (n <= 1 || row >= p.rows) return;
   const int s_idx = row / p.group;
   const int head = kvh * p.group + row % p.group;
@@ -1190,8 +650,8 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) 
   const int l16 = tid & 15;
   const int kvh = blockIdx.z / (kDv / kCombDims);
   const int quarter = blockIdx.z % (kDv / kCombDims);
-  const int slot0 = p.num_splits[b];
-  const int n = p.num_splits[b + 1] - slot0;
+  const int slot0 = ld_meta(p.num_splits + b);
+  const int n = ld_meta(p.num_splits + b + 1) - slot0;
   if (n <= 1 || row >= p.rows) return;
   const int s_idx = row / p.group;
   const int head = kvh * p.group + row % p.group;
@@ -1263,11 +723,8 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
     if (err != hipSuccess) return err;
   }
   if (plan.wide) {
-    if (kv_format == kFmtFp8)
-      hipLaunchKernelGGL(splitkv_wide_kernel<kFmtFp8>, dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL(splitkv_wide_kernel<kFmtBf16>, dim3(grid), dim3(kThreads), 0, stream, p);
-    err = hipGetLastError();
+    if (kv_format != kFmtBf16) return hipErrorInvalidValue;   // the 128-row kernel reads bf16 pages only
+    err = launch_split_x(p, grid, stream);
   } else if (plan.rb == 1) {
     err = launch_split<1, 4>(p, kv_format, grid, stream);
   } else if (plan.rb == 2) {

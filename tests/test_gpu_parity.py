@@ -64,6 +64,9 @@ SMALL = [
     ("rows48", 2, 1, 48, 1, [70, 500], False, "bf16"),
     ("rows128", 3, 1, 128, 1, [5, 300, 2000], False, "bf16"),
     ("rows256_causal", 2, 2, 128, 1, [100, 1500], True, "bf16"),
+    ("rows80", 2, 1, 80, 1, [33, 97], False, "bf16"),
+    ("rows192_causal", 2, 3, 64, 1, [31, 161], True, "bf16"),
+    ("hkv2_rows128", 2, 1, 256, 2, [65, 320], False, "bf16"),
     ("hkv2", 2, 1, 32, 2, [90, 400], False, "bf16"),
     ("fp8_rows16", 3, 1, 16, 1, [64, 200, 1025], False, "fp8"),
     ("fp8_rows128", 2, 1, 128, 1, [33, 1100], False, "fp8"),
@@ -149,9 +152,10 @@ def test_page_permutation_and_determinism(fmt):
     assert bitwise
 
 
+@pytest.mark.parametrize("h_q", [16, 128])
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-def test_poisoned_tails_and_unused_pages(fmt):
-    w = make_workload(name="poison", batch=3, s_q=2, h_q=16, seqlens=[100, 37, 640], causal=True, kv_format=fmt,
+def test_poisoned_tails_and_unused_pages(fmt, h_q):
+    w = make_workload(name="poison", batch=3, s_q=2, h_q=h_q, seqlens=[100, 37, 640], causal=True, kv_format=fmt,
                       seed=57, max_blocks=12)
     O1, L1 = run_gpu(w)
     O2, L2 = run_gpu(poison_unused(w))
@@ -170,8 +174,10 @@ def test_single_token_gives_value_row_exactly():
     compare(w, O, LSE, O_ref, LSE_ref, label="L=1")
 
 
-def test_empty_and_fully_masked_rows():
-    w = make_workload(name="empty", batch=4, s_q=2, h_q=16, seqlens=[0, 1, 2, 70], causal=True, seed=59, max_blocks=3)
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_empty_and_fully_masked_rows(h_q):
+    w = make_workload(name="empty", batch=4, s_q=2, h_q=h_q, seqlens=[0, 1, 2, 70], causal=True, seed=59,
+                      max_blocks=3)
     for parts in (0, 1, 9):
         O, LSE = run_gpu(w, num_parts=parts)
         O_ref, LSE_ref = oracle.mla_decode_workload(w)
@@ -180,26 +186,28 @@ def test_empty_and_fully_masked_rows():
         assert np.all(O[1, 0] == 0) and np.all(np.isneginf(LSE[1, :, 0]))
 
 
-def test_invalid_block_table_entry_poisons_only_its_sequence():
-    w = make_workload(name="badpage", batch=3, s_q=1, h_q=16, seqlens=[100, 200, 50], seed=60)
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_invalid_block_table_entry_poisons_only_its_sequence(h_q):
+    w = make_workload(name="badpage", batch=3, s_q=1, h_q=h_q, seqlens=[100, 200, 50], seed=60)
     w.block_table[1, 2] = 10_000
     O, LSE = run_gpu(w)
     assert np.all(np.isnan(O[1])) and np.all(np.isnan(LSE[1]))
-    w_ok = make_workload(name="badpage", batch=3, s_q=1, h_q=16, seqlens=[100, 200, 50], seed=60)
+    w_ok = make_workload(name="badpage", batch=3, s_q=1, h_q=h_q, seqlens=[100, 200, 50], seed=60)
     O_ref, LSE_ref = oracle.mla_decode_workload(w_ok, batches=[0, 2])
     compare(w_ok, O, LSE, O_ref, LSE_ref, batches=[0, 2], label="sequences next to a bad page")
 
 
-def test_noncontiguous_q_and_custom_scale():
-    w = make_workload(name="strided", batch=2, s_q=2, h_q=32, seqlens=[333, 90], causal=True, seed=61,
+@pytest.mark.parametrize("h_q", [32, 128])
+def test_noncontiguous_q_and_custom_scale(h_q):
+    w = make_workload(name="strided", batch=2, s_q=2, h_q=h_q, seqlens=[333, 90], causal=True, seed=61,
                       softmax_scale=0.07)
-    big = torch.zeros(2, 2, 40, 576, dtype=torch.bfloat16)
-    big[:, :, 4:36] = w.q
-    w.q = big[:, :, 4:36]                        # head stride 576, batch stride 2*40*576
+    big = torch.zeros(2, 2, h_q + 8, 576, dtype=torch.bfloat16)
+    big[:, :, 4:4 + h_q] = w.q
+    w.q = big[:, :, 4:4 + h_q]                   # head stride 576, batch stride 2*(h_q+8)*576
     assert not w.q.is_contiguous()
     import paged_mla_decode_amd as mla
     meta, splits = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, 1, device=torch.device(DEV))
-    o, lse = mla.mla_decode_kvcache(big.to(DEV)[:, :, 4:36], w.kvcache.to(DEV), w.block_table.to(DEV),
+    o, lse = mla.mla_decode_kvcache(big.to(DEV)[:, :, 4:4 + h_q], w.kvcache.to(DEV), w.block_table.to(DEV),
                                     w.cache_seqlens.to(DEV), 512, meta, splits, causal=True, softmax_scale=0.07)
     torch.cuda.synchronize()
     O_ref, LSE_ref = oracle.mla_decode_workload(w)
