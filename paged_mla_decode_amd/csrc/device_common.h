@@ -68,14 +68,36 @@ __device__ __forceinline__ uint32_t e4m3fn_to_bf16_bits(uint32_t c) {
 // so the compiler's own wait-count tracking sees it.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__device__ __forceinline__ float max4lanes(float v) {   // over the 4 lanes sharing lane % 16
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// Lane l and lane l ^ 32 (v_permlane32_swap: the pair it returns holds, in
+// every lane, the value of that lane and of its partner across the halves).
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Lane l and lane l ^ 16 (v_permlane16_swap, the same within each 32-lane half).
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Over the 4 lanes sharing lane % 16 (VALU lane swaps, no LDS round trip).
+__device__ __forceinline__ float max4lanes(float v) {
+  float a, b;
+  pair16(v, a, b);
+  v = fmaxf(a, b);
+  pair32(v, a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float sum4lanes(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  float a, b;
+  pair16(v, a, b);
+  v = a + b;
+  pair32(v, a, b);
+  return a + b;
 }
 
 // ----------------------------------------------------------------------------

@@ -102,20 +102,28 @@ __device__ __forceinline__ uint32_t x_load_off(int k, int lane, int st) {
   return static_cast<uint32_t>(t * st + 16 * ((pc - 72 * t) ^ swz(t)));
 }
 
-// Issue the direct loads of one unit (32 tokens starting at `src`) into `dst`.
-__device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, int lane, int st) {
+// Buffer resource word 3 for raw (unformatted, stride 0) buffer access on gfx9-family GPUs.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Issue the direct loads of one unit (32 tokens starting at `src`, token stride
+// `st`) into `dst`: MUBUF loads to LDS (buffer_load_dwordx4 ... lds), 16 bytes
+// per lane, with the unit as the buffer (offsets past its 32 rows read zeros).
+// The buffer form keeps the LDS read waits of the compute phases partial
+// (the FLAT form makes every LDS wait a full drain while a load is in flight).
+__device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, const uint32_t (&off)[9], int st) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, kXHalf * st, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < XLayout::kLoadsPerWave; ++j) {
     const int k = wave + kWaves * j;
-    __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src + x_load_off(k, lane, st)), LDS_PTR(void, dst + 1024 * k), 16, 0,
-                                     0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
   }
 }
 
 // s_waitcnt vmcnt(9): one unit's direct loads may stay in flight.
 // (vmcnt: bits 3:0 and 15:14; expcnt 6:4 = 7 and lgkmcnt 11:8 = 15 mean no wait.)
 __device__ __forceinline__ void wait_vm_one_unit() { __builtin_amdgcn_s_waitcnt(0x0F70 | XLayout::kLoadsPerWave); }
-static_assert(XLayout::kLoadsPerWave < 16, "vmcnt low field");
+static_assert(XLayout::kLoadsPerWave < 16 && XLayout::kLoadsPerWave == 9, "vmcnt low field; load offsets per lane");
 
 // Lane-constant indices. MFMA 16x16x32: lane l supplies A[i = l % 16][k-slots
 // 8 (l / 16) .. + 7] and B[the same k-slots][j = l % 16]; D register i of lane
@@ -125,6 +133,7 @@ struct XLane {
   int r16, q4;          // lane % 16, lane / 16
   int k_off[2];         // S phase: K row r16, logical chunks q4 and 4 + q4 (swizzled), bytes
   int v_off[4];         // PV phase: transposed V read offsets, by 16-dim block d & 3
+  uint32_t ld_off[9];   // direct loads: source offset of this lane's 16 bytes in load wave + 4 j
 };
 
 // One unit of the pipeline. `cur` holds the unit (32 bf16 rows), `nxt`
@@ -150,7 +159,7 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   }
 
   // ---- the unit two ahead -> nxt ----------------------------------------------------
-  if (next_src != nullptr) x_issue(next_src, nxt, wave, ln.lane, st);
+  if (next_src != nullptr) x_issue(next_src, nxt, wave, ln.ld_off, st);
 
   // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 32 w + 16 rb + r16] -------------------
   const uint8_t* qlds = lds + X::kQ;
@@ -292,7 +301,10 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) ln.v_off[e] = tok * kRowBytes + 16 * ((2 * e + hh) ^ sw_v) + 8 * half8;
   }
-  const int tid = ln.tid, lane = ln.lane, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+  const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+  const int st = static_cast<int>(p.kv_st);
+#pragma unroll
+  for (int j = 0; j < X::kLoadsPerWave; ++j) ln.ld_off[j] = x_load_off(wave + kWaves * j, ln.lane, st);
 
   // XCD-aware order: consecutive logical workgroups share an XCD (and its L2)
   const int per_xcd = gridDim.x / 8;
@@ -327,7 +339,6 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     shead[rb] = kvh * p.group + (srow_ok[rb] ? srow[rb] % p.group : 0);
   }
 
-  const int st = static_cast<int>(p.kv_st);
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
   // global address of a unit (nullptr: block-table entry outside the pool)
   auto unit_src = [&](XUnit u) -> const uint8_t* {
@@ -349,7 +360,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   if (u1.b <= r.end_b) {
     const uint8_t* src = unit_src(u1);
     ok1 = src != nullptr;
-    if (ok1) x_issue(src, lds + X::kRing, wave, lane, st);
+    if (ok1) x_issue(src, lds + X::kRing, wave, ln.ld_off, st);
     u2 = x_next(p, r, u1);
   } else {
     u2 = u1;
@@ -357,7 +368,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   if (u2.b <= r.end_b) {
     const uint8_t* src = unit_src(u2);
     ok2 = src != nullptr;
-    if (ok2) x_issue(src, lds + X::kRing + X::kSlot, wave, lane, st);
+    if (ok2) x_issue(src, lds + X::kRing + X::kSlot, wave, ln.ld_off, st);
   }
   int slot = 0;
   int unit_id = 0;
