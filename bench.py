@@ -143,8 +143,8 @@ def main():
     kvs = [w.kvcache.to(dev) for _ in range(copies)]
     M = w.heads_per_kv
     parts = mla.mla_num_parts(w.batch, M, w.h_kv, w.kv_format)
-    meta_dev = torch.empty((parts, 8), dtype=torch.int32, device=dev)
-    splits_dev = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    flat_dev = torch.empty((parts * 8 + w.batch + 1,), dtype=torch.int32, device=dev)
+    meta_dev, splits_dev = mla.split_metadata(flat_dev, w.batch)
     out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.h_q, w.s_q), dtype=torch.float32, device=dev)
     ws = torch.empty((mla.mla_workspace_bytes(w.batch, parts, M, w.h_kv),), dtype=torch.uint8, device=dev)
@@ -157,9 +157,9 @@ def main():
 
     def step(i, ev=None):
         # a1: host tile scheduler for this step's lengths, uploaded on the decode stream
-        m_h, s_h = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts, pin=True)
-        meta_dev.copy_(m_h, non_blocking=True)
-        splits_dev.copy_(s_h, non_blocking=True)
+        # (metadata rows and num_splits share one pinned buffer: one copy)
+        m_h, _ = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts, pin=True)
+        flat_dev.copy_(mla.packed_metadata(m_h), non_blocking=True)
         d = decoders[i % copies]
         d.set_events(ev if ev is not None else (None, None, None))
         d.run(stream)

@@ -86,12 +86,29 @@ def mla_get_metadata_host(cache_seqlens_host: torch.Tensor, heads_per_kv: int, h
         parts = lib.mla_num_parts(B, int(heads_per_kv), int(h_kv), fmt, int(num_cus))
         if parts < 0:
             raise ValueError(_lib.last_error())
-    meta = torch.empty((parts, META_INTS), dtype=torch.int32, pin_memory=pin)
-    splits = torch.empty((B + 1,), dtype=torch.int32, pin_memory=pin)
+    # one buffer [tile_metadata (parts x 8) | num_splits (B + 1)]: a single upload
+    flat = torch.empty((parts * META_INTS + B + 1,), dtype=torch.int32, pin_memory=pin)
+    meta = flat[:parts * META_INTS].view(parts, META_INTS)
+    splits = flat[parts * META_INTS:]
     got = ctypes.c_int(0)
     _lib.check(lib.mla_get_metadata(_i32p(L), B, int(heads_per_kv), int(h_kv), fmt, int(num_cus), parts,
                                     _i32p(meta), _i32p(splits), ctypes.byref(got)))
     return meta, splits
+
+
+def split_metadata(flat: torch.Tensor, batch: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Views (tile_metadata [P, 8], num_splits [batch + 1]) of one packed int32 buffer
+    laid out as mla_get_metadata_host leaves it (metadata rows, then num_splits)."""
+    n = int(flat.shape[0]) - (batch + 1)
+    if n <= 0 or n % META_INTS:
+        raise ValueError("packed metadata buffer has the wrong length for this batch")
+    return flat[:n].view(n // META_INTS, META_INTS), flat[n:]
+
+
+def packed_metadata(meta: torch.Tensor) -> torch.Tensor:
+    """The packed buffer behind a (tile_metadata, num_splits) pair from mla_get_metadata_host."""
+    base = meta._base if meta._base is not None else meta
+    return base
 
 
 def mla_get_metadata(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *, kv_format="bf16",
@@ -105,7 +122,8 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int =
     pin = torch.device(device).type == "cuda"
     meta, splits = mla_get_metadata_host(cache_seqlens, heads_per_kv, h_kv, kv_format=kv_format,
                                          num_parts=num_parts, num_cus=num_cus, pin=pin)
-    meta_d, splits_d = meta.to(device, non_blocking=True), splits.to(device, non_blocking=True)
+    flat_d = packed_metadata(meta).to(device, non_blocking=True)
+    meta_d, splits_d = split_metadata(flat_d, int(splits.shape[0]) - 1)
     # host-side fact carried along for the decode call's combine-shape hint
     splits_d._mla_max_splits = max_splits_of(splits)
     return meta_d, splits_d

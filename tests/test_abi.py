@@ -145,3 +145,17 @@ def test_python_binding_refuses_cpu_tensors():
     meta, splits = mla.mla_get_metadata_host(L, 16, 1, num_cus=256)
     with pytest.raises(ValueError):
         mla.mla_decode_kvcache(q, kv, bt, L, 512, meta, splits)
+
+
+def test_packed_metadata_round_trip():
+    import torch
+    import paged_mla_decode_amd as mla
+    L = torch.tensor([0, 5, 700, 64, 3000], dtype=torch.int32)
+    meta, splits = mla.mla_get_metadata_host(L, 128, 1, num_cus=256, num_parts=9)
+    flat = mla.packed_metadata(meta)
+    assert flat.shape == (9 * 8 + 6,)
+    m2, s2 = mla.split_metadata(flat, 5)
+    assert torch.equal(m2, meta) and torch.equal(s2, splits)
+    assert m2.data_ptr() == meta.data_ptr() and s2.data_ptr() == splits.data_ptr()
+    with pytest.raises(ValueError):
+        mla.split_metadata(flat, 6)
