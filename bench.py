@@ -108,6 +108,107 @@ def cpu_baseline(w, target_s: float = 15.0):
                       f"({sum(L)} cached tokens), {t_total:.2f} s, numpy float64"}
 
 
+def source_sha256() -> str:
+    """Hash of the library sources: a stored counter summary is only used for the same kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_mla_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when there is
+    none or it was taken on other kernel sources."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha256():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _pmc_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter: str, match) -> list:
+    """Counter value per dispatch (summed over the instances rocprofv3 reports) for kernels matching."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+            acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def pmc_summary(args) -> str:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel by what the same
+    counters read for the calibration copy of known size."""
+    from workloads import named_workload
+    w = named_workload(args.workload)
+    split_name = "splitkv_x_kernel" if (w.kv_format == "bf16" and w.heads_per_kv > 64) else "splitkv_kernel"
+    is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
+    is_copy = lambda n: "elementwise" in n and "Mul" in n
+    fr, wr = _pmc_rows(args.pmc_summary[0]), _pmc_rows(args.pmc_summary[1])
+    f_split, w_split = _per_dispatch(fr, "FETCH_SIZE", is_split), _per_dispatch(wr, "WRITE_SIZE", is_split)
+    f_copy, w_copy = _per_dispatch(fr, "FETCH_SIZE", is_copy), _per_dispatch(wr, "WRITE_SIZE", is_copy)
+    if not (f_split and w_split and f_copy and w_copy):
+        raise SystemExit("missing split-kernel or calibration-copy dispatches in the counter files")
+    copy_bytes = args.calibrate_copy_mb * (1 << 20)
+    if copy_bytes <= 0:
+        raise SystemExit("--calibrate-copy-mb must give the calibration copy size")
+    fetch_scale = copy_bytes / (sum(f_copy) / len(f_copy) * 1024.0)
+    write_scale = copy_bytes / (sum(w_copy) / len(w_copy) * 1024.0)
+    fetch = sum(f_split) / len(f_split) * 1024.0 * fetch_scale
+    write = sum(w_split) / len(w_split) * 1024.0 * write_scale
+    byts, _, _ = algorithmic_work(w)
+    lines = [
+        f"# HBM traffic of {split_name} on workload {w.name} (rocprofv3 --pmc, scaled by a plain copy)",
+        f"kernel: {split_name}",
+        f"workload: {w.name}",
+        f"source_sha256: {source_sha256()}",
+        f"split_dispatches: {len(f_split)} (FETCH_SIZE run), {len(w_split)} (WRITE_SIZE run)",
+        f"split_fetch_kib_per_dispatch: {sum(f_split) / len(f_split):.1f}",
+        f"split_write_kib_per_dispatch: {sum(w_split) / len(w_split):.1f}",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_fetch_kib: {sum(f_copy) / len(f_copy):.1f}",
+        f"copy_write_kib: {sum(w_copy) / len(w_copy):.1f}",
+        f"fetch_scale: {fetch_scale:.4f}",
+        f"write_scale: {write_scale:.4f}",
+        f"hbm_fetch_bytes_per_launch: {int(fetch)}",
+        f"hbm_write_bytes_per_launch: {int(write)}",
+        f"hbm_bytes_per_launch: {int(fetch + write)}",
+        f"algorithmic_bytes_per_step: {byts}",
+        f"traffic_over_algorithmic: {(fetch + write) / byts:.3f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,7 +218,16 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="KV pool replicas to rotate through (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="run one plain fp32 copy kernel (out = in * 1) of this size before timing, as the "
+                         "reference for scaling HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "bench made with --calibrate-copy-mb, and print the traffic summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(args), end="")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode path shards by sequence with no communication; see the design notes)", file=sys.stderr)
@@ -164,6 +274,15 @@ def main():
         d.set_events(ev if ev is not None else (None, None, None))
         d.run(stream)
 
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)            # reads and writes calibrate_copy_mb MiB once
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -196,6 +315,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(split_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(split_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    split_name = "splitkv_x_kernel" if (w.kv_format == "bf16" and w.heads_per_kv > 64) else "splitkv_kernel"
+    roof["traffic"] = stored_traffic(split_name, w.name)
 
     result = {
         "metric": "paged MLA decode achieved HBM GB/s and TFLOPS (+% of roofline), 1 MI355X",

@@ -167,8 +167,9 @@ typedef struct mla_decode_args {
      shape of the combine kernel (results do not depend on it). */
   int max_splits;
 
-  /* Optional timing hooks (hipEvent_t or NULL): recorded on the stream before
-     the split-KV kernel, after it, and after the combine kernel. */
+  /* Optional timing hooks (hipEvent_t or NULL): events[0] and events[1] take
+     the split-KV kernel's own start and end timestamps (the kernel is launched
+     with hipExtLaunchKernel), events[2] is recorded after the combine kernel. */
   void* events[3];
 } mla_decode_args;
 

@@ -28,6 +28,7 @@
 //   * Waves that split a page's tokens merge (m, l, O) through LDS at the end of
 //     a sequence piece. A piece that is the whole sequence writes bf16 O and LSE;
 //     otherwise fp32 O / l and its LSE go to the piece's partial slot.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -704,11 +705,14 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) 
 constexpr int kNarrowCombineMax = 8;
 
 template <int RB, int TG>
-hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStream_t stream) {
+hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
+                        hipEvent_t ev_stop) {
   if (kv_format == kFmtFp8)
-    hipLaunchKernelGGL((splitkv_kernel<RB, TG, kFmtFp8>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((splitkv_kernel<RB, TG, kFmtFp8>), dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop,
+                          0, p);
   else
-    hipLaunchKernelGGL((splitkv_kernel<RB, TG, kFmtBf16>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((splitkv_kernel<RB, TG, kFmtBf16>), dim3(grid), dim3(kThreads), 0, stream, ev_start,
+                          ev_stop, 0, p);
   return hipGetLastError();
 }
 
@@ -717,26 +721,23 @@ hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStrea
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]) {
   const int grid = (p.grid_wgs + 7) / 8 * 8;
+  // events[0] / events[1] take the split kernel's own start / end timestamps
+  // (hipExtLaunchKernelGGL), events[2] is recorded after the combine kernel.
+  hipEvent_t ev0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
+  hipEvent_t ev1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+  hipEvent_t ev2 = events ? static_cast<hipEvent_t>(events[2]) : nullptr;
   hipError_t err;
-  if (events && events[0]) {
-    err = hipEventRecord(static_cast<hipEvent_t>(events[0]), stream);
-    if (err != hipSuccess) return err;
-  }
   if (plan.wide) {
     if (kv_format != kFmtBf16) return hipErrorInvalidValue;   // the 128-row kernel reads bf16 pages only
-    err = launch_split_x(p, grid, stream);
+    err = launch_split_x(p, grid, stream, ev0, ev1);
   } else if (plan.rb == 1) {
-    err = launch_split<1, 4>(p, kv_format, grid, stream);
+    err = launch_split<1, 4>(p, kv_format, grid, stream, ev0, ev1);
   } else if (plan.rb == 2) {
-    err = launch_split<2, 2>(p, kv_format, grid, stream);
+    err = launch_split<2, 2>(p, kv_format, grid, stream, ev0, ev1);
   } else {
-    err = launch_split<4, 1>(p, kv_format, grid, stream);
+    err = launch_split<4, 1>(p, kv_format, grid, stream, ev0, ev1);
   }
   if (err != hipSuccess) return err;
-  if (events && events[1]) {
-    err = hipEventRecord(static_cast<hipEvent_t>(events[1]), stream);
-    if (err != hipSuccess) return err;
-  }
   if (p.max_splits > 0 && p.max_splits <= kNarrowCombineMax) {
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
     hipLaunchKernelGGL(combine_rows_kernel, cgrid, dim3(kThreads), 0, stream, p);
@@ -746,8 +747,8 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (events && events[2]) {
-    err = hipEventRecord(static_cast<hipEvent_t>(events[2]), stream);
+  if (ev2) {
+    err = hipEventRecord(ev2, stream);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -6,6 +6,7 @@
 // dims; pieces of a sequence leave partial O / LSE for the combine kernel:
 // wmrh.cn FlashMLA深度解析, "计算流水线设计"), organised so that V is read from
 // LDS once per workgroup instead of once per wave.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -505,8 +506,9 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_split_x(const DecodeParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(splitkv_x_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+hipError_t launch_split_x(const DecodeParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop) {
+  hipExtLaunchKernelGGL(splitkv_x_kernel, dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 
