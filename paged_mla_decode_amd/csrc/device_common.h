@@ -44,10 +44,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Swizzle of the 16-byte chunk index inside a token row (stays inside its
-// aligned group of 8 chunks): K reads (8 consecutive tokens, one chunk) and
-// transposed V reads (4 consecutive tokens, 2 chunks) both spread over 8 groups.
-__device__ __forceinline__ int swz(int token) { return ((token & 3) << 1) | ((token >> 2) & 1); }
+// Swizzle of the 16-byte chunk index inside a token row: chunk j of token t is
+// stored at j ^ (t & 7), inside its aligned group of 8 chunks. Chosen by
+// measurement on gfx950 (a 1152-byte row puts consecutive tokens half a bank
+// window apart): with it both the K reads (ds_read_b128, 16 consecutive
+// tokens x one chunk) and the transposed V reads (ds_read_b64_tr_b16, 4
+// tokens x 2 chunks per 16 lanes) run at the full LDS rate (~286 and ~266
+// B/clk/CU with 16 waves); the XOR patterns tried before reached 157-163.
+__device__ __forceinline__ int swz(int token) { return token & 7; }
 
 __device__ __forceinline__ int chunk_off(int token, int chunk) { return token * kRowBytes + 16 * (chunk ^ swz(token)); }
 

@@ -79,20 +79,28 @@ static_assert(XLayout::kLoads % kWaves == 0, "equal direct-load counts per wave"
 //   P^T slot s: tokens 4 s + 0..3, then 16 + 4 s + 0..3.
 __device__ __forceinline__ int xrow_off(int row, int slot16) { return row * 64 + 16 * (slot16 ^ ((row >> 1) & 3)); }
 
-// One unit of work: half `hf` of page `pi` of sequence `b`.
+// One unit of work: half `hf` of page `pi` of sequence `b`, with that
+// sequence's length L and end page pg1 inside the range (so stepping through a
+// sequence reads no metadata).
 struct XUnit {
-  int b, pi, hf;
+  int b, pi, hf, L, pg1;
 };
 
-// Next unit after u inside range r (b > r.end_b when there is none).
-__device__ __forceinline__ XUnit x_next(const DecodeParams& p, const Range& r, XUnit u) {
-  int L, pg0, pg1;
-  seq_pages(p, r, u.b, L, pg0, pg1);
-  if (u.hf == 0 && L - u.pi * kPage > kXHalf) return XUnit{u.b, u.pi, 1};
-  if (u.pi + 1 < pg1) return XUnit{u.b, u.pi + 1, 0};
-  int nb, npg;
-  next_with_pages(p, r, u.b + 1, nb, npg);
-  return XUnit{nb, npg, 0};
+// First unit at or after sequence b inside range r (b > r.end_b when there is none).
+__device__ __forceinline__ XUnit x_seek(const DecodeParams& p, const Range& r, int b) {
+  for (; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    seq_pages(p, r, b, L, pg0, pg1);
+    if (pg0 < pg1) return XUnit{b, pg0, 0, L, pg1};
+  }
+  return XUnit{r.end_b + 1, 0, 0, 0, 0};
+}
+
+// Next unit after u inside range r.
+__device__ __forceinline__ XUnit x_next(const DecodeParams& p, const Range& r, const XUnit& u) {
+  if (u.hf == 0 && u.L - u.pi * kPage > kXHalf) return XUnit{u.b, u.pi, 1, u.L, u.pg1};
+  if (u.pi + 1 < u.pg1) return XUnit{u.b, u.pi + 1, 0, u.L, u.pg1};
+  return x_seek(p, r, u.b + 1);
 }
 
 // Source offset of the 16 bytes that lane `lane` of direct load k brings into
@@ -200,49 +208,58 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   uint8_t* pbuf = lds + X::kP;
   float* alpha_buf = reinterpret_cast<float*>(lds + X::kAlpha);
   int* flags = reinterpret_cast<int*>(lds + X::kFlag);
-  bool rescaled = false;
+  // Both 16-row blocks are handled side by side without branches, so their
+  // dependent VALU chains interleave.
+  float mx[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     // token tok0 + 16 tt + 4 q4 + i is allowed iff 16 tt + i <= lim
     const int lim = min(L - 1, last_ok[rb]) - tok0 - 4 * q4;
-    float mx = kNegInf;
+    mx[rb] = kNegInf;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = 16 * tt + i <= lim;
-        const float v = ok ? s[tt][rb][i] * scale_log2 : kNegInf;
+        const float v = (16 * tt + i <= lim) ? s[tt][rb][i] * scale_log2 : kNegInf;
         s[tt][rb][i] = v;
-        mx = fmaxf(mx, v);
+        mx[rb] = fmaxf(mx[rb], v);
       }
-    }
-    mx = max4lanes(mx);
-    float alpha = 1.f;
-    if (mx > m_run[rb] + kRescaleSlack) {
-      // a row's first allowed tokens need no rescale: its O and l are still 0
-      if (m_run[rb] != kNegInf) {
-        alpha = fast_exp2(m_run[rb] - mx);
-        rescaled = true;
-        l_run[rb] *= alpha;
-      }
-      m_run[rb] = mx;
-    }
-    const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-    float psum = 0.f;
-    bf16x8 pv;
+  }
+  mx[0] = max4lanes(mx[0]);
+  mx[1] = max4lanes(mx[1]);
+  bool rescaled = false;
+  float alpha[2], m_use[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+  for (int rb = 0; rb < 2; ++rb) {
+    // the running max moves only when it grows by more than the slack; a row's
+    // first allowed tokens need no rescale (its O and l are still 0)
+    const bool grow = mx[rb] > m_run[rb] + kRescaleSlack;
+    const bool had = m_run[rb] != kNegInf;
+    alpha[rb] = (grow && had) ? fast_exp2(m_run[rb] - mx[rb]) : 1.f;
+    rescaled |= grow && had;
+    l_run[rb] *= alpha[rb];
+    m_run[rb] = grow ? mx[rb] : m_run[rb];
+    m_use[rb] = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
+  }
+  bf16x8 pv[2];
+  float psum[2] = {0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = fast_exp2(s[tt][rb][i] - m_use);
-        psum += e;
-        pv[4 * tt + i] = static_cast<__bf16>(e);
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float e = fast_exp2(s[tt][rb][i] - m_use[rb]);
+        psum[rb] += e;
+        pv[rb][4 * tt + i] = static_cast<__bf16>(e);
       }
-    }
-    l_run[rb] += psum;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    l_run[rb] += psum[rb];
     const int row = 32 * wave + 16 * rb + r16;
-    *reinterpret_cast<bf16x8*>(pbuf + xrow_off(row, q4)) = pv;
-    if (q4 == 0) alpha_buf[row] = alpha;
+    // slot q4 of the row holds tokens 4 q4 .. 4 q4 + 3 and 16 + 4 q4 .. 16 + 4 q4 + 3
+    *reinterpret_cast<bf16x8*>(pbuf + xrow_off(row, q4)) = pv[rb];
+    if (q4 == 0) alpha_buf[row] = alpha[rb];
   }
   if (ln.lane == 0 && __builtin_amdgcn_ballot_w64(rescaled) != 0) flags[wave] = unit_id;
   lds_barrier_keep_loads();
@@ -341,9 +358,20 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   }
 
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
+  // Block-table window: lane i holds entry win_pi + i of sequence win_b's row
+  // (-1 past the row). Refilled with one vector load when a unit falls outside
+  // it (a new sequence, or every 64 pages), so units need no scalar load each.
+  int bt_win = -1, win_b = -1, win_pi = 0;
   // global address of a unit (nullptr: block-table entry outside the pool)
-  auto unit_src = [&](XUnit u) -> const uint8_t* {
-    const int pg = ld_meta(p.block_table + static_cast<int64_t>(u.b) * p.bt_stride + u.pi);
+  auto unit_src = [&](const XUnit& u) -> const uint8_t* {
+    if (u.b != win_b || u.pi < win_pi || u.pi >= win_pi + 64) {
+      win_b = u.b;
+      win_pi = u.pi;
+      const int e = u.pi + ln.lane;
+      bt_win = e < p.max_blocks ? p.block_table[static_cast<int64_t>(u.b) * p.bt_stride + e] : -1;
+      wait_vm_all();
+    }
+    const int pg = __builtin_amdgcn_readlane(bt_win, u.pi - win_pi);
     if (pg < 0 || pg >= p.num_pages) return nullptr;
     return kv_head + static_cast<int64_t>(pg) * p.kv_sp + static_cast<int64_t>(u.hf) * kXHalf * st;
   };
@@ -351,12 +379,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   // ---- prime the ring: the first two units ----------------------------------------------
   // u1 is in flight into `slot`, u2 into the next slot; ok = its page is valid
   // (a unit is issued iff it is inside the range and ok).
-  XUnit u1, u2;
-  {
-    int nb, npg;
-    next_with_pages(p, r, r.begin_b, nb, npg);
-    u1 = XUnit{nb, npg, 0};
-  }
+  XUnit u1 = x_seek(p, r, r.begin_b), u2;
   bool ok1 = true, ok2 = true;
   if (u1.b <= r.end_b) {
     const uint8_t* src = unit_src(u1);
