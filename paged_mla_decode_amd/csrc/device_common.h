@@ -55,17 +55,14 @@ __device__ __forceinline__ int swz(int token) { return token & 7; }
 
 __device__ __forceinline__ int chunk_off(int token, int chunk) { return token * kRowBytes + 16 * (chunk ^ swz(token)); }
 
-// OCP E4M3FN code (low 8 bits of c) -> bf16 bits, exactly. Codes 0x7F/0xFF -> NaN.
-__device__ __forceinline__ uint32_t e4m3fn_to_bf16_bits(uint32_t c) {
-  const uint32_t mag = c & 0x7Fu;
-  uint32_t v;
-  if (mag >= 8u) {
-    v = (mag << 4) + 0x3C00u;                      // exponent e - 7 + 127, mantissa m << 4
-  } else {
-    v = __float_as_uint(static_cast<float>(mag) * 0.001953125f) >> 16;   // m * 2^-9, exact in bf16
-  }
-  v = (mag == 0x7Fu) ? 0x7FC0u : v;
-  return v | ((c & 0x80u) << 8);
+// Four OCP E4M3FN codes (the bytes of w, lowest first) -> four bf16 values
+// (two per 32-bit word, lowest first), exactly: an e4m3 value has at most 4
+// significant bits, so bf16 holds it without rounding. v_cvt_scalef32_pk_bf16_fp8
+// with scale 1.0 converts two codes per instruction; checked against the OCP
+// definition for all 256 codes (subnormals m * 2^-9, 0x7F / 0xFF -> NaN).
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, true));
 }
 
 // s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt fields left at "no wait"),

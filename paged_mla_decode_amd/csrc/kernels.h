@@ -34,9 +34,9 @@ struct DecodeParams {
   int grid_wgs;               // real workgroups of the split kernel (the grid is padded to a multiple of 8)
 };
 
-// The 128-row split kernel (mla_kernels_x.hip; bf16 pages, grid padded to a multiple of 8).
+// The 128-row split kernel (mla_kernels_x.hip; grid padded to a multiple of 8).
 // ev_start / ev_stop (may be null) take the kernel's start and end timestamps.
-hipError_t launch_split_x(const DecodeParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+hipError_t launch_split_x(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop);
 
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,

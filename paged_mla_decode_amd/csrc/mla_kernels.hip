@@ -79,10 +79,13 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint32_t a = w[i], c = w[i + 2];
-        lo[2 * i] = e4m3fn_to_bf16_bits(a) | (e4m3fn_to_bf16_bits(a >> 8) << 16);
-        lo[2 * i + 1] = e4m3fn_to_bf16_bits(a >> 16) | (e4m3fn_to_bf16_bits(a >> 24) << 16);
-        hi[2 * i] = e4m3fn_to_bf16_bits(c) | (e4m3fn_to_bf16_bits(c >> 8) << 16);
-        hi[2 * i + 1] = e4m3fn_to_bf16_bits(c >> 16) | (e4m3fn_to_bf16_bits(c >> 24) << 16);
+        uint32_t x0, x1, y0, y1;
+        e4m3x4_to_bf16(a, x0, x1);
+        e4m3x4_to_bf16(c, y0, y1);
+        lo[2 * i] = x0;
+        lo[2 * i + 1] = x1;
+        hi[2 * i] = y0;
+        hi[2 * i + 1] = y1;
       }
       if (!keep) {
         lo = u32x4{0u, 0u, 0u, 0u};
@@ -728,8 +731,7 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   hipEvent_t ev2 = events ? static_cast<hipEvent_t>(events[2]) : nullptr;
   hipError_t err;
   if (plan.wide) {
-    if (kv_format != kFmtBf16) return hipErrorInvalidValue;   // the 128-row kernel reads bf16 pages only
-    err = launch_split_x(p, grid, stream, ev0, ev1);
+    err = launch_split_x(p, kv_format, grid, stream, ev0, ev1);
   } else if (plan.rb == 1) {
     err = launch_split<1, 4>(p, kv_format, grid, stream, ev0, ev1);
   } else if (plan.rb == 2) {

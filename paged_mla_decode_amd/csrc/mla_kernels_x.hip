@@ -38,39 +38,54 @@ using namespace dev;
 //               every wave's P^T.
 // Per page this reads K four times (288 KB) but V once (64 KB), against four
 // times each when every wave owns whole rows.
-// Built for bf16 pages; FP8 pages use the 64-row kernel.
+// FP8 pages (656-byte records) stream raw into the ring; one LDS pass per
+// unit turns the e4m3 codes into bf16 exactly (4 significant bits fit in 8)
+// and copies RoPE and the 4 per-128-dim scales. The S phase applies the fp32
+// scales to the per-group partial logits; in the PV phase wave w's dims are
+// exactly scale group w, so it multiplies its P^T operand by that group's
+// per-token scales and V enters the MFMA as the exact codes.
 // ----------------------------------------------------------------------------
 
 constexpr int kXHalf = 32;                                  // tokens per unit
-constexpr int kXHalfBytes = kXHalf * kRowBytes;             // 36864 = 36 x 1 KB
-constexpr int kXHalfLoads = kXHalfBytes / 1024;             // 36
-constexpr int kXSlots = 3;
+constexpr int kXHalfBytes = kXHalf * kRowBytes;             // 36864 = 36 x 1 KB: bf16 rows
+constexpr int kXRawBytes = kXHalf * kFp8Record;             // 20992: FP8 records
 constexpr int kXPBytes = 128 * kXHalf * 2;                  // 8192: P^T [128 rows][32 tokens] bf16
 constexpr int kXQChunkBytes = 128 * 64;                     // one 32-dim Q^T chunk of 128 rows
-// LDS layout (bytes): the ring, P^T, rescale factors, flags, and the Q^T
-// chunks {0, 1, 2, 16, 17} of the 128 rows; the other 13 chunks of each row
-// stay in VGPRs.
+
+// LDS layout (bytes): the ring (bf16: 3 slots, two units ahead; FP8: 2 slots of
+// raw records, one unit ahead); FP8 only: the converted unit (bf16 rows, the
+// bf16 ring layout) and the scales [4 groups][32 tokens]; then P^T, rescale
+// factors, flags, and the Q^T chunks kept in LDS for all 128 rows (the other
+// chunks of each row stay in VGPRs): bf16 {0, 1, 2, 16, 17}, FP8 {0 .. 6, 16, 17}.
+template <int FMT>
 struct XLayout {
-  static constexpr int kSlot = kXHalfBytes;
+  static constexpr bool kFp8 = (FMT == kFmtFp8);
+  static constexpr int kSlot = kFp8 ? 21 * 1024 : kXHalfBytes;
+  static constexpr int kSlots = kFp8 ? 2 : 3;
+  static constexpr int kAhead = kSlots - 1;                 // units in flight beyond the current one
   static constexpr int kRing = 0;
-  static constexpr int kP = kRing + kXSlots * kSlot;        // 110592
+  static constexpr int kConv = kRing + kSlots * kSlot;
+  static constexpr int kScale = kConv + (kFp8 ? kXHalfBytes : 0);
+  static constexpr int kP = kScale + (kFp8 ? 4 * kXHalf * 4 : 0);
   static constexpr int kAlpha = kP + kXPBytes;              // [128] fp32
   static constexpr int kFlag = kAlpha + 128 * 4;            // [4] int32 (64 B)
   static constexpr int kQ = kFlag + 64;
-  static constexpr int kQChunks = 5;
-  static constexpr int kTotal = kQ + kQChunks * kXQChunkBytes;   // 160320
-  static constexpr int kLoads = kXHalfLoads;
-  static constexpr int kLoadsPerWave = kLoads / kWaves;          // 9
+  static constexpr int kQChunks = kFp8 ? 9 : 5;
+  static constexpr int kTotal = kQ + kQChunks * kXQChunkBytes;   // bf16 160320, FP8 162880
+  static constexpr int kLoads = kFp8 ? 21 : kXHalfBytes / 1024;   // 1 KB direct loads per unit (36 / 21)
+  static constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;   // 9 / 6
+  static constexpr int kLow = kFp8 ? 7 : 3;                      // chunks 0 .. kLow-1 in LDS
   // LDS slot of Q^T chunk c, or -1 when it lives in VGPRs
-  static constexpr int qslot(int c) { return c < 3 ? c : (c == 16 ? 3 : (c == 17 ? 4 : -1)); }
+  static constexpr int qslot(int c) { return c < kLow ? c : (c == 16 ? kLow : (c == 17 ? kLow + 1 : -1)); }
   static constexpr int kRegChunks = 18 - kQChunks;
-  // register index of chunk c (chunks 3 .. 15)
-  static constexpr int qreg(int c) { return c - 3; }
+  // register index of chunk c (chunks kLow .. 15)
+  static constexpr int qreg(int c) { return c - kLow; }
   // LDS chunk index qs -> Q chunk
-  static constexpr int qchunk(int qs) { return qs < 3 ? qs : 13 + qs; }
+  static constexpr int qchunk(int qs) { return qs < kLow ? qs : 16 - kLow + qs; }
 };
-static_assert(XLayout::kTotal <= 163840, "LDS budget");
-static_assert(XLayout::kLoads % kWaves == 0, "equal direct-load counts per wave");
+static_assert(XLayout<kFmtBf16>::kTotal <= 163840 && XLayout<kFmtFp8>::kTotal <= 163840, "LDS budget");
+static_assert(XLayout<kFmtBf16>::kLoads % kWaves == 0, "equal direct-load counts per wave (bf16)");
+static_assert(XLayout<kFmtFp8>::kSlot >= kXRawBytes, "FP8 slot holds a unit");
 
 // Q^T chunks and P^T rows in LDS: 64 bytes per row (4 x 16 B); the 16-byte
 // slot is XOR-swizzled with (row >> 1) & 3 so 8 consecutive rows hit 8
@@ -104,11 +119,20 @@ __device__ __forceinline__ XUnit x_next(const DecodeParams& p, const Range& r, c
 }
 
 // Source offset of the 16 bytes that lane `lane` of direct load k brings into
-// LDS byte 1024 k + 16 lane: token t, LDS chunk j holds global chunk j ^ swz(t).
+// LDS byte 1024 k + 16 lane. bf16: token t, LDS chunk j holds global chunk
+// j ^ swz(t). FP8: records land unchanged; the part of the last load past the
+// 32 records (t = 32) lies outside the buffer and reads zeros.
+template <int FMT>
 __device__ __forceinline__ uint32_t x_load_off(int k, int lane, int st) {
-  const int pc = 64 * k + lane;
-  const int t = pc / 72;
-  return static_cast<uint32_t>(t * st + 16 * ((pc - 72 * t) ^ swz(t)));
+  if constexpr (FMT == kFmtFp8) {
+    const int x = 1024 * k + 16 * lane;
+    const int t = x / kFp8Record;
+    return static_cast<uint32_t>(t * st + (x - kFp8Record * t));
+  } else {
+    const int pc = 64 * k + lane;
+    const int t = pc / 72;
+    return static_cast<uint32_t>(t * st + 16 * ((pc - 72 * t) ^ swz(t)));
+  }
 }
 
 // Buffer resource word 3 for raw (unformatted, stride 0) buffer access on gfx9-family GPUs.
@@ -119,20 +143,36 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // per lane, with the unit as the buffer (offsets past its 32 rows read zeros).
 // The buffer form keeps the LDS read waits of the compute phases partial
 // (the FLAT form makes every LDS wait a full drain while a load is in flight).
+template <int FMT>
 __device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, const uint32_t (&off)[9], int st) {
+  using X = XLayout<FMT>;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, kXHalf * st, kRawBufferWord3);
 #pragma unroll
-  for (int j = 0; j < XLayout::kLoadsPerWave; ++j) {
+  for (int j = 0; j < X::kLoadsPerWave; ++j) {
     const int k = wave + kWaves * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
+    if (k < X::kLoads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
   }
 }
 
-// s_waitcnt vmcnt(9): one unit's direct loads may stay in flight.
-// (vmcnt: bits 3:0 and 15:14; expcnt 6:4 = 7 and lgkmcnt 11:8 = 15 mean no wait.)
-__device__ __forceinline__ void wait_vm_one_unit() { __builtin_amdgcn_s_waitcnt(0x0F70 | XLayout::kLoadsPerWave); }
-static_assert(XLayout::kLoadsPerWave < 16 && XLayout::kLoadsPerWave == 9, "vmcnt low field; load offsets per lane");
+// Wait until at most one unit's direct loads of this wave are in flight:
+// s_waitcnt vmcnt(n) with n = the wave's loads per unit (bf16 9; FP8 6 for
+// wave 0, 5 for the others). (vmcnt: bits 3:0 and 15:14; expcnt 6:4 = 7 and
+// lgkmcnt 11:8 = 15 mean no wait.)
+template <int FMT>
+__device__ __forceinline__ void wait_vm_one_unit(int wave) {
+  if constexpr (FMT == kFmtFp8) {
+    if (wave == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 9);
+  }
+}
+static_assert(XLayout<kFmtBf16>::kLoadsPerWave == 9 && XLayout<kFmtFp8>::kLoadsPerWave == 6,
+              "wait counts and load offsets per lane");
 
 // Lane-constant indices. MFMA 16x16x32: lane l supplies A[i = l % 16][k-slots
 // 8 (l / 16) .. + 7] and B[the same k-slots][j = l % 16]; D register i of lane
@@ -145,30 +185,78 @@ struct XLane {
   uint32_t ld_off[9];   // direct loads: source offset of this lane's 16 bytes in load wave + 4 j
 };
 
-// One unit of the pipeline. `cur` holds the unit (32 bf16 rows), `nxt`
-// receives the unit two ahead, `work` is the LDS after the ring (P^T, rescale
-// factors, flags, Q^T chunks). The regions are disjoint; the restrict
-// qualifiers let the compiler see that the LDS reads of this unit never touch
-// the direct loads in flight into `nxt`.
+// One unit of the pipeline. `cur` holds the unit (32 bf16 rows, or 32 FP8
+// records), `nxt` receives the unit two ahead, `work` is the LDS after the
+// ring (FP8 conversion buffers, P^T, rescale factors, flags, Q^T chunks). The
+// regions are disjoint; the restrict qualifiers let the compiler see that the
+// LDS reads of this unit never touch the direct loads in flight into `nxt`.
+template <int FMT>
 __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
                                        uint8_t* __restrict__ work, const uint8_t* next_src, int st, const XLane& ln,
                                        int L, const int (&last_ok)[2], int tok0, int valid, bool this_ok,
-                                       float scale_log2, int unit_id, const bf16x8 (&qf)[XLayout::kRegChunks][2],
-                                       f32x4 (&acc)[8][8], float (&m_run)[2], float (&l_run)[2]) {
-  using X = XLayout;
+                                       float scale_log2, int unit_id,
+                                       const bf16x8 (&qf)[XLayout<FMT>::kRegChunks][2], f32x4 (&acc)[8][8],
+                                       float (&m_run)[2], float (&l_run)[2]) {
+  using X = XLayout<FMT>;
+  constexpr bool kFp8 = X::kFp8;
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
-  uint8_t* const lds = work - X::kP;
+  uint8_t* const lds = work - X::kConv;
+  const float* sct = reinterpret_cast<const float*>(lds + X::kScale);   // FP8: [group][token] scales
 
-  // ---- zero the rows past the sequence end (or the whole unit of a bad page) --------
-  if (valid < kXHalf || !this_ok) {
-    const int z0 = this_ok ? valid : 0;
-    for (int x = z0 * kRowBytes + 16 * tid; x < kXHalfBytes; x += 16 * kThreads)
-      *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
+  // ---- stage the unit: FP8 conversion, or zero the bf16 rows past the end --------------
+  uint8_t* page;                                  // bf16 rows (1152 B, swizzled chunks)
+  if constexpr (kFp8) {
+    uint8_t* conv = lds + X::kConv;
+    float* scw = reinterpret_cast<float*>(lds + X::kScale);
+    if (tid < 4 * kXHalf) {
+      const int g = tid >> 5, t = tid & 31;
+      scw[tid] = (this_ok && t < valid) ? *reinterpret_cast<const float*>(cur + t * kFp8Record + 512 + 4 * g) : 0.f;
+    }
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+      const int item = tid + kThreads * j;          // 32 tokens x 32 chunks of 16 codes
+      const int t = item >> 5, ch = item & 31;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 16 * ch);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t k01, k23;
+        e4m3x4_to_bf16(w[i], k01, k23);
+        if (i < 2) {
+          lo[2 * i] = k01;
+          lo[2 * i + 1] = k23;
+        } else {
+          hi[2 * i - 4] = k01;
+          hi[2 * i - 3] = k23;
+        }
+      }
+      if (!(this_ok && t < valid)) {
+        lo = u32x4{0u, 0u, 0u, 0u};
+        hi = lo;
+      }
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch)) = lo;
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch + 1)) = hi;
+    }
+    {
+      const int t = tid >> 3, rr = tid & 7;         // 32 tokens x 8 RoPE chunks
+      u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 528 + 16 * rr);
+      if (!(this_ok && t < valid)) w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 64 + rr)) = w;
+    }
     lds_barrier_keep_loads();
+    page = conv;
+  } else {
+    if (valid < kXHalf || !this_ok) {
+      const int z0 = this_ok ? valid : 0;
+      for (int x = z0 * kRowBytes + 16 * tid; x < kXHalfBytes; x += 16 * kThreads)
+        *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
+      lds_barrier_keep_loads();
+    }
+    page = cur;
   }
 
   // ---- the unit two ahead -> nxt ----------------------------------------------------
-  if (next_src != nullptr) x_issue(next_src, nxt, wave, ln.ld_off, st);
+  if (next_src != nullptr) x_issue<FMT>(next_src, nxt, wave, ln.ld_off, st);
 
   // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 32 w + 16 rb + r16] -------------------
   const uint8_t* qlds = lds + X::kQ;
@@ -180,27 +268,58 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   };
   // K: token 16 tt + r16, dims 32 c + 8 q4 .. + 7 = logical chunk 8 (c / 2) + 4 (c & 1) + q4
   auto kload = [&](int c, int tt) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(cur + ln.k_off[c & 1] + 16 * tt * kRowBytes + 128 * (c >> 1));
+    return *reinterpret_cast<const bf16x8*>(page + ln.k_off[c & 1] + 16 * tt * kRowBytes + 128 * (c >> 1));
   };
   f32x4 s[2][2];                                  // [token tile][row block]
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) s[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // chunk order: bf16 0..17; FP8 the RoPE chunks 16, 17 first (unscaled), then
+  // the 4 latent groups of 4 chunks, each group's partial logits scaled and added
+  auto corder = [](int i) { return kFp8 ? (i < 2 ? 16 + i : i - 2) : i; };
   bf16x8 kbuf[2][2];
+  f32x4 part[2][2];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(0, tt);
+  for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(corder(0), tt);
 #pragma unroll
-  for (int c = 0; c < 18; ++c) {
-    if (c + 1 < 18) {
+  for (int i = 0; i < 18; ++i) {
+    const int c = corder(i);
+    if (i + 1 < 18) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) kbuf[(c + 1) & 1][tt] = kload(c + 1, tt);
+      for (int tt = 0; tt < 2; ++tt) kbuf[(i + 1) & 1][tt] = kload(corder(i + 1), tt);
     }
     const bf16x8 q0 = qop(c, 0), q1 = qop(c, 1);
+    if (!kFp8 || i < 2) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      s[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c & 1][tt], q0, s[tt][0], 0, 0, 0);
-      s[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c & 1][tt], q1, s[tt][1], 0, 0, 0);
+      for (int tt = 0; tt < 2; ++tt) {
+        s[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q0, s[tt][0], 0, 0, 0);
+        s[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q1, s[tt][1], 0, 0, 0);
+      }
+    } else {
+      const int g = (i - 2) >> 2, j = (i - 2) & 3;
+      if (j == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) part[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        part[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q0, part[tt][0], 0, 0, 0);
+        part[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q1, part[tt][1], 0, 0, 0);
+      }
+      if (j == 3) {
+        // tokens 16 tt + 4 q4 + 0..3 of this lane, scale group g
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + g * kXHalf + 16 * tt + 4 * q4);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[tt][rb][e] += sc[e] * part[tt][rb][e];
+        }
+      }
     }
   }
 
@@ -277,27 +396,53 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   // the token order of P^T slot q4
   auto vload = [&](int dd) -> bf16x8 {
     const int d = 8 * wave + dd;                  // 16-dim block of V
-    const uint8_t* a0 = cur + ln.v_off[d & 3] + 128 * (d >> 2);
+    const uint8_t* a0 = page + ln.v_off[d & 3] + 128 * (d >> 2);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  bf16x8 pb[8];
+  // bf16: all 8 row blocks of P^T in registers, each V^T operand read once.
+  // FP8: two halves of 4 row blocks (V^T read twice) -- the scale folding
+  // needs the registers.
+  constexpr int kHalves = kFp8 ? 2 : 1;
+  constexpr int kRB = 8 / kHalves;
+  f32x4 sa, sb;
+  if constexpr (kFp8) {
+    // this wave's dims are scale group `wave`: the per-token scales of its
+    // k-slot tokens (4 q4 + 0..3, 16 + 4 q4 + 0..3) are folded into P^T
+    sa = *reinterpret_cast<const f32x4*>(sct + wave * kXHalf + 4 * q4);
+    sb = *reinterpret_cast<const f32x4*>(sct + wave * kXHalf + 16 + 4 * q4);
+  }
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) pb[rr] = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(16 * rr + r16, q4));
-  bf16x8 va[2];
-  va[0] = vload(0);
+  for (int hv = 0; hv < kHalves; ++hv) {
+    bf16x8 pb[kRB];
 #pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    if (dd + 1 < 8) va[(dd + 1) & 1] = vload(dd + 1);
+    for (int r = 0; r < kRB; ++r)
+      pb[r] = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(16 * (kRB * hv + r) + r16, q4));
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr)
-      acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd & 1], pb[rr], acc[dd][rr], 0, 0, 0);
+      for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[r][e] = static_cast<__bf16>(static_cast<float>(pb[r][e]) * (e < 4 ? sa[e] : sb[e - 4]));
+    }
+    bf16x8 va[2];
+    va[0] = vload(0);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      if (dd + 1 < 8) va[(dd + 1) & 1] = vload(dd + 1);
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        const int rr = kRB * hv + r;
+        acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd & 1], pb[r], acc[dd][rr], 0, 0, 0);
+      }
+    }
   }
 }
 
+template <int FMT>
 __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
-  using X = XLayout;
+  using X = XLayout<FMT>;
   constexpr int M_TILE = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[X::kTotal];
 
@@ -322,7 +467,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   const int st = static_cast<int>(p.kv_st);
 #pragma unroll
-  for (int j = 0; j < X::kLoadsPerWave; ++j) ln.ld_off[j] = x_load_off(wave + kWaves * j, ln.lane, st);
+  for (int j = 0; j < X::kLoadsPerWave; ++j) ln.ld_off[j] = x_load_off<FMT>(wave + kWaves * j, ln.lane, st);
 
   // XCD-aware order: consecutive logical workgroups share an XCD (and its L2)
   const int per_xcd = gridDim.x / 8;
@@ -376,23 +521,25 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     return kv_head + static_cast<int64_t>(pg) * p.kv_sp + static_cast<int64_t>(u.hf) * kXHalf * st;
   };
 
-  // ---- prime the ring: the first two units ----------------------------------------------
-  // u1 is in flight into `slot`, u2 into the next slot; ok = its page is valid
-  // (a unit is issued iff it is inside the range and ok).
-  XUnit u1 = x_seek(p, r, r.begin_b), u2;
-  bool ok1 = true, ok2 = true;
-  if (u1.b <= r.end_b) {
-    const uint8_t* src = unit_src(u1);
-    ok1 = src != nullptr;
-    if (ok1) x_issue(src, lds + X::kRing, wave, ln.ld_off, st);
-    u2 = x_next(p, r, u1);
-  } else {
-    u2 = u1;
-  }
-  if (u2.b <= r.end_b) {
-    const uint8_t* src = unit_src(u2);
-    ok2 = src != nullptr;
-    if (ok2) x_issue(src, lds + X::kRing + X::kSlot, wave, ln.ld_off, st);
+  // ---- prime the ring -------------------------------------------------------------------
+  // uq[0] is in flight into `slot` (the next unit to compute), uq[i] into the
+  // i-th slot after it; okq = its page is valid (a unit is issued iff it is
+  // inside the range and ok).
+  constexpr int kAhead = X::kAhead;
+  XUnit uq[kAhead];
+  bool okq[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    if (i == 0)
+      uq[0] = x_seek(p, r, r.begin_b);
+    else
+      uq[i] = (uq[i - 1].b <= r.end_b) ? x_next(p, r, uq[i - 1]) : uq[i - 1];
+    okq[i] = true;
+    if (uq[i].b <= r.end_b) {
+      const uint8_t* src = unit_src(uq[i]);
+      okq[i] = src != nullptr;
+      if (okq[i]) x_issue<FMT>(src, lds + X::kRing + i * X::kSlot, wave, ln.ld_off, st);
+    }
   }
   int slot = 0;
   int unit_id = 0;
@@ -443,31 +590,38 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
       for (int rr = 0; rr < 8; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool bad = false;
 
-    while (u1.b == b) {
-      const XUnit u = u1;
-      const bool this_ok = ok1;
+    while (uq[0].b == b) {
+      const XUnit u = uq[0];
+      const bool this_ok = okq[0];
       bad |= !this_ok;
-      const bool u2_issued = u2.b <= r.end_b && ok2;
-      if (u2_issued) wait_vm_one_unit(); else wait_vm_all();
+      // loads still allowed in flight: those of the units after u
+      bool later_issued = false;
+#pragma unroll
+      for (int i = 1; i < kAhead; ++i) later_issued |= uq[i].b <= r.end_b && okq[i];
+      if (later_issued) wait_vm_one_unit<FMT>(wave); else wait_vm_all();
       lds_barrier_keep_loads();               // every wave's loads of u landed; unit u - 1 is done everywhere
-      const XUnit u3 = (u2.b <= r.end_b) ? x_next(p, r, u2) : u2;
-      const uint8_t* src3 = nullptr;
-      bool ok3 = true;
-      if (u3.b <= r.end_b) {
-        src3 = unit_src(u3);
-        ok3 = src3 != nullptr;
+      const XUnit last = uq[kAhead - 1];
+      const XUnit un = (last.b <= r.end_b) ? x_next(p, r, last) : last;
+      const uint8_t* src_n = nullptr;
+      bool ok_n = true;
+      if (un.b <= r.end_b) {
+        src_n = unit_src(un);
+        ok_n = src_n != nullptr;
       }
       const int tok0 = u.pi * kPage + u.hf * kXHalf;
       const int valid = min(L - tok0, kXHalf);
-      const int slot3 = (slot + 2) % kXSlots;  // held unit u - 1, free now
-      x_step(lds + X::kRing + slot * X::kSlot, lds + X::kRing + slot3 * X::kSlot, lds + X::kP, src3, st, ln, L,
-             last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run);
+      const int slot_n = (slot + kAhead) % X::kSlots;   // held unit u - 1, free now
+      x_step<FMT>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + slot_n * X::kSlot, lds + X::kConv, src_n, st,
+                  ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run);
       ++unit_id;
-      slot = (slot + 1) % kXSlots;
-      u1 = u2;
-      ok1 = ok2;
-      u2 = u3;
-      ok2 = ok3;
+      slot = (slot + 1) % X::kSlots;
+#pragma unroll
+      for (int i = 0; i + 1 < kAhead; ++i) {
+        uq[i] = uq[i + 1];
+        okq[i] = okq[i + 1];
+      }
+      uq[kAhead - 1] = un;
+      okq[kAhead - 1] = ok_n;
     }
 
     // ---- epilogue: l of every row through LDS; each wave writes its 128 dims ----
@@ -529,9 +683,12 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_split_x(const DecodeParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+hipError_t launch_split_x(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop) {
-  hipExtLaunchKernelGGL(splitkv_x_kernel, dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
+  if (kv_format == kFmtFp8)
+    hipExtLaunchKernelGGL(splitkv_x_kernel<kFmtFp8>, dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
+  else
+    hipExtLaunchKernelGGL(splitkv_x_kernel<kFmtBf16>, dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 

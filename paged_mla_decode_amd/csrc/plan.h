@@ -3,13 +3,13 @@
 // The split-KV kernels run 4 wavefronts per workgroup over the query rows of
 // one KV head (rows = s_q * h_q / h_kv, the head fold of the
 // deepseekonline.chat day-1 post, "Dynamische Sequenzoptimierung").
-// Up to 64 rows (and FP8 pages): each wavefront owns a block of 16 rows and a
+// Up to 64 rows: each wavefront owns a block of 16 rows and a
 // group of the 64 tokens of every page it visits:
 //   rb = 16-row blocks per workgroup, tg = token groups per page, rb * tg = 4.
 // Few rows (memory-bound decode) split each page's tokens over the waves; 64
 // rows give each wave 16 rows and the whole page.
-// More than 64 rows with bf16 pages: 128-row tiles (wide = 1, rb = 8), the S
-// phase split by rows and the PV phase by value dims over the 4 wavefronts.
+// More than 64 rows: 128-row tiles (wide = 1, rb = 8), the S phase split by
+// rows and the PV phase by value dims over the 4 wavefronts.
 #pragma once
 
 #include <cstdint>
@@ -25,7 +25,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
 struct Plan {
-  int wide;        // 1: 128-row tiles (more than 64 rows, bf16 pages)
+  int wide;        // 1: 128-row tiles (more than 64 rows)
   int rb;          // 16-row blocks per workgroup
   int tg;          // token groups per page (rb * tg == kWaves unless wide)
   int m_tile;      // rows per workgroup
@@ -36,15 +36,16 @@ struct Plan {
 };
 
 inline Plan make_plan(int heads_per_kv, int kv_format) {
+  (void)kv_format;
   Plan p{};
   if (heads_per_kv <= 16) {
     p.rb = 1; p.tg = 4;
   } else if (heads_per_kv <= 32) {
     p.rb = 2; p.tg = 2;
-  } else if (heads_per_kv <= 64 || kv_format != 0) {
+  } else if (heads_per_kv <= 64) {
     p.rb = 4; p.tg = 1;
   } else {
-    p.wide = 1; p.rb = 8; p.tg = 1;   // bf16 pages, more than 64 rows: 128-row tiles
+    p.wide = 1; p.rb = 8; p.tg = 1;   // more than 64 rows: 128-row tiles
   }
   p.m_tile = 16 * p.rb;
   p.m_tiles = (heads_per_kv + p.m_tile - 1) / p.m_tile;

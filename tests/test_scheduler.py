@@ -124,12 +124,12 @@ def test_metadata_independent_of_nothing_but_inputs():
 
 def test_default_parts_fill_the_chip():
     lib = _lib.load()
-    # one workgroup per CU. bf16 pages: up to 64 rows one tile, more than 64
-    # rows 128-row tiles (256 rows: two per range). FP8 pages: 64-row tiles.
+    # one workgroup per CU: up to 64 rows one tile, more than 64 rows 128-row
+    # tiles (256 rows: two per range), for bf16 and FP8 pages alike.
     assert lib.mla_num_parts(64, 16, 1, 0, 256) == 256
     assert lib.mla_num_parts(64, 64, 1, 0, 256) == 256
     assert lib.mla_num_parts(64, 128, 1, 0, 256) == 256
     assert lib.mla_num_parts(64, 256, 1, 0, 256) == 128
-    assert lib.mla_num_parts(64, 128, 1, 1, 256) == 128
-    assert lib.mla_num_parts(64, 256, 1, 1, 256) == 64
+    assert lib.mla_num_parts(64, 128, 1, 1, 256) == 256
+    assert lib.mla_num_parts(64, 256, 1, 1, 256) == 128
     assert lib.mla_num_parts(64, 16, 1, 0, 0) in (-1, 256, lib.mla_device_cu_count(0))
