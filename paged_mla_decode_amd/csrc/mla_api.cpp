@@ -159,6 +159,8 @@ mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
   if (!aligned16(a->q)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: q must be 16-byte aligned");
   if (a->q_stride[2] < mla::kDqk && a->h_q > 1)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: q head stride overlaps the 576 dims");
+  if (((a->s_q - 1) * a->q_stride[1] + (a->h_q - 1) * a->q_stride[2] + mla::kDqk) * 2 >= (int64_t{1} << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: the q rows of one sequence must span less than 2 GiB");
 
   // kvcache rows: contiguous, 16-byte aligned.
   const int64_t elem = (a->kv_format == MLA_KV_BF16) ? 2 : 1;

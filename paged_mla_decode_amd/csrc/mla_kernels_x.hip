@@ -568,16 +568,33 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
       }
     }
     lds_barrier_keep_loads();                 // no wave still reads the previous sequence's Q^T chunks
-    for (int item = tid; item < X::kQChunks * 128 * 4; item += kThreads) {
-      const int qs = item / 512, row = (item >> 2) & 127, sl = item & 3;
-      const int c = X::qchunk(qs);
-      const int grow = mt * M_TILE + row;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (grow < p.rows) {
-        const int sg = grow / p.group, hg = kvh * p.group + grow % p.group;
-        v = *reinterpret_cast<const u32x4*>(p.q + b * p.q_sb + sg * p.q_ss + hg * p.q_sh + 32 * c + 8 * sl);
+    {
+      // Q^T chunks of the 128 rows straight into LDS: one direct load per 16
+      // rows of a chunk (lane l: row 16 i + l / 4, stored slot l % 4, i.e. the
+      // logical slot (l % 4) ^ ((row >> 1) & 3)); rows past p.rows read zeros
+      // (their offset lies outside the buffer)
+      const uint16_t* qb = p.q + b * p.q_sb;
+      const int q_bytes = 2 * static_cast<int>((p.s_q - 1) * p.q_ss + (p.h_q - 1) * p.q_sh + kDqk);
+      const __amdgpu_buffer_rsrc_t qrsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qb), 0, q_bytes, kRawBufferWord3);
+      const int lrow = ln.lane >> 2, pslot = ln.lane & 3;
+#pragma unroll
+      for (int j = 0; j < (X::kQChunks * 8 + kWaves - 1) / kWaves; ++j) {
+        const int k = wave + kWaves * j;
+        if (k < X::kQChunks * 8) {
+          const int qs = k >> 3, i = k & 7;
+          const int row = 16 * i + lrow;
+          const int sl = pslot ^ ((row >> 1) & 3);
+          const int grow = mt * M_TILE + row;
+          uint32_t off = 0xFFFFFFF0u;
+          if (grow < p.rows) {
+            const int sg = grow / p.group, hg = kvh * p.group + grow % p.group;
+            off = static_cast<uint32_t>(2 * (sg * p.q_ss + hg * p.q_sh + 32 * X::qchunk(qs) + 8 * sl));
+          }
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, LDS_PTR(void, lds + X::kQ + qs * kXQChunkBytes + 1024 * i),
+                                                   16, off, 0, 0, 0);
+        }
       }
-      *reinterpret_cast<u32x4*>(lds + X::kQ + qs * kXQChunkBytes + xrow_off(row, sl)) = v;
     }
     wait_vm_all();
     lds_barrier();

@@ -50,7 +50,10 @@ inline Plan make_plan(int heads_per_kv, int kv_format) {
   p.m_tile = 16 * p.rb;
   p.m_tiles = (heads_per_kv + p.m_tile - 1) / p.m_tile;
   p.wgs_per_cu = 1;      // the two-page LDS ring (144-155 KB) leaves room for one workgroup per CU
-  p.split_cost = 1;
+  // per-piece fixed work (Q load, partial write and merge) in pages of KV: 16 rows
+  // carry 18 KB of Q and 32 KB of partial O per piece, 128 rows 8x that
+  // (measured best at 3 for 128-row tiles on the h_q = 128 workloads)
+  p.split_cost = p.wide ? 3 : 1;
   p.min_pages = 1;
   return p;
 }

@@ -7,88 +7,84 @@
 // only those shapes; the field layout and the cut rule below are this
 // library's own.
 //
-// Cost line: sequence b occupies split_cost + n_b units, n_b = ceil(L_b / 64)
-// pages, sequences laid end to end in batch order. Range p is the interval
-// [floor(p * T / P), floor((p + 1) * T / P)) of the line (T = total cost,
-// P = ranges). A cut that falls inside a sequence's fixed cost moves to the
-// start of that sequence; one that falls inside its pages cuts between pages,
-// snapped to the sequence's start or end when it would leave a piece smaller
-// than min_pages. Cuts are monotone, so the ranges partition every
-// (sequence, page) exactly once, in order, and every sequence -- also one of
-// length 0 -- lies in exactly one range or spans several consecutive ones.
-#include <algorithm>
+// Greedy fill: every piece of a sequence costs split_cost (its fixed work:
+// loading Q, writing a partial result, merging it) plus its pages. Each range
+// gets a budget of ceil(T / P) + split_cost, T = sum of pages + split_cost per
+// sequence, P = ranges, and takes sequences in batch order while they fit;
+// the sequence that does not fit is cut between pages so that the range uses
+// its budget, unless that would leave a piece smaller than min_pages (then
+// the range stops before it, or takes its few remaining pages). The last
+// range takes whatever is left. Ranges are consecutive, so every
+// (sequence, page) lies in exactly one range, in order, and every sequence --
+// also one of length 0 -- lies in exactly one range or spans several
+// consecutive ones.
 #include <cstring>
 #include <vector>
 
 #include "plan.h"
 
 namespace mla {
-namespace {
-
-struct Cut {
-  int b;      // sequence
-  int64_t i;  // page within b; normalised so that i < n_b unless n_b == 0 (then i == 0)
-};
-
-}  // namespace
 
 int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, int min_pages,
              int32_t* meta, int32_t* num_splits) {
-  std::vector<int64_t> npages(batch), start(batch + 1);
+  std::vector<int64_t> npages(batch);
   int64_t total = 0;
   for (int b = 0; b < batch; ++b) {
     npages[b] = (static_cast<int64_t>(seqlens[b]) + kPage - 1) / kPage;
-    start[b] = total;
     total += split_cost + npages[b];
   }
-  start[batch] = total;
-
-  // Cut position x on the cost line -> (sequence, page), normalised.
-  auto cut_at = [&](int64_t x) -> Cut {
-    if (x >= total) return Cut{batch, 0};
-    int b = static_cast<int>(std::upper_bound(start.begin(), start.begin() + batch + 1, x) - start.begin()) - 1;
-    int64_t i = x - start[b] - split_cost;
-    if (i <= 0 || i < min_pages) return Cut{b, 0};
-    if (npages[b] - i < min_pages) return Cut{b + 1, 0};
-    return Cut{b, i};
-  };
-
-  std::vector<Cut> cuts(num_parts + 1);
-  for (int p = 0; p <= num_parts; ++p) {
-    int64_t x = (p == num_parts) ? total : static_cast<int64_t>((static_cast<__int128>(p) * total) / num_parts);
-    cuts[p] = cut_at(x);
-  }
-  cuts[0] = Cut{0, 0};
-  cuts[num_parts] = Cut{batch, 0};
+  const int64_t budget = (total + num_parts - 1) / num_parts + split_cost;
 
   std::vector<int32_t> pieces(batch, 0);
   std::memset(meta, 0, sizeof(int32_t) * static_cast<size_t>(num_parts) * kMetaInts);
+  int b = 0;        // position: sequence b, page i
+  int64_t i = 0;
   for (int p = 0; p < num_parts; ++p) {
     int32_t* m = meta + static_cast<size_t>(p) * kMetaInts;
-    const Cut a = cuts[p], e = cuts[p + 1];
-    const bool empty = (a.b == e.b && a.i == e.i) || a.b >= batch;
-    if (empty) {
+    const int b0 = b;
+    const int64_t i0 = i;
+    int64_t room = budget;
+    const bool last_range = (p == num_parts - 1);
+    while (b < batch) {
+      const int64_t left = npages[b] - i;
+      if (last_range || split_cost + left <= room) {      // the rest of sequence b fits
+        room -= split_cost + left;
+        ++b;
+        i = 0;
+        continue;
+      }
+      const int64_t take = room - split_cost;
+      if (take < min_pages || take <= 0) break;            // nothing worth a new piece fits
+      if (left - take < min_pages) {                       // do not leave a sliver behind
+        ++b;
+        i = 0;
+      } else {
+        i += take;
+      }
+      break;
+    }
+    if (b0 == b && i0 == i) {                              // empty range
       m[0] = -1; m[1] = 0; m[2] = -2; m[3] = 0; m[4] = 0;
       continue;
     }
     int end_b;
     int64_t end_page;
-    if (e.i == 0) {             // ends at the end of the previous sequence
-      end_b = e.b - 1;
+    if (i == 0) {               // ends at the end of the previous sequence
+      end_b = b - 1;
       end_page = npages[end_b];
     } else {
-      end_b = e.b;
-      end_page = e.i;
+      end_b = b;
+      end_page = i;
     }
-    m[0] = a.b;
-    m[1] = static_cast<int32_t>(a.i);
+    m[0] = b0;
+    m[1] = static_cast<int32_t>(i0);
     m[2] = end_b;
     m[3] = static_cast<int32_t>(end_page);
-    m[4] = pieces[a.b];
-    for (int b = a.b; b <= end_b; ++b) pieces[b] += 1;
+    m[4] = pieces[b0];
+    for (int s = b0; s <= end_b; ++s) pieces[s] += 1;
   }
   num_splits[0] = 0;
-  for (int b = 0; b < batch; ++b) num_splits[b + 1] = num_splits[b] + pieces[b];
+  for (int s = 0; s < batch; ++s) num_splits[s + 1] = num_splits[s] + pieces[s];
   return num_splits[batch];
 }
 
