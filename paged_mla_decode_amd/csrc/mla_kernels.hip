@@ -731,7 +731,7 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   hipEvent_t ev2 = events ? static_cast<hipEvent_t>(events[2]) : nullptr;
   hipError_t err;
   if (plan.wide) {
-    err = launch_split_x(p, kv_format, grid, stream, ev0, ev1);
+    err = launch_split_x(p, kv_format, plan.m_tile / 4, grid, stream, ev0, ev1);
   } else if (plan.rb == 1) {
     err = launch_split<1, 4>(p, kv_format, grid, stream, ev0, ev1);
   } else if (plan.rb == 2) {

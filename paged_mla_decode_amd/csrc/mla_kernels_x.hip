@@ -49,43 +49,49 @@ using namespace dev;
 constexpr int kXHalf = 32;                                  // tokens per unit
 constexpr int kXHalfBytes = kXHalf * kRowBytes;             // 36864 = 36 x 1 KB: bf16 rows
 constexpr int kXRawBytes = kXHalf * kFp8Record;             // 20992: FP8 records
-constexpr int kXPBytes = 128 * kXHalf * 2;                  // 8192: P^T [128 rows][32 tokens] bf16
-constexpr int kXQChunkBytes = 128 * 64;                     // one 32-dim Q^T chunk of 128 rows
 
-// LDS layout (bytes): the ring (bf16: 3 slots, two units ahead; FP8: 2 slots of
-// raw records, one unit ahead); FP8 only: the converted unit (bf16 rows, the
-// bf16 ring layout) and the scales [4 groups][32 tokens]; then P^T, rescale
-// factors, flags, and the Q^T chunks kept in LDS for all 128 rows (the other
-// chunks of each row stay in VGPRs): bf16 {0, 1, 2, 16, 17}, FP8 {0 .. 6, 16, 17}.
-template <int FMT>
+// LDS layout (bytes) for a tile of 64 RBW rows (RBW = 16-row blocks per wave
+// in the S phase: 2 for 128-row tiles, 1 for 64-row tiles): the ring of
+// 32-token units (bf16 rows, or raw FP8 records); FP8 only: the converted unit
+// (bf16 rows, the bf16 ring layout) and the scales [4 groups][32 tokens]; then
+// P^T, rescale factors, flags, and the Q^T chunks kept in LDS for all rows
+// (128-row tiles only: bf16 {0, 1, 2, 16, 17}, FP8 {0 .. 6, 16, 17}; the other
+// chunks of each row stay in VGPRs). Ring depth: 128-row bf16 3 slots (two
+// units ahead), 128-row FP8 2 slots (one ahead), 64-row 4 slots (three ahead).
+template <int FMT, int RBW>
 struct XLayout {
   static constexpr bool kFp8 = (FMT == kFmtFp8);
+  static constexpr int kRows = 64 * RBW;                    // rows per tile
   static constexpr int kSlot = kFp8 ? 21 * 1024 : kXHalfBytes;
-  static constexpr int kSlots = kFp8 ? 2 : 3;
+  static constexpr int kSlots = RBW == 1 ? 4 : (kFp8 ? 2 : 3);
   static constexpr int kAhead = kSlots - 1;                 // units in flight beyond the current one
   static constexpr int kRing = 0;
   static constexpr int kConv = kRing + kSlots * kSlot;
   static constexpr int kScale = kConv + (kFp8 ? kXHalfBytes : 0);
   static constexpr int kP = kScale + (kFp8 ? 4 * kXHalf * 4 : 0);
-  static constexpr int kAlpha = kP + kXPBytes;              // [128] fp32
-  static constexpr int kFlag = kAlpha + 128 * 4;            // [4] int32 (64 B)
-  static constexpr int kQ = kFlag + 64;
-  static constexpr int kQChunks = kFp8 ? 9 : 5;
-  static constexpr int kTotal = kQ + kQChunks * kXQChunkBytes;   // bf16 160320, FP8 162880
+  static constexpr int kAlpha = kP + kRows * kXHalf * 2;    // P^T: [rows][32 tokens] bf16
+  static constexpr int kFlag = kAlpha + kRows * 4;          // alpha: [rows] fp32
+  static constexpr int kQ = kFlag + 64;                     // flags: [4] int32
+  static constexpr int kQChunks = RBW == 1 ? 0 : (kFp8 ? 9 : 5);
+  static constexpr int kQChunkBytes = kRows * 64;           // one 32-dim Q^T chunk of all rows
+  static constexpr int kTotal = kQ + kQChunks * kQChunkBytes;
   static constexpr int kLoads = kFp8 ? 21 : kXHalfBytes / 1024;   // 1 KB direct loads per unit (36 / 21)
   static constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;   // 9 / 6
-  static constexpr int kLow = kFp8 ? 7 : 3;                      // chunks 0 .. kLow-1 in LDS
+  static constexpr int kLow = RBW == 1 ? 0 : (kFp8 ? 7 : 3);     // chunks 0 .. kLow-1 in LDS
   // LDS slot of Q^T chunk c, or -1 when it lives in VGPRs
-  static constexpr int qslot(int c) { return c < kLow ? c : (c == 16 ? kLow : (c == 17 ? kLow + 1 : -1)); }
+  static constexpr int qslot(int c) {
+    return kQChunks == 0 ? -1 : (c < kLow ? c : (c == 16 ? kLow : (c == 17 ? kLow + 1 : -1)));
+  }
   static constexpr int kRegChunks = 18 - kQChunks;
-  // register index of chunk c (chunks kLow .. 15)
-  static constexpr int qreg(int c) { return c - kLow; }
+  // register index of chunk c
+  static constexpr int qreg(int c) { return kQChunks == 0 ? c : c - kLow; }
   // LDS chunk index qs -> Q chunk
   static constexpr int qchunk(int qs) { return qs < kLow ? qs : 16 - kLow + qs; }
 };
-static_assert(XLayout<kFmtBf16>::kTotal <= 163840 && XLayout<kFmtFp8>::kTotal <= 163840, "LDS budget");
-static_assert(XLayout<kFmtBf16>::kLoads % kWaves == 0, "equal direct-load counts per wave (bf16)");
-static_assert(XLayout<kFmtFp8>::kSlot >= kXRawBytes, "FP8 slot holds a unit");
+static_assert(XLayout<kFmtBf16, 2>::kTotal <= 163840 && XLayout<kFmtFp8, 2>::kTotal <= 163840, "LDS budget");
+static_assert(XLayout<kFmtBf16, 1>::kTotal <= 163840 && XLayout<kFmtFp8, 1>::kTotal <= 163840, "LDS budget");
+static_assert(XLayout<kFmtBf16, 2>::kLoads % kWaves == 0, "equal direct-load counts per wave (bf16)");
+static_assert(XLayout<kFmtFp8, 2>::kSlot >= kXRawBytes, "FP8 slot holds a unit");
 
 // Q^T chunks and P^T rows in LDS: 64 bytes per row (4 x 16 B); the 16-byte
 // slot is XOR-swizzled with (row >> 1) & 3 so 8 consecutive rows hit 8
@@ -118,10 +124,22 @@ __device__ __forceinline__ XUnit x_next(const DecodeParams& p, const Range& r, c
   return x_seek(p, r, u.b + 1);
 }
 
-// Source offset of the 16 bytes that lane `lane` of direct load k brings into
-// LDS byte 1024 k + 16 lane. bf16: token t, LDS chunk j holds global chunk
-// j ^ swz(t). FP8: records land unchanged; the part of the last load past the
-// 32 records (t = 32) lies outside the buffer and reads zeros.
+// bf16 unit layout in LDS (32 tokens x 1152 B = 36 KB), chunk-group major:
+// 16-byte chunk c of token t sits at
+//   4096 (c / 8) + 128 t + 16 ((c % 8) ^ (t % 8)).
+// Each 128-byte column block of the 32 rows is 4 KB; inside it the XOR keeps
+// the K reads (16 consecutive tokens, one chunk) and the transposed V reads
+// (4 tokens x 2 chunks per 16 lanes) on distinct banks, as with 1152-byte
+// rows (consecutive tokens again sit half a bank window apart). This layout
+// lets one direct load cover 8 tokens x 128 B with a per-lane source offset
+// that does not depend on the load: lane l reads token l / 8 of the block,
+// chunk (l % 8) ^ (l / 8).
+__device__ __forceinline__ int xk_off(int t, int c) { return 4096 * (c >> 3) + 128 * t + 16 * ((c & 7) ^ (t & 7)); }
+
+// Per-lane source offset of the direct loads (bf16: above, the load-dependent
+// part goes into the scalar offset; FP8: records land unchanged and the part
+// of the last load past the 32 records lies outside the buffer and reads
+// zeros -- one offset per load).
 template <int FMT>
 __device__ __forceinline__ uint32_t x_load_off(int k, int lane, int st) {
   if constexpr (FMT == kFmtFp8) {
@@ -129,9 +147,8 @@ __device__ __forceinline__ uint32_t x_load_off(int k, int lane, int st) {
     const int t = x / kFp8Record;
     return static_cast<uint32_t>(t * st + (x - kFp8Record * t));
   } else {
-    const int pc = 64 * k + lane;
-    const int t = pc / 72;
-    return static_cast<uint32_t>(t * st + 16 * ((pc - 72 * t) ^ swz(t)));
+    (void)k;
+    return static_cast<uint32_t>((lane >> 3) * st + 16 * ((lane & 7) ^ (lane >> 3)));
   }
 }
 
@@ -143,35 +160,53 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // per lane, with the unit as the buffer (offsets past its 32 rows read zeros).
 // The buffer form keeps the LDS read waits of the compute phases partial
 // (the FLAT form makes every LDS wait a full drain while a load is in flight).
+// bf16: load k = 4 g + w (wave w issues the loads of token block w) brings
+// tokens 8 w .. 8 w + 7 of column block g; FP8: load k brings LDS bytes
+// 1024 k .. + 1023 of the 32 records.
 template <int FMT>
 __device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, const uint32_t (&off)[9], int st) {
-  using X = XLayout<FMT>;
+  using X = XLayout<FMT, 2>;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, kXHalf * st, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < X::kLoadsPerWave; ++j) {
     const int k = wave + kWaves * j;
-    if (k < X::kLoads)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
+    if constexpr (FMT == kFmtFp8) {
+      if (k < X::kLoads)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[0], 8 * wave * st + 128 * j,
+                                               0, 0);
+    }
   }
 }
 
-// Wait until at most one unit's direct loads of this wave are in flight:
-// s_waitcnt vmcnt(n) with n = the wave's loads per unit (bf16 9; FP8 6 for
-// wave 0, 5 for the others). (vmcnt: bits 3:0 and 15:14; expcnt 6:4 = 7 and
-// lgkmcnt 11:8 = 15 mean no wait.)
+// s_waitcnt vmcnt(N) (vmcnt: bits 3:0 and 15:14; expcnt 6:4 = 7 and lgkmcnt
+// 11:8 = 15 mean no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `later` units' direct loads of this wave are in flight
+// (later = 0, 1 or 2): the wave's loads per unit are 9 (bf16), or 6 for wave 0
+// and 5 for the others (FP8).
 template <int FMT>
-__device__ __forceinline__ void wait_vm_one_unit(int wave) {
-  if constexpr (FMT == kFmtFp8) {
-    if (wave == 0)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+__device__ __forceinline__ void wait_units(int later, int wave) {
+  if (later <= 0) {
+    wait_vmcnt<0>();
+  } else if constexpr (FMT == kFmtFp8) {
+    if (wave == 0) {
+      if (later == 1) wait_vmcnt<6>(); else wait_vmcnt<12>();
+    } else {
+      if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<10>();
+    }
   } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 9);
+    if (later == 1) wait_vmcnt<9>(); else wait_vmcnt<18>();
   }
 }
-static_assert(XLayout<kFmtBf16>::kLoadsPerWave == 9 && XLayout<kFmtFp8>::kLoadsPerWave == 6,
+static_assert(XLayout<kFmtBf16, 2>::kLoadsPerWave == 9 && XLayout<kFmtFp8, 2>::kLoadsPerWave == 6,
               "wait counts and load offsets per lane");
 
 // Lane-constant indices. MFMA 16x16x32: lane l supplies A[i = l % 16][k-slots
@@ -182,7 +217,7 @@ struct XLane {
   int r16, q4;          // lane % 16, lane / 16
   int k_off[2];         // S phase: K row r16, logical chunks q4 and 4 + q4 (swizzled), bytes
   int v_off[4];         // PV phase: transposed V read offsets, by 16-dim block d & 3
-  uint32_t ld_off[9];   // direct loads: source offset of this lane's 16 bytes in load wave + 4 j
+  uint32_t ld_off[9];   // direct loads: per-lane source offsets (bf16 uses [0] only)
 };
 
 // One unit of the pipeline. `cur` holds the unit (32 bf16 rows, or 32 FP8
@@ -190,14 +225,16 @@ struct XLane {
 // ring (FP8 conversion buffers, P^T, rescale factors, flags, Q^T chunks). The
 // regions are disjoint; the restrict qualifiers let the compiler see that the
 // LDS reads of this unit never touch the direct loads in flight into `nxt`.
-template <int FMT>
+template <int FMT, int RBW>
 __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
                                        uint8_t* __restrict__ work, const uint8_t* next_src, int st, const XLane& ln,
-                                       int L, const int (&last_ok)[2], int tok0, int valid, bool this_ok,
+                                       int L, const int (&last_ok)[RBW], int tok0, int valid, bool this_ok,
                                        float scale_log2, int unit_id,
-                                       const bf16x8 (&qf)[XLayout<FMT>::kRegChunks][2], f32x4 (&acc)[8][8],
-                                       float (&m_run)[2], float (&l_run)[2]) {
-  using X = XLayout<FMT>;
+                                       const bf16x8 (&qf)[XLayout<FMT, RBW>::kRegChunks][RBW],
+                                       f32x4 (&acc)[8][4 * RBW], float (&m_run)[RBW], float (&l_run)[RBW],
+                                       bool wave_live, int live_rr) {
+  using X = XLayout<FMT, RBW>;
+  constexpr int NRR = 4 * RBW;                    // 16-row blocks per tile
   constexpr bool kFp8 = X::kFp8;
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   uint8_t* const lds = work - X::kConv;
@@ -234,22 +271,24 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
         lo = u32x4{0u, 0u, 0u, 0u};
         hi = lo;
       }
-      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch)) = lo;
-      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 2 * ch + 1)) = hi;
+      *reinterpret_cast<u32x4*>(conv + xk_off(t, 2 * ch)) = lo;
+      *reinterpret_cast<u32x4*>(conv + xk_off(t, 2 * ch + 1)) = hi;
     }
     {
       const int t = tid >> 3, rr = tid & 7;         // 32 tokens x 8 RoPE chunks
       u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 528 + 16 * rr);
       if (!(this_ok && t < valid)) w = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(conv + chunk_off(t, 64 + rr)) = w;
+      *reinterpret_cast<u32x4*>(conv + xk_off(t, 64 + rr)) = w;
     }
     lds_barrier_keep_loads();
     page = conv;
   } else {
     if (valid < kXHalf || !this_ok) {
       const int z0 = this_ok ? valid : 0;
-      for (int x = z0 * kRowBytes + 16 * tid; x < kXHalfBytes; x += 16 * kThreads)
-        *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
+      for (int idx = tid; idx < 72 * kXHalf; idx += kThreads) {   // 16-byte chunks of the unit
+        const int t = (idx >> 3) & 31;                            // block idx / 256, token, chunk idx % 8
+        if (t >= z0) *reinterpret_cast<u32x4*>(cur + 4096 * (idx >> 8) + 128 * t + 16 * (idx & 7)) = u32x4{0u, 0u, 0u, 0u};
+      }
       lds_barrier_keep_loads();
     }
     page = cur;
@@ -258,66 +297,73 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   // ---- the unit two ahead -> nxt ----------------------------------------------------
   if (next_src != nullptr) x_issue<FMT>(next_src, nxt, wave, ln.ld_off, st);
 
-  // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 32 w + 16 rb + r16] -------------------
+  // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 16 RBW w + 16 rb + r16] ----------------
   const uint8_t* qlds = lds + X::kQ;
   auto qop = [&](int c, int rb) -> bf16x8 {
     const int qs = X::qslot(c);
     if (qs >= 0)
-      return *reinterpret_cast<const bf16x8*>(qlds + qs * kXQChunkBytes + xrow_off(32 * wave + 16 * rb + r16, q4));
+      return *reinterpret_cast<const bf16x8*>(qlds + qs * X::kQChunkBytes +
+                                              xrow_off(16 * RBW * wave + 16 * rb + r16, q4));
     return qf[X::qreg(c)][rb];
   };
   // K: token 16 tt + r16, dims 32 c + 8 q4 .. + 7 = logical chunk 8 (c / 2) + 4 (c & 1) + q4
   auto kload = [&](int c, int tt) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(page + ln.k_off[c & 1] + 16 * tt * kRowBytes + 128 * (c >> 1));
+    return *reinterpret_cast<const bf16x8*>(page + ln.k_off[c & 1] + 16 * tt * 128 + 4096 * (c >> 1));
   };
-  f32x4 s[2][2];                                  // [token tile][row block]
+  f32x4 s[2][RBW];                                // [token tile][row block]
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) s[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RBW; ++rb) s[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // chunk order: bf16 0..17; FP8 the RoPE chunks 16, 17 first (unscaled), then
   // the 4 latent groups of 4 chunks, each group's partial logits scaled and added
   auto corder = [](int i) { return kFp8 ? (i < 2 ? 16 + i : i - 2) : i; };
-  bf16x8 kbuf[2][2];
-  f32x4 part[2][2];
+  // (64-row tiles: a wave whose rows all lie past the last row skips the S
+  // phase; its S stays 0)
+  if (RBW == 2 || wave_live) {
+    bf16x8 kbuf[2][2];
+    f32x4 part[2][RBW];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(corder(0), tt);
+    for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(corder(0), tt);
 #pragma unroll
-  for (int i = 0; i < 18; ++i) {
-    const int c = corder(i);
-    if (i + 1 < 18) {
+    for (int i = 0; i < 18; ++i) {
+      const int c = corder(i);
+      if (i + 1 < 18) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) kbuf[(i + 1) & 1][tt] = kload(corder(i + 1), tt);
-    }
-    const bf16x8 q0 = qop(c, 0), q1 = qop(c, 1);
-    if (!kFp8 || i < 2) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        s[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q0, s[tt][0], 0, 0, 0);
-        s[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q1, s[tt][1], 0, 0, 0);
+        for (int tt = 0; tt < 2; ++tt) kbuf[(i + 1) & 1][tt] = kload(corder(i + 1), tt);
       }
-    } else {
-      const int g = (i - 2) >> 2, j = (i - 2) & 3;
-      if (j == 0) {
+      bf16x8 qv[RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) qv[rb] = qop(c, rb);
+      if (!kFp8 || i < 2) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) part[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+          for (int rb = 0; rb < RBW; ++rb)
+            s[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv[rb], s[tt][rb], 0, 0, 0);
+      } else {
+        const int g = (i - 2) >> 2, j = (i - 2) & 3;
+        if (j == 0) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        part[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q0, part[tt][0], 0, 0, 0);
-        part[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], q1, part[tt][1], 0, 0, 0);
-      }
-      if (j == 3) {
-        // tokens 16 tt + 4 q4 + 0..3 of this lane, scale group g
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + g * kXHalf + 16 * tt + 4 * q4);
+            for (int rb = 0; rb < RBW; ++rb) part[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[tt][rb][e] += sc[e] * part[tt][rb][e];
+          for (int rb = 0; rb < RBW; ++rb)
+            part[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv[rb], part[tt][rb], 0, 0, 0);
+        if (j == 3) {
+          // tokens 16 tt + 4 q4 + 0..3 of this lane, scale group g
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + g * kXHalf + 16 * tt + 4 * q4);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[tt][rb][e] += sc[e] * part[tt][rb][e];
+          }
         }
       }
     }
@@ -329,9 +375,9 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   int* flags = reinterpret_cast<int*>(lds + X::kFlag);
   // Both 16-row blocks are handled side by side without branches, so their
   // dependent VALU chains interleave.
-  float mx[2];
+  float mx[RBW];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     // token tok0 + 16 tt + 4 q4 + i is allowed iff 16 tt + i <= lim
     const int lim = min(L - 1, last_ok[rb]) - tok0 - 4 * q4;
     mx[rb] = kNegInf;
@@ -344,12 +390,12 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
         mx[rb] = fmaxf(mx[rb], v);
       }
   }
-  mx[0] = max4lanes(mx[0]);
-  mx[1] = max4lanes(mx[1]);
-  bool rescaled = false;
-  float alpha[2], m_use[2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) mx[rb] = max4lanes(mx[rb]);
+  bool rescaled = false;
+  float alpha[RBW], m_use[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
     // the running max moves only when it grows by more than the slack; a row's
     // first allowed tokens need no rescale (its O and l are still 0)
     const bool grow = mx[rb] > m_run[rb] + kRescaleSlack;
@@ -360,22 +406,24 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
     m_run[rb] = grow ? mx[rb] : m_run[rb];
     m_use[rb] = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
   }
-  bf16x8 pv[2];
-  float psum[2] = {0.f, 0.f};
+  bf16x8 pv[RBW];
+  float psum[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) psum[rb] = 0.f;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RBW; ++rb) {
         const float e = fast_exp2(s[tt][rb][i] - m_use[rb]);
         psum[rb] += e;
         pv[rb][4 * tt + i] = static_cast<__bf16>(e);
       }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     l_run[rb] += psum[rb];
-    const int row = 32 * wave + 16 * rb + r16;
+    const int row = 16 * RBW * wave + 16 * rb + r16;
     // slot q4 of the row holds tokens 4 q4 .. 4 q4 + 3 and 16 + 4 q4 .. 16 + 4 q4 + 3
     *reinterpret_cast<bf16x8*>(pbuf + xrow_off(row, q4)) = pv[rb];
     if (q4 == 0) alpha_buf[row] = alpha[rb];
@@ -386,7 +434,7 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   // ---- PV phase: O^T[dim 128 w + 16 dd + 4 q4 + i][row 16 rr + r16] += V^T P^T -------------
   if (flags[0] == unit_id || flags[1] == unit_id || flags[2] == unit_id || flags[3] == unit_id) {
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
+    for (int rr = 0; rr < NRR; ++rr) {
       const float a = alpha_buf[16 * rr + r16];
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) acc[dd][rr] *= a;
@@ -396,16 +444,16 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   // the token order of P^T slot q4
   auto vload = [&](int dd) -> bf16x8 {
     const int d = 8 * wave + dd;                  // 16-dim block of V
-    const uint8_t* a0 = page + ln.v_off[d & 3] + 128 * (d >> 2);
+    const uint8_t* a0 = page + ln.v_off[d & 3] + 4096 * (d >> 2);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * 128));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  // bf16: all 8 row blocks of P^T in registers, each V^T operand read once.
-  // FP8: two halves of 4 row blocks (V^T read twice) -- the scale folding
-  // needs the registers.
-  constexpr int kHalves = kFp8 ? 2 : 1;
-  constexpr int kRB = 8 / kHalves;
+  // All row blocks of P^T in registers, each V^T operand read once -- except
+  // FP8 128-row tiles: two halves of 4 row blocks (V^T read twice), as the
+  // scale folding needs the registers.
+  constexpr int kHalves = (kFp8 && RBW == 2) ? 2 : 1;
+  constexpr int kRB = NRR / kHalves;
   f32x4 sa, sb;
   if constexpr (kFp8) {
     // this wave's dims are scale group `wave`: the per-token scales of its
@@ -434,16 +482,18 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
 #pragma unroll
       for (int r = 0; r < kRB; ++r) {
         const int rr = kRB * hv + r;
-        acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd & 1], pb[r], acc[dd][rr], 0, 0, 0);
+        if (RBW == 2 || rr < live_rr)             // 64-row tiles: skip row blocks past the last row
+          acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd & 1], pb[r], acc[dd][rr], 0, 0, 0);
       }
     }
   }
 }
 
-template <int FMT>
+template <int FMT, int RBW>
 __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
-  using X = XLayout<FMT>;
-  constexpr int M_TILE = 128;
+  using X = XLayout<FMT, RBW>;
+  constexpr int M_TILE = X::kRows;
+  constexpr int NRR = 4 * RBW;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[X::kTotal];
 
   XLane ln;
@@ -453,21 +503,21 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   ln.r16 = ln.lane & 15;
   ln.q4 = ln.lane >> 4;
   {
-    const int sw_k = swz(ln.r16);     // = swz(r16 + 16)
-    ln.k_off[0] = ln.r16 * kRowBytes + 16 * (ln.q4 ^ sw_k);
-    ln.k_off[1] = ln.r16 * kRowBytes + 16 * ((4 + ln.q4) ^ sw_k);
+    // K reads: token 16 tt + r16 (the swizzle depends on t % 8 only), chunk
+    // 8 (c / 2) + 4 (c & 1) + q4: lane part for c even / odd, the rest immediate
+    ln.k_off[0] = xk_off(ln.r16, ln.q4);
+    ln.k_off[1] = xk_off(ln.r16, 4 + ln.q4);
     // transposed V reads: lane i of a 16-lane group addresses token 4 q4 + i / 4
     // (+16) and dims 4 (i % 4) .. + 3 of each 16-dim block
     const int tok = 4 * ln.q4 + (ln.r16 >> 2);
-    const int sw_v = swz(tok);        // = swz(tok + 16)
     const int hh = (ln.r16 & 3) >> 1, half8 = ln.r16 & 1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ln.v_off[e] = tok * kRowBytes + 16 * ((2 * e + hh) ^ sw_v) + 8 * half8;
+    for (int e = 0; e < 4; ++e) ln.v_off[e] = xk_off(tok, 2 * e + hh) + 8 * half8;
   }
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   const int st = static_cast<int>(p.kv_st);
 #pragma unroll
-  for (int j = 0; j < X::kLoadsPerWave; ++j) ln.ld_off[j] = x_load_off<FMT>(wave + kWaves * j, ln.lane, st);
+  for (int j = 0; j < (X::kFp8 ? X::kLoadsPerWave : 1); ++j) ln.ld_off[j] = x_load_off<FMT>(wave + kWaves * j, ln.lane, st);
 
   // XCD-aware order: consecutive logical workgroups share an XCD (and its L2)
   const int per_xcd = gridDim.x / 8;
@@ -492,15 +542,19 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   if (tid < 4) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
 
   // S-phase rows of this lane
-  int srow[2], s_idx[2], shead[2];
-  bool srow_ok[2];
+  int srow[RBW], s_idx[RBW], shead[RBW];
+  bool srow_ok[RBW];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    srow[rb] = mt * M_TILE + 32 * wave + 16 * rb + r16;
+  for (int rb = 0; rb < RBW; ++rb) {
+    srow[rb] = mt * M_TILE + 16 * RBW * wave + 16 * rb + r16;
     srow_ok[rb] = srow[rb] < p.rows;
     s_idx[rb] = srow_ok[rb] ? srow[rb] / p.group : 0;
     shead[rb] = kvh * p.group + (srow_ok[rb] ? srow[rb] % p.group : 0);
   }
+
+  // row blocks with at least one row (uniform): the rest of the tile is padding
+  const bool wave_live = mt * M_TILE + 16 * RBW * wave < p.rows;
+  const int live_rr = min(NRR, (p.rows - mt * M_TILE + 15) / 16);
 
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
   // Block-table window: lane i holds entry win_pi + i of sequence win_b's row
@@ -550,15 +604,15 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = ld_meta(p.num_splits + b);
     const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
-    int last_ok[2];
+    int last_ok[RBW];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) last_ok[rb] = p.causal ? (L - p.s_q + s_idx[rb]) : (L - 1);
+    for (int rb = 0; rb < RBW; ++rb) last_ok[rb] = p.causal ? (L - p.s_q + s_idx[rb]) : (L - 1);
 
     // Q^T of this sequence: chunks 3..15 of the lane's rows in VGPRs, chunks
     // 0, 1, 2, 16, 17 of all 128 rows in LDS
-    bf16x8 qf[X::kRegChunks][2];
+    bf16x8 qf[X::kRegChunks][RBW];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
       const uint16_t* qrow = p.q + b * p.q_sb + s_idx[rb] * p.q_ss + shead[rb] * p.q_sh;
 #pragma unroll
       for (int c = 0; c < 18; ++c) {
@@ -591,7 +645,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
             const int sg = grow / p.group, hg = kvh * p.group + grow % p.group;
             off = static_cast<uint32_t>(2 * (sg * p.q_ss + hg * p.q_sh + 32 * X::qchunk(qs) + 8 * sl));
           }
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, LDS_PTR(void, lds + X::kQ + qs * kXQChunkBytes + 1024 * i),
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, LDS_PTR(void, lds + X::kQ + qs * X::kQChunkBytes + 1024 * i),
                                                    16, off, 0, 0, 0);
         }
       }
@@ -599,12 +653,17 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     wait_vm_all();
     lds_barrier();
 
-    float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-    f32x4 acc[8][8];                          // [16-dim block][16-row block]
+    float m_run[RBW], l_run[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      m_run[rb] = kNegInf;
+      l_run[rb] = 0.f;
+    }
+    f32x4 acc[8][NRR];                        // [16-dim block][16-row block]
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd)
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < NRR; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool bad = false;
 
     while (uq[0].b == b) {
@@ -612,10 +671,10 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
       const bool this_ok = okq[0];
       bad |= !this_ok;
       // loads still allowed in flight: those of the units after u
-      bool later_issued = false;
+      int later = 0;
 #pragma unroll
-      for (int i = 1; i < kAhead; ++i) later_issued |= uq[i].b <= r.end_b && okq[i];
-      if (later_issued) wait_vm_one_unit<FMT>(wave); else wait_vm_all();
+      for (int i = 1; i < kAhead; ++i) later += (uq[i].b <= r.end_b && okq[i]) ? 1 : 0;
+      wait_units<FMT>(later, wave);
       lds_barrier_keep_loads();               // every wave's loads of u landed; unit u - 1 is done everywhere
       const XUnit last = uq[kAhead - 1];
       const XUnit un = (last.b <= r.end_b) ? x_next(p, r, last) : last;
@@ -628,8 +687,9 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
       const int tok0 = u.pi * kPage + u.hf * kXHalf;
       const int valid = min(L - tok0, kXHalf);
       const int slot_n = (slot + kAhead) % X::kSlots;   // held unit u - 1, free now
-      x_step<FMT>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + slot_n * X::kSlot, lds + X::kConv, src_n, st,
-                  ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run);
+      x_step<FMT, RBW>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + slot_n * X::kSlot, lds + X::kConv, src_n, st,
+                  ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run, wave_live,
+                  live_rr);
       ++unit_id;
       slot = (slot + 1) % X::kSlots;
 #pragma unroll
@@ -643,11 +703,11 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
 
     // ---- epilogue: l of every row through LDS; each wave writes its 128 dims ----
     lds_barrier_keep_loads();                 // the P^T buffer is free
-    float* lrow = reinterpret_cast<float*>(lds + X::kP);   // [128] l
+    float* lrow = reinterpret_cast<float*>(lds + X::kP);   // [rows] l
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
       const float l_tot = sum4lanes(l_run[rb]);
-      if (q4 == 0) lrow[32 * wave + 16 * rb + r16] = l_tot;
+      if (q4 == 0) lrow[16 * RBW * wave + 16 * rb + r16] = l_tot;
       if (q4 == 0 && srow_ok[rb]) {
         float lse = (l_tot > 0.f) ? (m_run[rb] + __log2f(l_tot)) * kLn2 : kNegInf;
         if (bad) lse = __builtin_nanf("");
@@ -661,7 +721,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     // lane l holds, per (dd, rr), row 16 rr + r16 and dims 128 w + 16 dd + 4 q4 + 0..3
     const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
+    for (int rr = 0; rr < NRR; ++rr) {
       const int row = mt * M_TILE + 16 * rr + r16;
       if (row >= p.rows) continue;
       const float l_row = lrow[16 * rr + r16];
@@ -700,12 +760,20 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_split_x(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
-                          hipEvent_t ev_stop) {
-  if (kv_format == kFmtFp8)
-    hipExtLaunchKernelGGL(splitkv_x_kernel<kFmtFp8>, dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
-  else
-    hipExtLaunchKernelGGL(splitkv_x_kernel<kFmtBf16>, dim3(grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
+hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wave, int grid, hipStream_t stream,
+                          hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const dim3 g(grid), blk(kThreads);
+  if (rows_per_wave == 32) {
+    if (kv_format == kFmtFp8)
+      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8, 2>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtBf16, 2>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  } else {
+    if (kv_format == kFmtFp8)
+      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8, 1>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtBf16, 1>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  }
   return hipGetLastError();
 }
 
