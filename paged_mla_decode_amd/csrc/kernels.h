@@ -34,8 +34,9 @@ struct DecodeParams {
   int grid_wgs;               // real workgroups of the split kernel (the grid is padded to a multiple of 8)
 };
 
-// The row-tile split kernel (mla_kernels_x.hip): 4 waves, rows_per_wave = 32
-// (128-row tiles) or 16 (64-row tiles); grid padded to a multiple of 8.
+// The row-tile split kernel (mla_kernels_x.hip): 128-row tiles, 8 waves of
+// 16 rows each in the S phase (rows_per_wave must be 32: the 4-wave row count
+// the plan records for a 128-row tile); grid padded to a multiple of 8.
 // ev_start / ev_stop (may be null) take the kernel's start and end timestamps.
 hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wave, int grid, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop);

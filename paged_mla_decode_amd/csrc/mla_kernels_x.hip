@@ -1,11 +1,11 @@
 // mla_kernels_x.hip -- split-KV MLA decode kernel for more than 64 query rows
-// per KV head on gfx950 (MI355X): 128-row tiles.
+// per KV head on gfx950 (MI355X): 128-row tiles, 8 wavefronts.
 //
 // Same computation as the 64-row kernel in mla_kernels.hip (softmax attention
 // of query rows over a sequence's cached latent rows, V = their first 512
 // dims; pieces of a sequence leave partial O / LSE for the combine kernel:
 // wmrh.cn FlashMLA深度解析, "计算流水线设计"), organised so that V is read from
-// LDS once per workgroup instead of once per wave.
+// LDS once per workgroup and two wavefronts share each SIMD.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -19,79 +19,71 @@ namespace {
 
 using namespace dev;
 
-
 // ----------------------------------------------------------------------------
 // 128-row tiles (more than 64 rows per KV head)
 //
-// Each workgroup covers 128 query rows. Work advances in units of 32 tokens
-// (half a page) through a three-slot LDS ring, so two units are in flight
-// while one is computed, and LDS keeps room for the exchange buffers:
-//   S phase  -- wave w owns rows 32w .. 32w + 31 as two 16-row blocks that
-//               share every K operand read: S^T = K Q^T on MFMA 16x16x32 bf16
-//               (A = 16 tokens x 32 dims of K from LDS, B = Q^T); 13 of the
-//               18 32-dim Q chunks stay in VGPRs, 5 in LDS (O alone takes 256
-//               of the 512 registers a lane has).
+// Each workgroup covers 128 query rows with 8 wavefronts, two per SIMD, so
+// one wave's LDS waits, softmax and barrier waits overlap the other's MFMA
+// work. Work advances in units of 32 tokens (half a page) through a two-slot
+// LDS ring (the unit after the current one is in flight):
+//   S phase  -- wave w owns rows 16w .. 16w + 15: S^T = K Q^T on MFMA
+//               16x16x32 bf16 (A = 16 tokens x 32 dims of K from LDS,
+//               B = Q^T); 9 of the 18 32-dim Q chunks stay in VGPRs, 9 in LDS.
 //   exchange -- each wave writes bf16 P^T of its rows, its rescale factors
 //               and a flag; one barrier.
-//   PV phase -- wave w accumulates O^T for value dims 128w .. 128w + 127 of
-//               all 128 rows: it reads only its quarter of V (transposed) and
-//               every wave's P^T.
-// Per page this reads K four times (288 KB) but V once (64 KB), against four
-// times each when every wave owns whole rows.
+//   PV phase -- wave w accumulates O^T for value dims 64w .. 64w + 63 of all
+//               128 rows (128 accumulator registers): it reads only its
+//               eighth of V (transposed) and every wave's P^T.
 // FP8 pages (656-byte records) stream raw into the ring; one LDS pass per
 // unit turns the e4m3 codes into bf16 exactly (4 significant bits fit in 8)
 // and copies RoPE and the 4 per-128-dim scales. The S phase applies the fp32
-// scales to the per-group partial logits; in the PV phase wave w's dims are
-// exactly scale group w, so it multiplies its P^T operand by that group's
+// scales to the per-group partial logits; in the PV phase wave w's dims lie
+// in scale group w / 2, so it multiplies its P^T operand by that group's
 // per-token scales and V enters the MFMA as the exact codes.
 // ----------------------------------------------------------------------------
 
+constexpr int kWW = 8;                                      // wavefronts per workgroup
+constexpr int kWThreads = 64 * kWW;
+constexpr int kLoadWaves = 4;                               // waves that issue the unit loads
 constexpr int kXHalf = 32;                                  // tokens per unit
 constexpr int kXHalfBytes = kXHalf * kRowBytes;             // 36864 = 36 x 1 KB: bf16 rows
 constexpr int kXRawBytes = kXHalf * kFp8Record;             // 20992: FP8 records
 
-// LDS layout (bytes) for a tile of 64 RBW rows (RBW = 16-row blocks per wave
-// in the S phase: 2 for 128-row tiles, 1 for 64-row tiles): the ring of
-// 32-token units (bf16 rows, or raw FP8 records); FP8 only: the converted unit
-// (bf16 rows, the bf16 ring layout) and the scales [4 groups][32 tokens]; then
-// P^T, rescale factors, flags, and the Q^T chunks kept in LDS for all rows
-// (128-row tiles only: bf16 {0, 1, 2, 16, 17}, FP8 {0 .. 6, 16, 17}; the other
-// chunks of each row stay in VGPRs). Ring depth: 128-row bf16 3 slots (two
-// units ahead), 128-row FP8 2 slots (one ahead), 64-row 4 slots (three ahead).
-template <int FMT, int RBW>
+// LDS layout (bytes): the ring of 32-token units (bf16 rows, or raw FP8
+// records); FP8 only: the converted unit (bf16 rows, the bf16 ring layout)
+// and the scales [4 groups][32 tokens]; then P^T, rescale factors, flags, and
+// the Q^T chunks kept in LDS for all 128 rows (chunks 0 .. 6, 16, 17; the
+// other chunks of each row stay in VGPRs).
+template <int FMT>
 struct XLayout {
   static constexpr bool kFp8 = (FMT == kFmtFp8);
-  static constexpr int kRows = 64 * RBW;                    // rows per tile
+  static constexpr int kRows = 128;                         // rows per tile
   static constexpr int kSlot = kFp8 ? 21 * 1024 : kXHalfBytes;
-  static constexpr int kSlots = RBW == 1 ? 4 : (kFp8 ? 2 : 3);
-  static constexpr int kAhead = kSlots - 1;                 // units in flight beyond the current one
+  static constexpr int kSlots = 2;
   static constexpr int kRing = 0;
   static constexpr int kConv = kRing + kSlots * kSlot;
   static constexpr int kScale = kConv + (kFp8 ? kXHalfBytes : 0);
   static constexpr int kP = kScale + (kFp8 ? 4 * kXHalf * 4 : 0);
   static constexpr int kAlpha = kP + kRows * kXHalf * 2;    // P^T: [rows][32 tokens] bf16
   static constexpr int kFlag = kAlpha + kRows * 4;          // alpha: [rows] fp32
-  static constexpr int kQ = kFlag + 64;                     // flags: [4] int32
-  static constexpr int kQChunks = RBW == 1 ? 0 : (kFp8 ? 9 : 5);
+  static constexpr int kQ = kFlag + 64;                     // flags: [8] int32
+  static constexpr int kQChunks = 9;
   static constexpr int kQChunkBytes = kRows * 64;           // one 32-dim Q^T chunk of all rows
   static constexpr int kTotal = kQ + kQChunks * kQChunkBytes;
   static constexpr int kLoads = kFp8 ? 21 : kXHalfBytes / 1024;   // 1 KB direct loads per unit (36 / 21)
-  static constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;   // 9 / 6
-  static constexpr int kLow = RBW == 1 ? 0 : (kFp8 ? 7 : 3);     // chunks 0 .. kLow-1 in LDS
+  static constexpr int kLoadsPerWave = (kLoads + kLoadWaves - 1) / kLoadWaves;   // 9 / 6
+  static constexpr int kLow = 7;                            // chunks 0 .. 6 in LDS, then 16, 17
   // LDS slot of Q^T chunk c, or -1 when it lives in VGPRs
-  static constexpr int qslot(int c) {
-    return kQChunks == 0 ? -1 : (c < kLow ? c : (c == 16 ? kLow : (c == 17 ? kLow + 1 : -1)));
-  }
+  static constexpr int qslot(int c) { return c < kLow ? c : (c >= 16 ? c - 16 + kLow : -1); }
   static constexpr int kRegChunks = 18 - kQChunks;
   // register index of chunk c
-  static constexpr int qreg(int c) { return kQChunks == 0 ? c : c - kLow; }
+  static constexpr int qreg(int c) { return c - kLow; }
   // LDS chunk index qs -> Q chunk
   static constexpr int qchunk(int qs) { return qs < kLow ? qs : 16 - kLow + qs; }
 };
-static_assert(XLayout<kFmtBf16, 2>::kTotal <= 163840 && XLayout<kFmtFp8, 2>::kTotal <= 163840, "LDS budget");
-static_assert(XLayout<kFmtBf16, 1>::kTotal <= 163840 && XLayout<kFmtFp8, 1>::kTotal <= 163840, "LDS budget");
-static_assert(XLayout<kFmtBf16, 2>::kLoads % kWaves == 0, "equal direct-load counts per wave (bf16)");
-static_assert(XLayout<kFmtFp8, 2>::kSlot >= kXRawBytes, "FP8 slot holds a unit");
+static_assert(XLayout<kFmtBf16>::kTotal <= 163840 && XLayout<kFmtFp8>::kTotal <= 163840, "LDS budget");
+static_assert(XLayout<kFmtBf16>::kLoads % kLoadWaves == 0, "equal direct-load counts per wave (bf16)");
+static_assert(XLayout<kFmtFp8>::kSlot >= kXRawBytes, "FP8 slot holds a unit");
 
 // Q^T chunks and P^T rows in LDS: 64 bytes per row (4 x 16 B); the 16-byte
 // slot is XOR-swizzled with (row >> 1) & 3 so 8 consecutive rows hit 8
@@ -156,21 +148,22 @@ __device__ __forceinline__ uint32_t x_load_off(int k, int lane, int st) {
 constexpr int kRawBufferWord3 = 0x00020000;
 
 // Issue the direct loads of one unit (32 tokens starting at `src`, token stride
-// `st`) into `dst`: MUBUF loads to LDS (buffer_load_dwordx4 ... lds), 16 bytes
-// per lane, with the unit as the buffer (offsets past its 32 rows read zeros).
-// The buffer form keeps the LDS read waits of the compute phases partial
-// (the FLAT form makes every LDS wait a full drain while a load is in flight).
+// `st`) into `dst` (waves 0 .. 3 issue them): MUBUF loads to LDS
+// (buffer_load_dwordx4 ... lds), 16 bytes per lane, with the unit as the
+// buffer (offsets past its 32 rows read zeros). The buffer form keeps the LDS
+// read waits of the compute phases partial (the FLAT form makes every LDS
+// wait a full drain while a load is in flight).
 // bf16: load k = 4 g + w (wave w issues the loads of token block w) brings
 // tokens 8 w .. 8 w + 7 of column block g; FP8: load k brings LDS bytes
 // 1024 k .. + 1023 of the 32 records.
 template <int FMT>
-__device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, const uint32_t (&off)[9], int st) {
-  using X = XLayout<FMT, 2>;
+__device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, const uint32_t (&off)[6], int st) {
+  using X = XLayout<FMT>;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, kXHalf * st, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < X::kLoadsPerWave; ++j) {
-    const int k = wave + kWaves * j;
+    const int k = wave + kLoadWaves * j;
     if constexpr (FMT == kFmtFp8) {
       if (k < X::kLoads)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
@@ -181,34 +174,6 @@ __device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wa
   }
 }
 
-// s_waitcnt vmcnt(N) (vmcnt: bits 3:0 and 15:14; expcnt 6:4 = 7 and lgkmcnt
-// 11:8 = 15 mean no wait).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Wait until at most `later` units' direct loads of this wave are in flight
-// (later = 0, 1 or 2): the wave's loads per unit are 9 (bf16), or 6 for wave 0
-// and 5 for the others (FP8).
-template <int FMT>
-__device__ __forceinline__ void wait_units(int later, int wave) {
-  if (later <= 0) {
-    wait_vmcnt<0>();
-  } else if constexpr (FMT == kFmtFp8) {
-    if (wave == 0) {
-      if (later == 1) wait_vmcnt<6>(); else wait_vmcnt<12>();
-    } else {
-      if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<10>();
-    }
-  } else {
-    if (later == 1) wait_vmcnt<9>(); else wait_vmcnt<18>();
-  }
-}
-static_assert(XLayout<kFmtBf16, 2>::kLoadsPerWave == 9 && XLayout<kFmtFp8, 2>::kLoadsPerWave == 6,
-              "wait counts and load offsets per lane");
-
 // Lane-constant indices. MFMA 16x16x32: lane l supplies A[i = l % 16][k-slots
 // 8 (l / 16) .. + 7] and B[the same k-slots][j = l % 16]; D register i of lane
 // l is D[4 (l / 16) + i][l % 16].
@@ -217,31 +182,28 @@ struct XLane {
   int r16, q4;          // lane % 16, lane / 16
   int k_off[2];         // S phase: K row r16, logical chunks q4 and 4 + q4 (swizzled), bytes
   int v_off[4];         // PV phase: transposed V read offsets, by 16-dim block d & 3
-  uint32_t ld_off[9];   // direct loads: per-lane source offsets (bf16 uses [0] only)
+  uint32_t ld_off[6];   // direct loads: per-lane source offsets (bf16 uses [0] only)
 };
 
 // One unit of the pipeline. `cur` holds the unit (32 bf16 rows, or 32 FP8
-// records), `nxt` receives the unit two ahead, `work` is the LDS after the
-// ring (FP8 conversion buffers, P^T, rescale factors, flags, Q^T chunks). The
+// records), `nxt` receives the next unit, `work` is the LDS after the ring
+// (FP8 conversion buffers, P^T, rescale factors, flags, Q^T chunks). The
 // regions are disjoint; the restrict qualifiers let the compiler see that the
 // LDS reads of this unit never touch the direct loads in flight into `nxt`.
-template <int FMT, int RBW>
+template <int FMT>
 __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
                                        uint8_t* __restrict__ work, const uint8_t* next_src, int st, const XLane& ln,
-                                       int L, const int (&last_ok)[RBW], int tok0, int valid, bool this_ok,
-                                       float scale_log2, int unit_id,
-                                       const bf16x8 (&qf)[XLayout<FMT, RBW>::kRegChunks][RBW],
-                                       f32x4 (&acc)[8][4 * RBW], float (&m_run)[RBW], float (&l_run)[RBW],
-                                       bool wave_live, int live_rr) {
-  using X = XLayout<FMT, RBW>;
-  constexpr int NRR = 4 * RBW;                    // 16-row blocks per tile
+                                       int L, int last_ok, int tok0, int valid, bool this_ok, float scale_log2,
+                                       int unit_id, const bf16x8 (&qf)[XLayout<FMT>::kRegChunks], f32x4 (&acc)[4][8],
+                                       float& m_run, float& l_run, bool wave_live, int live_rr) {
+  using X = XLayout<FMT>;
   constexpr bool kFp8 = X::kFp8;
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   uint8_t* const lds = work - X::kConv;
   const float* sct = reinterpret_cast<const float*>(lds + X::kScale);   // FP8: [group][token] scales
 
   // ---- stage the unit: FP8 conversion, or zero the bf16 rows past the end --------------
-  uint8_t* page;                                  // bf16 rows (1152 B, swizzled chunks)
+  uint8_t* page;                                  // bf16 rows (chunk-group-major, swizzled)
   if constexpr (kFp8) {
     uint8_t* conv = lds + X::kConv;
     float* scw = reinterpret_cast<float*>(lds + X::kScale);
@@ -250,8 +212,8 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
       scw[tid] = (this_ok && t < valid) ? *reinterpret_cast<const float*>(cur + t * kFp8Record + 512 + 4 * g) : 0.f;
     }
 #pragma unroll 1
-    for (int j = 0; j < 4; ++j) {
-      const int item = tid + kThreads * j;          // 32 tokens x 32 chunks of 16 codes
+    for (int j = 0; j < 2; ++j) {
+      const int item = tid + kWThreads * j;         // 32 tokens x 32 chunks of 16 codes
       const int t = item >> 5, ch = item & 31;
       const u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 16 * ch);
       u32x4 lo, hi;
@@ -274,7 +236,7 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
       *reinterpret_cast<u32x4*>(conv + xk_off(t, 2 * ch)) = lo;
       *reinterpret_cast<u32x4*>(conv + xk_off(t, 2 * ch + 1)) = hi;
     }
-    {
+    if (tid < 8 * kXHalf) {
       const int t = tid >> 3, rr = tid & 7;         // 32 tokens x 8 RoPE chunks
       u32x4 w = *reinterpret_cast<const u32x4*>(cur + t * kFp8Record + 528 + 16 * rr);
       if (!(this_ok && t < valid)) w = u32x4{0u, 0u, 0u, 0u};
@@ -285,7 +247,7 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   } else {
     if (valid < kXHalf || !this_ok) {
       const int z0 = this_ok ? valid : 0;
-      for (int idx = tid; idx < 72 * kXHalf; idx += kThreads) {   // 16-byte chunks of the unit
+      for (int idx = tid; idx < 72 * kXHalf; idx += kWThreads) {  // 16-byte chunks of the unit
         const int t = (idx >> 3) & 31;                            // block idx / 256, token, chunk idx % 8
         if (t >= z0) *reinterpret_cast<u32x4*>(cur + 4096 * (idx >> 8) + 128 * t + 16 * (idx & 7)) = u32x4{0u, 0u, 0u, 0u};
       }
@@ -294,35 +256,31 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
     page = cur;
   }
 
-  // ---- the unit two ahead -> nxt ----------------------------------------------------
-  if (next_src != nullptr) x_issue<FMT>(next_src, nxt, wave, ln.ld_off, st);
+  // ---- the next unit -> nxt (waves 0 .. 3) ------------------------------------------------
+  if (next_src != nullptr && wave < kLoadWaves) x_issue<FMT>(next_src, nxt, wave, ln.ld_off, st);
 
-  // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 16 RBW w + 16 rb + r16] ----------------
+  // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 16 w + r16] --------------------------------
   const uint8_t* qlds = lds + X::kQ;
-  auto qop = [&](int c, int rb) -> bf16x8 {
+  auto qop = [&](int c) -> bf16x8 {
     const int qs = X::qslot(c);
     if (qs >= 0)
-      return *reinterpret_cast<const bf16x8*>(qlds + qs * X::kQChunkBytes +
-                                              xrow_off(16 * RBW * wave + 16 * rb + r16, q4));
-    return qf[X::qreg(c)][rb];
+      return *reinterpret_cast<const bf16x8*>(qlds + qs * X::kQChunkBytes + xrow_off(16 * wave + r16, q4));
+    return qf[X::qreg(c)];
   };
   // K: token 16 tt + r16, dims 32 c + 8 q4 .. + 7 = logical chunk 8 (c / 2) + 4 (c & 1) + q4
   auto kload = [&](int c, int tt) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(page + ln.k_off[c & 1] + 16 * tt * 128 + 4096 * (c >> 1));
   };
-  f32x4 s[2][RBW];                                // [token tile][row block]
+  f32x4 s[2];                                     // [token tile]
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) s[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < 2; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // chunk order: bf16 0..17; FP8 the RoPE chunks 16, 17 first (unscaled), then
   // the 4 latent groups of 4 chunks, each group's partial logits scaled and added
   auto corder = [](int i) { return kFp8 ? (i < 2 ? 16 + i : i - 2) : i; };
-  // (64-row tiles: a wave whose rows all lie past the last row skips the S
-  // phase; its S stays 0)
-  if (RBW == 2 || wave_live) {
+  // (a wave whose rows all lie past the last row skips the S phase; its S stays 0)
+  if (wave_live) {
     bf16x8 kbuf[2][2];
-    f32x4 part[2][RBW];
+    f32x4 part[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(corder(0), tt);
 #pragma unroll
@@ -332,168 +290,133 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) kbuf[(i + 1) & 1][tt] = kload(corder(i + 1), tt);
       }
-      bf16x8 qv[RBW];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) qv[rb] = qop(c, rb);
+      const bf16x8 qv = qop(c);
       if (!kFp8 || i < 2) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb)
-            s[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv[rb], s[tt][rb], 0, 0, 0);
+        for (int tt = 0; tt < 2; ++tt) s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv, s[tt], 0, 0, 0);
       } else {
         const int g = (i - 2) >> 2, j = (i - 2) & 3;
         if (j == 0) {
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) part[tt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int tt = 0; tt < 2; ++tt) part[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb)
-            part[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv[rb], part[tt][rb], 0, 0, 0);
+          part[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv, part[tt], 0, 0, 0);
         if (j == 3) {
           // tokens 16 tt + 4 q4 + 0..3 of this lane, scale group g
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + g * kXHalf + 16 * tt + 4 * q4);
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) s[tt][rb][e] += sc[e] * part[tt][rb][e];
+            for (int e = 0; e < 4; ++e) s[tt][e] += sc[e] * part[tt][e];
           }
         }
       }
     }
   }
 
-  // ---- softmax of this wave's rows; P^T, rescale factors and a flag -> LDS ---------------
+  // ---- softmax of this wave's rows; P^T, rescale factor and a flag -> LDS -----------------
   uint8_t* pbuf = lds + X::kP;
   float* alpha_buf = reinterpret_cast<float*>(lds + X::kAlpha);
   int* flags = reinterpret_cast<int*>(lds + X::kFlag);
-  // Both 16-row blocks are handled side by side without branches, so their
-  // dependent VALU chains interleave.
-  float mx[RBW];
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    // token tok0 + 16 tt + 4 q4 + i is allowed iff 16 tt + i <= lim
-    const int lim = min(L - 1, last_ok[rb]) - tok0 - 4 * q4;
-    mx[rb] = kNegInf;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = (16 * tt + i <= lim) ? s[tt][rb][i] * scale_log2 : kNegInf;
-        s[tt][rb][i] = v;
-        mx[rb] = fmaxf(mx[rb], v);
-      }
-  }
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) mx[rb] = max4lanes(mx[rb]);
-  bool rescaled = false;
-  float alpha[RBW], m_use[RBW];
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    // the running max moves only when it grows by more than the slack; a row's
-    // first allowed tokens need no rescale (its O and l are still 0)
-    const bool grow = mx[rb] > m_run[rb] + kRescaleSlack;
-    const bool had = m_run[rb] != kNegInf;
-    alpha[rb] = (grow && had) ? fast_exp2(m_run[rb] - mx[rb]) : 1.f;
-    rescaled |= grow && had;
-    l_run[rb] *= alpha[rb];
-    m_run[rb] = grow ? mx[rb] : m_run[rb];
-    m_use[rb] = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-  }
-  bf16x8 pv[RBW];
-  float psum[RBW];
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) psum[rb] = 0.f;
+  // token tok0 + 16 tt + 4 q4 + i is allowed iff 16 tt + i <= lim
+  const int lim = min(L - 1, last_ok) - tok0 - 4 * q4;
+  float mx = kNegInf;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const float v = (16 * tt + i <= lim) ? s[tt][i] * scale_log2 : kNegInf;
+      s[tt][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max4lanes(mx);
+  // the running max moves only when it grows by more than the slack; a row's
+  // first allowed tokens need no rescale (its O and l are still 0)
+  const bool grow = mx > m_run + kRescaleSlack;
+  const bool had = m_run != kNegInf;
+  const float alpha = (grow && had) ? fast_exp2(m_run - mx) : 1.f;
+  const bool rescaled = grow && had;
+  l_run *= alpha;
+  m_run = grow ? mx : m_run;
+  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+  bf16x8 pv;
+  float psum = 0.f;
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-        const float e = fast_exp2(s[tt][rb][i] - m_use[rb]);
-        psum[rb] += e;
-        pv[rb][4 * tt + i] = static_cast<__bf16>(e);
-      }
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    l_run[rb] += psum[rb];
-    const int row = 16 * RBW * wave + 16 * rb + r16;
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(s[tt][i] - m_use);
+      psum += e;
+      pv[4 * tt + i] = static_cast<__bf16>(e);
+    }
+  l_run += psum;
+  {
+    const int row = 16 * wave + r16;
     // slot q4 of the row holds tokens 4 q4 .. 4 q4 + 3 and 16 + 4 q4 .. 16 + 4 q4 + 3
-    *reinterpret_cast<bf16x8*>(pbuf + xrow_off(row, q4)) = pv[rb];
-    if (q4 == 0) alpha_buf[row] = alpha[rb];
+    *reinterpret_cast<bf16x8*>(pbuf + xrow_off(row, q4)) = pv;
+    if (q4 == 0) alpha_buf[row] = alpha;
   }
   if (ln.lane == 0 && __builtin_amdgcn_ballot_w64(rescaled) != 0) flags[wave] = unit_id;
   lds_barrier_keep_loads();
 
-  // ---- PV phase: O^T[dim 128 w + 16 dd + 4 q4 + i][row 16 rr + r16] += V^T P^T -------------
-  if (flags[0] == unit_id || flags[1] == unit_id || flags[2] == unit_id || flags[3] == unit_id) {
+  // ---- PV phase: O^T[dim 64 w + 16 dd + 4 q4 + i][row 16 rr + r16] += V^T P^T -------------
+  {
+    bool any = false;
 #pragma unroll
-    for (int rr = 0; rr < NRR; ++rr) {
-      const float a = alpha_buf[16 * rr + r16];
+    for (int w = 0; w < kWW; ++w) any |= flags[w] == unit_id;
+    if (any) {
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) acc[dd][rr] *= a;
+      for (int rr = 0; rr < 8; ++rr) {
+        const float a = alpha_buf[16 * rr + r16];
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) acc[dd][rr] *= a;
+      }
     }
   }
   // transposed V reads: k-slots 0..3 = tokens 4 q4 + 0..3, 4..7 = the same + 16,
-  // the token order of P^T slot q4
-  auto vload = [&](int dd) -> bf16x8 {
-    const int d = 8 * wave + dd;                  // 16-dim block of V
-    const uint8_t* a0 = page + ln.v_off[d & 3] + 4096 * (d >> 2);
+  // the token order of P^T slot q4; 16-dim block d = 4 w + dd
+  bf16x8 va[4];
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd) {
+    const uint8_t* a0 = page + ln.v_off[dd] + 4096 * wave;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * 128));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  // All row blocks of P^T in registers, each V^T operand read once -- except
-  // FP8 128-row tiles: two halves of 4 row blocks (V^T read twice), as the
-  // scale folding needs the registers.
-  constexpr int kHalves = (kFp8 && RBW == 2) ? 2 : 1;
-  constexpr int kRB = NRR / kHalves;
+    va[dd] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   f32x4 sa, sb;
   if constexpr (kFp8) {
-    // this wave's dims are scale group `wave`: the per-token scales of its
+    // this wave's dims are scale group w / 2: the per-token scales of its
     // k-slot tokens (4 q4 + 0..3, 16 + 4 q4 + 0..3) are folded into P^T
-    sa = *reinterpret_cast<const f32x4*>(sct + wave * kXHalf + 4 * q4);
-    sb = *reinterpret_cast<const f32x4*>(sct + wave * kXHalf + 16 + 4 * q4);
+    sa = *reinterpret_cast<const f32x4*>(sct + (wave >> 1) * kXHalf + 4 * q4);
+    sb = *reinterpret_cast<const f32x4*>(sct + (wave >> 1) * kXHalf + 16 + 4 * q4);
   }
-#pragma unroll
-  for (int hv = 0; hv < kHalves; ++hv) {
-    bf16x8 pb[kRB];
-#pragma unroll
-    for (int r = 0; r < kRB; ++r)
-      pb[r] = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(16 * (kRB * hv + r) + r16, q4));
+  auto pload = [&](int rr) -> bf16x8 {
+    bf16x8 pb = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(16 * rr + r16, q4));
     if constexpr (kFp8) {
 #pragma unroll
-      for (int r = 0; r < kRB; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[r][e] = static_cast<__bf16>(static_cast<float>(pb[r][e]) * (e < 4 ? sa[e] : sb[e - 4]));
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(static_cast<float>(pb[e]) * (e < 4 ? sa[e] : sb[e - 4]));
     }
-    bf16x8 va[2];
-    va[0] = vload(0);
+    return pb;
+  };
+  bf16x8 pb[2];
+  pb[0] = pload(0);
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      if (dd + 1 < 8) va[(dd + 1) & 1] = vload(dd + 1);
+  for (int rr = 0; rr < 8; ++rr) {
+    if (rr + 1 < 8) pb[(rr + 1) & 1] = pload(rr + 1);
+    if (rr < live_rr) {                           // skip row blocks past the last row
 #pragma unroll
-      for (int r = 0; r < kRB; ++r) {
-        const int rr = kRB * hv + r;
-        if (RBW == 2 || rr < live_rr)             // 64-row tiles: skip row blocks past the last row
-          acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd & 1], pb[r], acc[dd][rr], 0, 0, 0);
-      }
+      for (int dd = 0; dd < 4; ++dd)
+        acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd], pb[rr & 1], acc[dd][rr], 0, 0, 0);
     }
   }
 }
 
-template <int FMT, int RBW>
-__global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
-  using X = XLayout<FMT, RBW>;
+template <int FMT>
+__global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
+  using X = XLayout<FMT>;
   constexpr int M_TILE = X::kRows;
-  constexpr int NRR = 4 * RBW;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[X::kTotal];
 
   XLane ln;
@@ -517,7 +440,8 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   const int st = static_cast<int>(p.kv_st);
 #pragma unroll
-  for (int j = 0; j < (X::kFp8 ? X::kLoadsPerWave : 1); ++j) ln.ld_off[j] = x_load_off<FMT>(wave + kWaves * j, ln.lane, st);
+  for (int j = 0; j < (X::kFp8 ? X::kLoadsPerWave : 1); ++j)
+    ln.ld_off[j] = x_load_off<FMT>((wave & (kLoadWaves - 1)) + kLoadWaves * j, ln.lane, st);
 
   // XCD-aware order: consecutive logical workgroups share an XCD (and its L2)
   const int per_xcd = gridDim.x / 8;
@@ -539,22 +463,17 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
   }
   if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
 
-  if (tid < 4) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
+  if (tid < kWW) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
 
-  // S-phase rows of this lane
-  int srow[RBW], s_idx[RBW], shead[RBW];
-  bool srow_ok[RBW];
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    srow[rb] = mt * M_TILE + 16 * RBW * wave + 16 * rb + r16;
-    srow_ok[rb] = srow[rb] < p.rows;
-    s_idx[rb] = srow_ok[rb] ? srow[rb] / p.group : 0;
-    shead[rb] = kvh * p.group + (srow_ok[rb] ? srow[rb] % p.group : 0);
-  }
+  // S-phase row of this lane
+  const int srow = mt * M_TILE + 16 * wave + r16;
+  const bool srow_ok = srow < p.rows;
+  const int s_idx = srow_ok ? srow / p.group : 0;
+  const int shead = kvh * p.group + (srow_ok ? srow % p.group : 0);
 
-  // row blocks with at least one row (uniform): the rest of the tile is padding
-  const bool wave_live = mt * M_TILE + 16 * RBW * wave < p.rows;
-  const int live_rr = min(NRR, (p.rows - mt * M_TILE + 15) / 16);
+  // waves / row blocks with at least one row (uniform): the rest of the tile is padding
+  const bool wave_live = mt * M_TILE + 16 * wave < p.rows;
+  const int live_rr = min(8, (p.rows - mt * M_TILE + 15) / 16);
 
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
   // Block-table window: lane i holds entry win_pi + i of sequence win_b's row
@@ -575,25 +494,15 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     return kv_head + static_cast<int64_t>(pg) * p.kv_sp + static_cast<int64_t>(u.hf) * kXHalf * st;
   };
 
-  // ---- prime the ring -------------------------------------------------------------------
-  // uq[0] is in flight into `slot` (the next unit to compute), uq[i] into the
-  // i-th slot after it; okq = its page is valid (a unit is issued iff it is
-  // inside the range and ok).
-  constexpr int kAhead = X::kAhead;
-  XUnit uq[kAhead];
-  bool okq[kAhead];
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) {
-    if (i == 0)
-      uq[0] = x_seek(p, r, r.begin_b);
-    else
-      uq[i] = (uq[i - 1].b <= r.end_b) ? x_next(p, r, uq[i - 1]) : uq[i - 1];
-    okq[i] = true;
-    if (uq[i].b <= r.end_b) {
-      const uint8_t* src = unit_src(uq[i]);
-      okq[i] = src != nullptr;
-      if (okq[i]) x_issue<FMT>(src, lds + X::kRing + i * X::kSlot, wave, ln.ld_off, st);
-    }
+  // ---- prime the ring: the first unit in flight into slot 0 -------------------------------
+  // uq = the next unit to compute, okq = its page is valid (a unit is issued
+  // iff it is inside the range and ok)
+  XUnit uq = x_seek(p, r, r.begin_b);
+  bool okq = true;
+  if (uq.b <= r.end_b) {
+    const uint8_t* src = unit_src(uq);
+    okq = src != nullptr;
+    if (okq && wave < kLoadWaves) x_issue<FMT>(src, lds + X::kRing, wave, ln.ld_off, st);
   }
   int slot = 0;
   int unit_id = 0;
@@ -604,21 +513,18 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = ld_meta(p.num_splits + b);
     const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
-    int last_ok[RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) last_ok[rb] = p.causal ? (L - p.s_q + s_idx[rb]) : (L - 1);
+    const int last_ok = p.causal ? (L - p.s_q + s_idx) : (L - 1);
 
-    // Q^T of this sequence: chunks 3..15 of the lane's rows in VGPRs, chunks
-    // 0, 1, 2, 16, 17 of all 128 rows in LDS
-    bf16x8 qf[X::kRegChunks][RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      const uint16_t* qrow = p.q + b * p.q_sb + s_idx[rb] * p.q_ss + shead[rb] * p.q_sh;
+    // Q^T of this sequence: chunks 7..15 of the lane's row in VGPRs, chunks
+    // 0..6, 16, 17 of all 128 rows in LDS
+    bf16x8 qf[X::kRegChunks];
+    {
+      const uint16_t* qrow = p.q + b * p.q_sb + s_idx * p.q_ss + shead * p.q_sh;
 #pragma unroll
       for (int c = 0; c < 18; ++c) {
         if (X::qslot(c) >= 0) continue;
-        const u32x4 v = srow_ok[rb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
-        qf[X::qreg(c)][rb] = __builtin_bit_cast(bf16x8, v);
+        const u32x4 v = srow_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+        qf[X::qreg(c)] = __builtin_bit_cast(bf16x8, v);
       }
     }
     lds_barrier_keep_loads();                 // no wave still reads the previous sequence's Q^T chunks
@@ -633,8 +539,8 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qb), 0, q_bytes, kRawBufferWord3);
       const int lrow = ln.lane >> 2, pslot = ln.lane & 3;
 #pragma unroll
-      for (int j = 0; j < (X::kQChunks * 8 + kWaves - 1) / kWaves; ++j) {
-        const int k = wave + kWaves * j;
+      for (int j = 0; j < (X::kQChunks * 8 + kWW - 1) / kWW; ++j) {
+        const int k = wave + kWW * j;
         if (k < X::kQChunks * 8) {
           const int qs = k >> 3, i = k & 7;
           const int row = 16 * i + lrow;
@@ -653,31 +559,21 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
     wait_vm_all();
     lds_barrier();
 
-    float m_run[RBW], l_run[RBW];
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 acc[4][8];                          // [16-dim block of this wave][16-row block]
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      m_run[rb] = kNegInf;
-      l_run[rb] = 0.f;
-    }
-    f32x4 acc[8][NRR];                        // [16-dim block][16-row block]
+    for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd)
-#pragma unroll
-      for (int rr = 0; rr < NRR; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < 8; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool bad = false;
 
-    while (uq[0].b == b) {
-      const XUnit u = uq[0];
-      const bool this_ok = okq[0];
+    while (uq.b == b) {
+      const XUnit u = uq;
+      const bool this_ok = okq;
       bad |= !this_ok;
-      // loads still allowed in flight: those of the units after u
-      int later = 0;
-#pragma unroll
-      for (int i = 1; i < kAhead; ++i) later += (uq[i].b <= r.end_b && okq[i]) ? 1 : 0;
-      wait_units<FMT>(later, wave);
+      wait_vm_all();                          // this wave's loads of u landed
       lds_barrier_keep_loads();               // every wave's loads of u landed; unit u - 1 is done everywhere
-      const XUnit last = uq[kAhead - 1];
-      const XUnit un = (last.b <= r.end_b) ? x_next(p, r, last) : last;
+      const XUnit un = x_next(p, r, u);
       const uint8_t* src_n = nullptr;
       bool ok_n = true;
       if (un.b <= r.end_b) {
@@ -686,51 +582,44 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
       }
       const int tok0 = u.pi * kPage + u.hf * kXHalf;
       const int valid = min(L - tok0, kXHalf);
-      const int slot_n = (slot + kAhead) % X::kSlots;   // held unit u - 1, free now
-      x_step<FMT, RBW>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + slot_n * X::kSlot, lds + X::kConv, src_n, st,
+      x_step<FMT>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + (slot ^ 1) * X::kSlot, lds + X::kConv, src_n, st,
                   ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run, wave_live,
                   live_rr);
       ++unit_id;
-      slot = (slot + 1) % X::kSlots;
-#pragma unroll
-      for (int i = 0; i + 1 < kAhead; ++i) {
-        uq[i] = uq[i + 1];
-        okq[i] = okq[i + 1];
-      }
-      uq[kAhead - 1] = un;
-      okq[kAhead - 1] = ok_n;
+      slot ^= 1;
+      uq = un;
+      okq = ok_n;
     }
 
-    // ---- epilogue: l of every row through LDS; each wave writes its 128 dims ----
+    // ---- epilogue: l of every row through LDS; each wave writes its 64 dims ----
     lds_barrier_keep_loads();                 // the P^T buffer is free
     float* lrow = reinterpret_cast<float*>(lds + X::kP);   // [rows] l
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      const float l_tot = sum4lanes(l_run[rb]);
-      if (q4 == 0) lrow[16 * RBW * wave + 16 * rb + r16] = l_tot;
-      if (q4 == 0 && srow_ok[rb]) {
-        float lse = (l_tot > 0.f) ? (m_run[rb] + __log2f(l_tot)) * kLn2 : kNegInf;
+    {
+      const float l_tot = sum4lanes(l_run);
+      if (q4 == 0) lrow[16 * wave + r16] = l_tot;
+      if (q4 == 0 && srow_ok) {
+        float lse = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
         if (bad) lse = __builtin_nanf("");
         if (nsplit == 1)
-          p.lse[(static_cast<int64_t>(b) * p.h_q + shead[rb]) * p.s_q + s_idx[rb]] = lse;
+          p.lse[(static_cast<int64_t>(b) * p.h_q + shead) * p.s_q + s_idx] = lse;
         else if (slot0 + split_idx < p.max_slots && split_idx < nsplit)
-          p.part_lse[(static_cast<int64_t>(slot0 + split_idx) * p.h_kv + kvh) * p.rows + srow[rb]] = lse;
+          p.part_lse[(static_cast<int64_t>(slot0 + split_idx) * p.h_kv + kvh) * p.rows + srow] = lse;
       }
     }
     lds_barrier_keep_loads();
-    // lane l holds, per (dd, rr), row 16 rr + r16 and dims 128 w + 16 dd + 4 q4 + 0..3
+    // lane l holds, per (dd, rr), row 16 rr + r16 and dims 64 w + 16 dd + 4 q4 + 0..3
     const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int rr = 0; rr < NRR; ++rr) {
+    for (int rr = 0; rr < 8; ++rr) {
       const int row = mt * M_TILE + 16 * rr + r16;
       if (row >= p.rows) continue;
       const float l_row = lrow[16 * rr + r16];
       const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
       const int si = row / p.group, hh = kvh * p.group + row % p.group;
       if (nsplit == 1) {
-        uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + si) * p.h_q + hh) * kDv + 128 * wave + 4 * q4;
+        uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + si) * p.h_q + hh) * kDv + 64 * wave + 4 * q4;
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
+        for (int dd = 0; dd < 4; ++dd) {
           float v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = bad ? nan : acc[dd][rr][i] * inv;
@@ -743,9 +632,9 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
           float* prow = p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv +
-                        128 * wave + 4 * q4;
+                        64 * wave + 4 * q4;
 #pragma unroll
-          for (int dd = 0; dd < 8; ++dd) {
+          for (int dd = 0; dd < 4; ++dd) {
             f32x4 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = bad ? nan : acc[dd][rr][i] * inv;
@@ -762,18 +651,12 @@ __global__ void __launch_bounds__(kThreads) splitkv_x_kernel(DecodeParams p) {
 
 hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wave, int grid, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const dim3 g(grid), blk(kThreads);
-  if (rows_per_wave == 32) {
-    if (kv_format == kFmtFp8)
-      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8, 2>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
-    else
-      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtBf16, 2>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
-  } else {
-    if (kv_format == kFmtFp8)
-      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8, 1>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
-    else
-      hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtBf16, 1>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
-  }
+  if (rows_per_wave != 32) return hipErrorInvalidValue;
+  const dim3 g(grid), blk(kWThreads);
+  if (kv_format == kFmtFp8)
+    hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  else
+    hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtBf16>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 

@@ -8,8 +8,8 @@
 //   rb = 16-row blocks per workgroup, tg = token groups per page, rb * tg = 4.
 // Few rows (memory-bound decode) split each page's tokens over the waves; 64
 // rows give each wave 16 rows and the whole page.
-// More than 64 rows: 128-row tiles (wide = 1, rb = 8), the S phase split by
-// rows and the PV phase by value dims over the 4 wavefronts.
+// More than 64 rows: 128-row tiles (wide = 1, rb = 8) on 8 wavefronts, the S
+// phase split by rows and the PV phase by value dims.
 #pragma once
 
 #include <cstdint>
