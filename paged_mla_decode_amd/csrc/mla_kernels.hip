@@ -9,9 +9,10 @@
 // below is designed for CDNA4, not taken from the Hopper design.
 //
 // Split kernel: one workgroup = 4 wavefronts per (KV range, row tile, KV head).
-//   * Pages stream into a two-slot LDS ring with global_load_lds_dwordx4:
+//   * Pages stream into a two-slot LDS ring with buffer_load_dwordx4 ... lds:
 //     64 lanes x 16 B land in 1 KB of LDS per instruction, so no VGPRs hold
-//     in-flight data and page i+1 loads while page i is computed. The 16-byte
+//     in-flight data, and page i+1 loads while page i is computed (its loads
+//     are issued right after the barrier that frees the slot). The 16-byte
 //     chunks of a 1152-byte token row are XOR-swizzled (chunk ^ f(token)) so
 //     both the K reads and the transposed V reads below hit distinct banks.
 //   * FP8 pages (656-byte records) stream raw into the ring; one LDS pass turns
@@ -45,21 +46,37 @@ using namespace dev;
 // Split-KV kernel
 // ----------------------------------------------------------------------------
 
+// Issue the direct loads of one page (bf16 rows, or raw FP8 records) from
+// `src` (`extent` bytes: 64 token strides) into the LDS slot `dst`: MUBUF
+// loads to LDS (buffer_load_dwordx4 ... lds), 16 bytes per lane at the
+// per-lane offsets `ld_off`. Unlike the FLAT form they count on vmcnt only,
+// so the LDS waits of the compute that follows never wait for them.
+template <int FMT>
+__device__ __forceinline__ void issue_page(const uint8_t* src, int extent, uint8_t* dst, const uint32_t* ld_off,
+                                           int wave) {
+  constexpr int kLoads = (FMT == kFmtFp8) ? kFp8Loads : kBf16Loads;
+  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, extent, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) {
+    const int k = wave + kWaves * j;
+    if (k < kLoads) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, ld_off[j], 0, 0, 0);
+  }
+}
+
 // One page of the pipeline. `cur` holds the page (bf16 rows, or raw FP8
-// records), `nxt` is the other ring slot and receives the next page, `conv`
-// (FP8 only) holds the converted bf16 page and its scales. The three regions
-// are disjoint; the restrict qualifiers let the compiler see that the reads
-// of this page never touch the loads in flight into `nxt`.
+// records), `conv` (FP8 only) holds the converted bf16 page and its scales;
+// the next page is in flight into the other ring slot. The regions are
+// disjoint; the restrict qualifiers let the compiler see that the reads of
+// this page never touch the loads in flight.
 template <int TG, int FMT>
-__device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
-                                          uint8_t* __restrict__ conv, const uint8_t* next_src,
-                                          const uint32_t* ld_off, const Lane& ln, int L, int last_allowed,
+__device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ conv,
+                                          const Lane& ln, int L, int last_allowed,
                                           int pi, bool this_ok, float scale_log2, const bf16x8 (&qf)[18],
                                           f32x4 (&acc)[32], float& m_run, float& l_run) {
   constexpr int NT = 4 / TG;
   constexpr bool kFp8 = (FMT == kFmtFp8);
-  constexpr int kLoads = kFp8 ? kFp8Loads : kBf16Loads;
-  constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
   constexpr int NG = kFp8 ? 4 : 1;    // scale groups folded into P
   const int tid = ln.tid, tg = ln.tg, r16 = ln.r16, q4 = ln.q4;
 
@@ -120,16 +137,6 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
       lds_barrier();
     }
     page = cur;
-  }
-
-  // next page -> nxt (direct to LDS; lands while this page is computed)
-  if (next_src != nullptr) {
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int k = ln.wave + kWaves * j;
-      if (k < kLoads)
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(next_src + ld_off[j]), LDS_PTR(void, nxt + 1024 * k), 16, 0, 0);
-    }
   }
 
   // ---- S^T tiles: rows = tokens, columns = query rows --------------------------
@@ -383,32 +390,57 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     }
   }
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
+  const int page_extent = kPage * static_cast<int>(p.kv_st);
 
+  // Block-table window: lane i holds entry win_pi + i of sequence win_b's row
+  // (-1 past the row). Refilled with one vector load when a page falls outside
+  // it (a new sequence, or every 64 pages), so pages need no scalar load each.
+  int bt_win = -1, win_b = -1, win_pi = 0;
   // Global address of page `pi` of sequence `b`; nullptr for a block-table
   // entry outside the pool (never dereferenced).
   auto page_src = [&](int b, int pi) -> const uint8_t* {
-    const int pg = ld_meta(p.block_table + static_cast<int64_t>(b) * p.bt_stride + pi);
+    if (b != win_b || pi < win_pi || pi >= win_pi + 64) {
+      win_b = b;
+      win_pi = pi;
+      const int e = pi + lane;
+      bt_win = e < p.max_blocks ? p.block_table[static_cast<int64_t>(b) * p.bt_stride + e] : -1;
+      wait_vm_all();
+    }
+    const int pg = __builtin_amdgcn_readlane(bt_win, pi - win_pi);
     if (pg < 0 || pg >= p.num_pages) return nullptr;
     return kv_head + static_cast<int64_t>(pg) * p.kv_sp;
   };
 
   // ---- pipeline: the page in flight always targets ring slot `slot` ------------
+  // (nb1, npi1) is the page after it, with its source src1 looked up one page
+  // early, so its loads are issued right after the barrier that frees the
+  // other slot.
   int slot = 0;
   bool load_ok = true;
+  int nb1 = r.end_b + 1, npi1 = 0;
+  const uint8_t* src1 = nullptr;
+  // the page after (b_, pi_) inside the range (b_ > r.end_b: none); e_ = end page of b_ if known (else -1)
+  auto advance = [&](int b_, int pi_, int e_, int& nb, int& npi) {
+    if (e_ < 0) {
+      int L_, a_;
+      seq_pages(p, r, b_, L_, a_, e_);
+    }
+    if (pi_ + 1 < e_) {
+      nb = b_;
+      npi = pi_ + 1;
+    } else {
+      next_with_pages(p, r, b_ + 1, nb, npi);
+    }
+  };
   {
     int nb, npi;
     next_with_pages(p, r, r.begin_b, nb, npi);
     if (nb <= r.end_b) {
       const uint8_t* src = page_src(nb, npi);
       load_ok = src != nullptr;
-      if (load_ok) {
-#pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j) {
-          const int k = wave + kWaves * j;
-          if (k < kLoads)
-            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src + ld_off[j]), LDS_PTR(void, ring + 1024 * k), 16, 0, 0);
-        }
-      }
+      if (load_ok) issue_page<FMT>(src, page_extent, ring, ld_off, wave);
+      advance(nb, npi, -1, nb1, npi1);
+      if (nb1 <= r.end_b) src1 = page_src(nb1, npi1);
     }
   }
 
@@ -446,17 +478,18 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       bad |= !this_ok;
       wait_vm_all();
       lds_barrier();                   // its bytes are in LDS; every wave is done with slot ^ 1
-      const uint8_t* next_src = nullptr;
-      {
-        int nb = b, npi = pi + 1;
-        if (npi >= pg1) next_with_pages(p, r, b + 1, nb, npi);
-        if (nb <= r.end_b) {
-          next_src = page_src(nb, npi);
-          load_ok = next_src != nullptr;
-        }
+      // the next page -> the other slot (direct to LDS; lands while this page is computed)
+      if (nb1 <= r.end_b) {
+        load_ok = src1 != nullptr;
+        if (load_ok) issue_page<FMT>(src1, page_extent, ring + (slot ^ 1) * kSlotBytes, ld_off, wave);
+        int nb2, npi2;
+        advance(nb1, npi1, nb1 == b ? pg1 : -1, nb2, npi2);
+        nb1 = nb2;
+        npi1 = npi2;
+        src1 = (nb1 <= r.end_b) ? page_src(nb1, npi1) : nullptr;
       }
-      page_step<TG, FMT>(ring + slot * kSlotBytes, ring + (slot ^ 1) * kSlotBytes, conv, next_src, ld_off, ln, L,
-                         last_allowed, pi, this_ok, p.scale_log2, qf, acc, m_run, l_run);
+      page_step<TG, FMT>(ring + slot * kSlotBytes, conv, ln, L, last_allowed, pi, this_ok, p.scale_log2, qf, acc,
+                         m_run, l_run);
       slot ^= 1;
     }
 

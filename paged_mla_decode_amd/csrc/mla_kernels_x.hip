@@ -66,7 +66,7 @@ struct XLayout {
   static constexpr int kP = kScale + (kFp8 ? 4 * kXHalf * 4 : 0);
   static constexpr int kAlpha = kP + kRows * kXHalf * 2;    // P^T: [rows][32 tokens] bf16
   static constexpr int kFlag = kAlpha + kRows * 4;          // alpha: [rows] fp32
-  static constexpr int kQ = kFlag + 64;                     // flags: [8] int32
+  static constexpr int kQ = kFlag + 64;                     // rescale flag word (64 bytes reserved)
   static constexpr int kQChunks = 9;
   static constexpr int kQChunkBytes = kRows * 64;           // one 32-dim Q^T chunk of all rows
   static constexpr int kTotal = kQ + kQChunks * kQChunkBytes;
@@ -195,7 +195,7 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
                                        uint8_t* __restrict__ work, const uint8_t* next_src, int st, const XLane& ln,
                                        int L, int last_ok, int tok0, int valid, bool this_ok, float scale_log2,
                                        int unit_id, const bf16x8 (&qf)[XLayout<FMT>::kRegChunks], f32x4 (&acc)[4][8],
-                                       float& m_run, float& l_run, bool wave_live, int live_rr) {
+                                       float& m_run, float& l_run) {
   using X = XLayout<FMT>;
   constexpr bool kFp8 = X::kFp8;
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
@@ -277,20 +277,23 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   // chunk order: bf16 0..17; FP8 the RoPE chunks 16, 17 first (unscaled), then
   // the 4 latent groups of 4 chunks, each group's partial logits scaled and added
   auto corder = [](int i) { return kFp8 ? (i < 2 ? 16 + i : i - 2) : i; };
-  // (a wave whose rows all lie past the last row skips the S phase; its S stays 0)
-  if (wave_live) {
-    bf16x8 kbuf[2][2];
+  // (padding rows of the last tile run through the phases like real rows: their
+  // Q^T is zero and nothing of theirs is written)
+  {
+    // the K and Q^T operands of chunk i + 1 are read while chunk i's MFMAs run
+    bf16x8 kbuf[2][2], qbuf[2];
     f32x4 part[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(corder(0), tt);
+    qbuf[0] = qop(corder(0));
 #pragma unroll
     for (int i = 0; i < 18; ++i) {
-      const int c = corder(i);
       if (i + 1 < 18) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) kbuf[(i + 1) & 1][tt] = kload(corder(i + 1), tt);
+        qbuf[(i + 1) & 1] = qop(corder(i + 1));
       }
-      const bf16x8 qv = qop(c);
+      const bf16x8 qv = qbuf[i & 1];
       if (!kFp8 || i < 2) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv, s[tt], 0, 0, 0);
@@ -358,15 +361,22 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
     *reinterpret_cast<bf16x8*>(pbuf + xrow_off(row, q4)) = pv;
     if (q4 == 0) alpha_buf[row] = alpha;
   }
-  if (ln.lane == 0 && __builtin_amdgcn_ballot_w64(rescaled) != 0) flags[wave] = unit_id;
+  // one flag word: every wave with a rescaled row writes this unit's id there
+  // (the same value, so concurrent writes agree)
+  if (ln.lane == 0 && __builtin_amdgcn_ballot_w64(rescaled) != 0) flags[0] = unit_id;
   lds_barrier_keep_loads();
 
   // ---- PV phase: O^T[dim 64 w + 16 dd + 4 q4 + i][row 16 rr + r16] += V^T P^T -------------
   {
-    bool any = false;
-#pragma unroll
-    for (int w = 0; w < kWW; ++w) any |= flags[w] == unit_id;
-    if (any) {
+    // The flag word is read in inline asm (the wait inside the same block):
+    // the compiler cannot tell that this fixed LDS address is not a target of
+    // the direct loads in flight and would otherwise wait for all of them here.
+    int fl;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(fl)
+                 : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(flags)))
+                 : "memory");
+    if (__builtin_amdgcn_readfirstlane(fl) == unit_id) {
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const float a = alpha_buf[16 * rr + r16];
@@ -405,11 +415,9 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
     if (rr + 1 < 8) pb[(rr + 1) & 1] = pload(rr + 1);
-    if (rr < live_rr) {                           // skip row blocks past the last row
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
-        acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd], pb[rr & 1], acc[dd][rr], 0, 0, 0);
-    }
+    for (int dd = 0; dd < 4; ++dd)
+      acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd], pb[rr & 1], acc[dd][rr], 0, 0, 0);
   }
 }
 
@@ -463,17 +471,13 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
   }
   if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
 
-  if (tid < kWW) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
+  if (tid == 0) reinterpret_cast<int*>(lds + X::kFlag)[0] = -1;
 
   // S-phase row of this lane
   const int srow = mt * M_TILE + 16 * wave + r16;
   const bool srow_ok = srow < p.rows;
   const int s_idx = srow_ok ? srow / p.group : 0;
   const int shead = kvh * p.group + (srow_ok ? srow % p.group : 0);
-
-  // waves / row blocks with at least one row (uniform): the rest of the tile is padding
-  const bool wave_live = mt * M_TILE + 16 * wave < p.rows;
-  const int live_rr = min(8, (p.rows - mt * M_TILE + 15) / 16);
 
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
   // Block-table window: lane i holds entry win_pi + i of sequence win_b's row
@@ -583,8 +587,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
       const int tok0 = u.pi * kPage + u.hf * kXHalf;
       const int valid = min(L - tok0, kXHalf);
       x_step<FMT>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + (slot ^ 1) * X::kSlot, lds + X::kConv, src_n, st,
-                  ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run, wave_live,
-                  live_rr);
+                  ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run);
       ++unit_id;
       slot ^= 1;
       uq = un;
