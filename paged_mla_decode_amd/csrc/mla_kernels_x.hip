@@ -480,22 +480,33 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
   const int shead = kvh * p.group + (srow_ok ? srow % p.group : 0);
 
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
-  // Block-table window: lane i holds entry win_pi + i of sequence win_b's row
-  // (-1 past the row). Refilled with one vector load when a unit falls outside
-  // it (a new sequence, or every 64 pages), so units need no scalar load each.
-  int bt_win = -1, win_b = -1, win_pi = 0;
+  // Page-address window: lane i holds the global address of page win_pi + i
+  // of sequence win_b (0 for an entry past the row or outside the pool).
+  // Refilled with one vector load of the block-table row when a unit falls
+  // outside it (a new sequence, or every 64 pages), so a unit's address costs
+  // two lane reads and an add.
+  uint32_t win_lo = 0, win_hi = 0;
+  int win_b = -1, win_pi = 0;
+  const int64_t half_bytes = static_cast<int64_t>(kXHalf) * st;
   // global address of a unit (nullptr: block-table entry outside the pool)
   auto unit_src = [&](const XUnit& u) -> const uint8_t* {
     if (u.b != win_b || u.pi < win_pi || u.pi >= win_pi + 64) {
       win_b = u.b;
       win_pi = u.pi;
       const int e = u.pi + ln.lane;
-      bt_win = e < p.max_blocks ? p.block_table[static_cast<int64_t>(u.b) * p.bt_stride + e] : -1;
+      const int pg = e < p.max_blocks ? p.block_table[static_cast<int64_t>(u.b) * p.bt_stride + e] : -1;
+      const uint64_t a = (pg >= 0 && pg < p.num_pages)
+                             ? reinterpret_cast<uint64_t>(kv_head + static_cast<int64_t>(pg) * p.kv_sp)
+                             : 0ull;
+      win_lo = static_cast<uint32_t>(a);
+      win_hi = static_cast<uint32_t>(a >> 32);
       wait_vm_all();
     }
-    const int pg = __builtin_amdgcn_readlane(bt_win, u.pi - win_pi);
-    if (pg < 0 || pg >= p.num_pages) return nullptr;
-    return kv_head + static_cast<int64_t>(pg) * p.kv_sp + static_cast<int64_t>(u.hf) * kXHalf * st;
+    const uint32_t lo = __builtin_amdgcn_readlane(win_lo, u.pi - win_pi);
+    const uint32_t hi = __builtin_amdgcn_readlane(win_hi, u.pi - win_pi);
+    const uint64_t a = (static_cast<uint64_t>(hi) << 32) | lo;
+    if (a == 0) return nullptr;
+    return reinterpret_cast<const uint8_t*>(a) + (u.hf ? half_bytes : 0);
   };
 
   // ---- prime the ring: the first unit in flight into slot 0 -------------------------------
