@@ -163,8 +163,9 @@ typedef struct mla_decode_args {
   size_t workspace_bytes;
 
   /* Optional hint: 0 = unknown, else the largest number of pieces of any
-     sequence (max_b num_splits[b+1] - num_splits[b]); it only selects the
-     shape of the combine kernel (results do not depend on it). */
+     sequence (max_b num_splits[b+1] - num_splits[b]). Accepted for
+     compatibility; the current combine kernel handles any piece count and
+     does not use it (results never depend on it). */
   int max_splits;
 
   /* Optional timing hooks (hipEvent_t or NULL): events[0] and events[1] take

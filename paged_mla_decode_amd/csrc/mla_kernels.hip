@@ -585,101 +585,81 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
 
 // ----------------------------------------------------------------------------
 // Combine: LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i
-// One workgroup per (sequence, row, KV head, 128-dim quarter). Thread t takes
-// splits i = t / 16 (mod 16) and dims 8 * (t % 16) .. +8 of the quarter, so 16
-// splits are read at once; the 16 partial sums are reduced through LDS.
+// (the split epilogue of the wmrh.cn page, "计算流水线设计"; O_i are the
+// pieces' normalised partial outputs). The narrow kernel reads each piece's
+// LSE and O together and merges them online -- a running max M,
+// l = sum exp(LSE_i - M) and acc = sum exp(LSE_i - M) O_i, rescaled when M
+// grows -- so the partials are read in one pass with all loads of a group of
+// pieces in flight.
+// Empty pieces (LSE = -inf, O = 0) add nothing; a NaN LSE (a piece with a
+// page outside the pool) makes l NaN for good, and with it O and LSE.
 // ----------------------------------------------------------------------------
 
-constexpr int kCombDims = 128;                  // dims per workgroup
-constexpr int kCombGroups = kThreads / (kCombDims / 8);   // 16 split lanes
+struct MergeState {
+  float m = kNegInf;      // running max of the LSEs seen
+  float l = 0.f;          // sum exp(LSE_i - m)
+  f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = f32x4{0.f, 0.f, 0.f, 0.f};   // sum exp(LSE_i - m) O_i (8 dims)
+};
 
-__global__ void __launch_bounds__(kThreads) combine_kernel(DecodeParams p) {
-  __shared__ float red[kCombGroups][kCombDims + 4];
-  __shared__ float stat[2][kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x;
-  const int row = blockIdx.y;
-  const int kvh = blockIdx.z / (kDv / kCombDims);
-  const int quarter = blockIdx.z % (kDv / kCombDims);
-  const int slot0 = ld_meta(p.num_splits + b);
-  const int n = ld_meta(p.num_splits + b + 1) - slot0;
-  if (n <= 1 || row >= p.rows) return;
-  const int s_idx = row / p.group;
-  const int head = kvh * p.group + row % p.group;
-  const int sub = tid / (kCombDims / 8), dl = tid % (kCombDims / 8);
-  const int dim0 = quarter * kCombDims + 8 * dl;
-  uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
-  float* lse_out = p.lse + (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
-  if (slot0 < 0 || slot0 + n > p.max_slots) {
-    if (sub == 0) *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    if (tid == 0 && quarter == 0) *lse_out = __builtin_nanf("");
-    return;
+// Merge up to N pieces (valid[i]) whose LSE and 8 dims of O are already in registers.
+template <int N>
+__device__ __forceinline__ void merge_group(MergeState& st, const float (&lse)[N], const f32x4 (&x0)[N],
+                                            const f32x4 (&x1)[N], int n_valid) {
+  float mc = kNegInf;
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < n_valid) {
+      mc = fmaxf(mc, lse[i]);
+      nan |= lse[i] != lse[i];
+    }
   }
-  const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;             // slots apart
-  const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
-  const float* o_in = p.part_o + (static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row) * kDv
-                      + dim0;
-
-  // LSE over all splits (block-wide max, then sum)
-  float mx = kNegInf;
-  for (int i = tid; i < n; i += kThreads) mx = fmaxf(mx, lse_in[i * stride]);
+  if (nan) st.l = __builtin_nanf("");
+  const float mn = fmaxf(st.m, mc);
+  if (mn == kNegInf) return;                 // nothing allowed so far
+  const float sc = (st.m == kNegInf) ? 0.f : __expf(st.m - mn);
+  st.l *= sc;
+  st.a0 *= sc;
+  st.a1 *= sc;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) stat[0][wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(stat[0][0], stat[0][1]), fmaxf(stat[0][2], stat[0][3]));
-  const bool any = mx != kNegInf;
-  const float mxu = any ? mx : 0.f;
-  float sum = 0.f;
-  for (int i = tid; i < n; i += kThreads) sum += __expf(lse_in[i * stride] - mxu);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-  if (lane == 0) stat[1][wave] = sum;
-  __syncthreads();
-  sum = stat[1][0] + stat[1][1] + stat[1][2] + stat[1][3];
-  const float lse = any ? mxu + __logf(sum) : kNegInf;
-
-  f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  if (any) {
-#pragma unroll 4
-    for (int i = sub; i < n; i += kCombGroups) {
-      const float w = __expf(lse_in[i * stride] - lse);
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
-      if (w != 0.f) {          // a split with no allowed key has w = 0 and O = 0
-        a0 += w * x0;
-        a1 += w * x1;
+  for (int i = 0; i < N; ++i) {
+    if (i < n_valid) {
+      const float w = __expf(lse[i] - mn);
+      st.l += w;
+      if (w != 0.f) {                        // an empty piece has w = 0 and O = 0
+        st.a0 += w * x0[i];
+        st.a1 += w * x1[i];
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    red[sub][8 * dl + j] = a0[j];
-    red[sub][8 * dl + 4 + j] = a1[j];
-  }
-  __syncthreads();
-  if (tid < kCombDims / 8) {
-    float o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int g = 0; g < kCombGroups; ++g) acc += red[g][8 * tid + j];
-      o[j] = acc;
-    }
-    u32x4 outw;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      outw[j] = static_cast<uint32_t>(f32_to_bf16(o[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(o[2 * j + 1])) << 16);
-    *reinterpret_cast<u32x4*>(p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv +
-                              quarter * kCombDims + 8 * tid) = outw;
-    if (tid == 0 && quarter == 0) *lse_out = lse;
-  }
+  st.m = mn;
 }
 
-// Narrow combine, for sequences cut into few pieces: one workgroup per
-// (sequence, 16 rows, KV head, 128-dim quarter); 16 lanes per row, 8 dims per
-// lane, the pieces walked in a loop with independent loads.
+// 1 / l for the final normalisation: 0 when nothing was allowed (O = 0), NaN for NaN.
+__device__ __forceinline__ float merge_inv(float l) { return (l > 0.f) ? 1.f / l : ((l != l) ? l : 0.f); }
+
+// LSE of a merged state: -inf when nothing was allowed, NaN for NaN.
+__device__ __forceinline__ float merge_lse(const MergeState& st) {
+  return (st.l > 0.f || st.l != st.l) ? st.m + __logf(st.l) : kNegInf;
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const f32x4& a0, const f32x4& a1) {
+  u32x4 w;
+  w[0] = static_cast<uint32_t>(f32_to_bf16(a0[0])) | (static_cast<uint32_t>(f32_to_bf16(a0[1])) << 16);
+  w[1] = static_cast<uint32_t>(f32_to_bf16(a0[2])) | (static_cast<uint32_t>(f32_to_bf16(a0[3])) << 16);
+  w[2] = static_cast<uint32_t>(f32_to_bf16(a1[0])) | (static_cast<uint32_t>(f32_to_bf16(a1[1])) << 16);
+  w[3] = static_cast<uint32_t>(f32_to_bf16(a1[2])) | (static_cast<uint32_t>(f32_to_bf16(a1[3])) << 16);
+  return w;
+}
+
+constexpr int kCombDims = 128;                  // dims per workgroup
+constexpr int kCombGroup = 8;                   // pieces whose loads are in flight together
+
+// One workgroup per (sequence, 16 rows, KV head, 128-dim quarter); 16 lanes
+// per row, 8 dims per lane, the pieces in groups of kCombGroup with all their
+// loads in flight at once. (A two-pass kernel with 16 pieces per workgroup in
+// parallel, for sequences cut into many pieces, was slower on the ragged
+// workload: 24 us against 19 us.)
 __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -704,41 +684,30 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) 
   const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   const float* o_in = p.part_o + (static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row) * kDv
                       + dim0;
-  float mx = kNegInf;
-  for (int i = l16; i < n; i += 16) mx = fmaxf(mx, lse_in[i * stride]);
+  MergeState st;
+  for (int i0 = 0; i0 < n; i0 += kCombGroup) {
+    float lse[kCombGroup];
+    f32x4 x0[kCombGroup], x1[kCombGroup];
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  const bool any = mx != kNegInf;
-  const float mxu = any ? mx : 0.f;
-  float sum = 0.f;
-  for (int i = l16; i < n; i += 16) sum += __expf(lse_in[i * stride] - mxu);
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-  const float lse = any ? mxu + __logf(sum) : kNegInf;
-  f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  if (any) {
-#pragma unroll 4
-    for (int i = 0; i < n; ++i) {
-      const float w = __expf(lse_in[i * stride] - lse);
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
-      if (w != 0.f) {
-        a0 += w * x0;
-        a1 += w * x1;
+    for (int j = 0; j < kCombGroup; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        lse[j] = lse_in[i * stride];
+        x0[j] = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
+        x1[j] = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
+      } else {
+        lse[j] = kNegInf;
+        x0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        x1[j] = x0[j];
       }
     }
+    merge_group<kCombGroup>(st, lse, x0, x1, min(n - i0, kCombGroup));
   }
-  u32x4 outw;
-  outw[0] = static_cast<uint32_t>(f32_to_bf16(a0[0])) | (static_cast<uint32_t>(f32_to_bf16(a0[1])) << 16);
-  outw[1] = static_cast<uint32_t>(f32_to_bf16(a0[2])) | (static_cast<uint32_t>(f32_to_bf16(a0[3])) << 16);
-  outw[2] = static_cast<uint32_t>(f32_to_bf16(a1[0])) | (static_cast<uint32_t>(f32_to_bf16(a1[1])) << 16);
-  outw[3] = static_cast<uint32_t>(f32_to_bf16(a1[2])) | (static_cast<uint32_t>(f32_to_bf16(a1[3])) << 16);
-  *reinterpret_cast<u32x4*>(orow) = outw;
-  if (l16 == 0 && quarter == 0) *lse_out = lse;
+  const float inv = merge_inv(st.l);
+  *reinterpret_cast<u32x4*>(orow) = pack_bf16x8(st.a0 * inv, st.a1 * inv);
+  if (l16 == 0 && quarter == 0) *lse_out = merge_lse(st);
 }
 
-// Pieces per sequence up to which the narrow combine is used.
-constexpr int kNarrowCombineMax = 8;
 
 template <int RB, int TG>
 hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
@@ -773,15 +742,12 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
     err = launch_split<4, 1>(p, kv_format, grid, stream, ev0, ev1);
   }
   if (err != hipSuccess) return err;
-  if (p.max_splits > 0 && p.max_splits <= kNarrowCombineMax) {
+  {
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
     hipLaunchKernelGGL(combine_rows_kernel, cgrid, dim3(kThreads), 0, stream, p);
-  } else {
-    const dim3 cgrid(p.batch, p.rows, p.h_kv * (kDv / kCombDims));
-    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, stream, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
   if (ev2) {
     err = hipEventRecord(ev2, stream);
     if (err != hipSuccess) return err;
