@@ -50,10 +50,12 @@ inline Plan make_plan(int heads_per_kv, int kv_format) {
   p.m_tile = 16 * p.rb;
   p.m_tiles = (heads_per_kv + p.m_tile - 1) / p.m_tile;
   p.wgs_per_cu = 1;      // the two-page LDS ring (144-155 KB) leaves room for one workgroup per CU
-  // per-piece fixed work (Q load, partial write and merge) in pages of KV: 16 rows
-  // carry 18 KB of Q and 32 KB of partial O per piece, 128 rows 8x that
-  // (measured best at 3 for 128-row tiles on the h_q = 128 workloads)
-  p.split_cost = p.wide ? 3 : 1;
+  // per-piece fixed work in pages of KV: a 128-row piece loads 147 KB of Q,
+  // writes 256 KB of partial O and the combine reads it back (about 9 pages of
+  // KV bytes); a piece of up to 64 rows carries 1/8 of that plus the merge of
+  // the token groups. Measured: 8 and 2 (compute_heavy, uniform_long; mtp,
+  // fp8 and ragged unchanged within noise).
+  p.split_cost = p.wide ? 8 : 2;
   p.min_pages = 1;
   return p;
 }
