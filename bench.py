@@ -171,7 +171,7 @@ def pmc_summary(args) -> str:
     counters read for the calibration copy of known size."""
     from workloads import named_workload
     w = named_workload(args.workload)
-    split_name = "splitkv_x_kernel" if (w.kv_format == "bf16" and w.heads_per_kv > 64) else "splitkv_kernel"
+    split_name = "splitkv_x_kernel" if w.heads_per_kv > 64 else "splitkv_kernel"
     is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
     is_copy = lambda n: "elementwise" in n and "Mul" in n
     fr, wr = _pmc_rows(args.pmc_summary[0]), _pmc_rows(args.pmc_summary[1])
@@ -316,7 +316,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(split_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(split_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
 
-    split_name = "splitkv_x_kernel" if (w.kv_format == "bf16" and w.heads_per_kv > 64) else "splitkv_kernel"
+    split_name = "splitkv_x_kernel" if w.heads_per_kv > 64 else "splitkv_kernel"
     roof["traffic"] = stored_traffic(split_name, w.name)
 
     result = {
