@@ -8,13 +8,15 @@
 // library's own.
 //
 // Greedy fill: every piece of a sequence costs split_cost (its fixed work:
-// loading Q, writing a partial result, merging it) plus its pages. Each range
-// gets a budget of ceil(T / P) + split_cost, T = sum of pages + split_cost per
-// sequence, P = ranges, and takes sequences in batch order while they fit;
-// the sequence that does not fit is cut between pages so that the range uses
-// its budget, unless that would leave a piece smaller than min_pages (then
-// the range stops before it, or takes its few remaining pages). The last
-// range takes whatever is left. Ranges are consecutive, so every
+// loading Q, writing a partial result, merging it) plus its pages. Every
+// range gets the same budget and takes sequences in batch order while they
+// fit; the sequence that does not fit is cut between pages so that the range
+// uses its budget, unless that would leave a piece smaller than min_pages
+// (then the range stops before it, or takes its few remaining pages). The
+// budget is the smallest one with which this pass places all the work in
+// the ranges (binary search; a guessed budget such as ceil(T / P) +
+// split_cost lets ranges that take only whole sequences run ahead and leaves
+// the last ranges empty). Ranges are consecutive, so every
 // (sequence, page) lies in exactly one range, in order, and every sequence --
 // also one of length 0 -- lies in exactly one range or spans several
 // consecutive ones.
@@ -25,29 +27,25 @@
 
 namespace mla {
 
-int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, int min_pages,
-             int32_t* meta, int32_t* num_splits) {
-  std::vector<int64_t> npages(batch);
-  int64_t total = 0;
-  for (int b = 0; b < batch; ++b) {
-    npages[b] = (static_cast<int64_t>(seqlens[b]) + kPage - 1) / kPage;
-    total += split_cost + npages[b];
-  }
-  const int64_t budget = (total + num_parts - 1) / num_parts + split_cost;
+namespace {
 
-  std::vector<int32_t> pieces(batch, 0);
-  std::memset(meta, 0, sizeof(int32_t) * static_cast<size_t>(num_parts) * kMetaInts);
+// One greedy pass with a fixed budget per range. Returns true when every
+// (sequence, page) fits into the num_parts ranges; when `meta` is non-null it
+// also writes the ranges (the last range then takes whatever is left) and
+// counts the pieces of each sequence.
+bool fill(const std::vector<int64_t>& npages, int num_parts, int split_cost, int min_pages, int64_t budget,
+          int32_t* meta, std::vector<int32_t>* pieces) {
+  const int batch = static_cast<int>(npages.size());
   int b = 0;        // position: sequence b, page i
   int64_t i = 0;
   for (int p = 0; p < num_parts; ++p) {
-    int32_t* m = meta + static_cast<size_t>(p) * kMetaInts;
     const int b0 = b;
     const int64_t i0 = i;
     int64_t room = budget;
-    const bool last_range = (p == num_parts - 1);
+    const bool take_rest = meta != nullptr && p == num_parts - 1;
     while (b < batch) {
       const int64_t left = npages[b] - i;
-      if (last_range || split_cost + left <= room) {      // the rest of sequence b fits
+      if (take_rest || split_cost + left <= room) {        // the rest of sequence b fits
         room -= split_cost + left;
         ++b;
         i = 0;
@@ -63,6 +61,8 @@ int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, i
       }
       break;
     }
+    if (meta == nullptr) continue;
+    int32_t* m = meta + static_cast<size_t>(p) * kMetaInts;
     if (b0 == b && i0 == i) {                              // empty range
       m[0] = -1; m[1] = 0; m[2] = -2; m[3] = 0; m[4] = 0;
       continue;
@@ -80,9 +80,36 @@ int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, i
     m[1] = static_cast<int32_t>(i0);
     m[2] = end_b;
     m[3] = static_cast<int32_t>(end_page);
-    m[4] = pieces[b0];
-    for (int s = b0; s <= end_b; ++s) pieces[s] += 1;
+    m[4] = (*pieces)[b0];
+    for (int s = b0; s <= end_b; ++s) (*pieces)[s] += 1;
   }
+  return b >= batch;
+}
+
+}  // namespace
+
+int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, int min_pages,
+             int32_t* meta, int32_t* num_splits) {
+  std::vector<int64_t> npages(batch);
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) {
+    npages[b] = (static_cast<int64_t>(seqlens[b]) + kPage - 1) / kPage;
+    total += split_cost + npages[b];
+  }
+  // smallest budget with which the greedy pass places everything (binary
+  // search: a larger budget never needs more ranges)
+  int64_t lo = (total + num_parts - 1) / num_parts, hi = total + split_cost;
+  if (lo < 1) lo = 1;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (fill(npages, num_parts, split_cost, min_pages, mid, nullptr, nullptr))
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  std::vector<int32_t> pieces(batch, 0);
+  std::memset(meta, 0, sizeof(int32_t) * static_cast<size_t>(num_parts) * kMetaInts);
+  fill(npages, num_parts, split_cost, min_pages, lo, meta, &pieces);
   num_splits[0] = 0;
   for (int s = 0; s < batch; ++s) num_splits[s + 1] = num_splits[s] + pieces[s];
   return num_splits[batch];

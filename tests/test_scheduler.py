@@ -96,8 +96,8 @@ def test_balance_on_ragged_lengths():
     pieces = check_schedule(L, meta, splits)
     npg = (L + 63) // 64
     # cost of each range = its pages + a fixed cost per piece (the scheduler's
-    # split cost: 2 pages for tiles of up to 64 rows)
-    split_cost = 2
+    # split cost: 3 pages for tiles of up to 64 rows)
+    split_cost = 3
     costs = []
     for m in meta:
         bb, bp, eb, ep = (int(x) for x in m[:4])
