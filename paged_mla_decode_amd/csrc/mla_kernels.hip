@@ -61,7 +61,9 @@ __device__ __forceinline__ void issue_page(const uint8_t* src, int extent, uint8
 #pragma unroll
   for (int j = 0; j < kLoadsPerWave; ++j) {
     const int k = wave + kWaves * j;
-    if (k < kLoads) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, ld_off[j], 0, 0, 0);
+    if (k < kLoads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, ld_off[j], 0, 0,
+                                               kPageLoadPolicy);
   }
 }
 

@@ -166,10 +166,11 @@ __device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wa
     const int k = wave + kLoadWaves * j;
     if constexpr (FMT == kFmtFp8) {
       if (k < X::kLoads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0,
+                                                 kPageLoadPolicy);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[0], 8 * wave * st + 128 * j,
-                                               0, 0);
+                                               0, kPageLoadPolicy);
     }
   }
 }
