@@ -265,11 +265,23 @@ def main():
     stream = torch.cuda.current_stream(dev)
     hip = HipEvents()
 
+    # two pinned staging buffers for the host scheduler's output, used in turn; a buffer is
+    # rewritten only after the upload that read it two steps earlier has finished
+    stage = [torch.empty((parts * 8 + w.batch + 1,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    stage_done = [None, None]
+
     def step(i, ev=None):
         # a1: host tile scheduler for this step's lengths, uploaded on the decode stream
         # (metadata rows and num_splits share one pinned buffer: one copy)
-        m_h, _ = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts, pin=True)
-        flat_dev.copy_(mla.packed_metadata(m_h), non_blocking=True)
+        k = i & 1
+        if stage_done[k] is not None:
+            stage_done[k].synchronize()
+        m_h, _ = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts,
+                                           out=stage[k])
+        flat_dev.copy_(stage[k], non_blocking=True)
+        if stage_done[k] is None:
+            stage_done[k] = torch.cuda.Event()
+        stage_done[k].record(stream)
         d = decoders[i % copies]
         d.set_events(ev if ev is not None else (None, None, None))
         d.run(stream)

@@ -70,8 +70,12 @@ def _i32p(t: torch.Tensor):
 
 def mla_get_metadata_host(cache_seqlens_host: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *,
                           kv_format="bf16", num_parts: int = 0, num_cus: int = 0,
-                          pin: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Host tile scheduler: int32 CPU tensors (tile_metadata [P, 8], num_splits [B + 1])."""
+                          pin: bool = False, out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Host tile scheduler: int32 CPU tensors (tile_metadata [P, 8], num_splits [B + 1]).
+
+    `out` (optional): a contiguous int32 CPU tensor of P * 8 + B + 1 elements (pinned, say) that
+    receives [tile_metadata | num_splits]; the returned tensors are views of it. The caller must
+    not overwrite a buffer whose previous contents are still being copied to the device."""
     lib = _lib.load()
     L = cache_seqlens_host
     if L.device.type != "cpu":
@@ -87,7 +91,14 @@ def mla_get_metadata_host(cache_seqlens_host: torch.Tensor, heads_per_kv: int, h
         if parts < 0:
             raise ValueError(_lib.last_error())
     # one buffer [tile_metadata (parts x 8) | num_splits (B + 1)]: a single upload
-    flat = torch.empty((parts * META_INTS + B + 1,), dtype=torch.int32, pin_memory=pin)
+    n = parts * META_INTS + B + 1
+    if out is not None:
+        if (out.device.type != "cpu" or out.dtype != torch.int32 or not out.is_contiguous()
+                or out.dim() != 1 or int(out.shape[0]) != n):
+            raise ValueError(f"out must be a contiguous 1-D int32 CPU tensor of {n} elements")
+        flat = out
+    else:
+        flat = torch.empty((n,), dtype=torch.int32, pin_memory=pin)
     meta = flat[:parts * META_INTS].view(parts, META_INTS)
     splits = flat[parts * META_INTS:]
     got = ctypes.c_int(0)

@@ -159,3 +159,16 @@ def test_packed_metadata_round_trip():
     assert m2.data_ptr() == meta.data_ptr() and s2.data_ptr() == splits.data_ptr()
     with pytest.raises(ValueError):
         mla.split_metadata(flat, 6)
+
+
+def test_metadata_into_caller_buffer():
+    import torch
+    import paged_mla_decode_amd as mla
+    L = torch.tensor([0, 5, 700, 64, 3000], dtype=torch.int32)
+    meta, splits = mla.mla_get_metadata_host(L, 16, 1, num_cus=256, num_parts=7)
+    buf = torch.full((7 * 8 + 6,), -123, dtype=torch.int32)
+    m2, s2 = mla.mla_get_metadata_host(L, 16, 1, num_cus=256, num_parts=7, out=buf)
+    assert torch.equal(m2, meta) and torch.equal(s2, splits)
+    assert m2.data_ptr() == buf.data_ptr()
+    with pytest.raises(ValueError):
+        mla.mla_get_metadata_host(L, 16, 1, num_cus=256, num_parts=7, out=torch.empty(10, dtype=torch.int32))
