@@ -209,6 +209,12 @@ def pmc_summary(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def percentiles(xs, ps):
+    """Nearest-rank percentiles of a list of floats."""
+    ys = sorted(xs)
+    return [ys[min(len(ys) - 1, max(0, math.ceil(p / 100 * len(ys)) - 1))] for p in ps]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +357,7 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "split_kernel_ms": round(split_avg, 5),
+        "split_kernel_ms_p10_p50_p90": [round(x, 5) for x in percentiles(split_ms, (10, 50, 90))],
         "combine_kernel_ms": round(comb_avg, 5),
         "algorithmic_bytes": byts,
         "algorithmic_flops": flops,
