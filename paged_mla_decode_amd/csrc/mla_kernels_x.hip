@@ -1,5 +1,8 @@
-// mla_kernels_x.hip -- split-KV MLA decode kernel for more than 64 query rows
-// per KV head on gfx950 (MI355X): 128-row tiles, 8 wavefronts.
+// mla_kernels_x.hip -- split-KV MLA decode kernels for more than 64 query rows
+// per KV head on gfx950 (MI355X): 128-row tiles, 8 wavefronts. FP8 pages use
+// splitkv_x_kernel (two barriers per unit: the conversion buffer of a unit
+// must outlive its S and PV phases); bf16 pages use splitkv_x1_kernel (one
+// barrier per unit, see its section).
 //
 // Same computation as the 64-row kernel in mla_kernels.hip (softmax attention
 // of query rows over a sequence's cached latent rows, V = their first 512
@@ -662,6 +665,404 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
   wait_vm_all();
 }
 
+
+// ----------------------------------------------------------------------------
+// 128-row tiles, bf16 pages: one barrier per unit
+//
+// The same S / softmax / PV phases on 8 waves, but P^T, the rescale factors
+// and the flag word are double-buffered by unit parity and the ring has three
+// slots, so one barrier per unit suffices: between the barriers of units
+// u - 1 and u a wave runs PV of u - 1 and then S and the softmax of u, and a
+// wave that finishes PV early goes on with S while the others still multiply
+// (the two waves on a SIMD drift into different phases). Rows past the
+// sequence end read zeros straight from the loads (the buffer resource ends at
+// the unit's last valid token), so the unit needs no zeroing pass.
+// ----------------------------------------------------------------------------
+
+struct X1Layout {
+  static constexpr int kRows = 128;
+  static constexpr int kSlot = kXHalfBytes;
+  static constexpr int kSlots = 3;
+  static constexpr int kRing = 0;
+  static constexpr int kP = kRing + kSlots * kSlot;
+  static constexpr int kPBytes = kRows * kXHalf * 2;          // one P^T buffer: 8 KB
+  static constexpr int kAlpha = kP + 2 * kPBytes;             // [2][128] fp32
+  static constexpr int kFlag = kAlpha + 2 * kRows * 4;        // [2] flag words (64 B reserved)
+  static constexpr int kQ = kFlag + 64;
+  static constexpr int kQChunks = 4;                          // Q^T chunks 0, 1, 16, 17 of all rows
+  static constexpr int kQChunkBytes = kRows * 64;
+  static constexpr int kTotal = kQ + kQChunks * kQChunkBytes;
+  static constexpr int kLow = 2;
+  static constexpr int qslot(int c) { return c < kLow ? c : (c >= 16 ? c - 16 + kLow : -1); }
+  static constexpr int kRegChunks = 18 - kQChunks;
+  static constexpr int qreg(int c) { return c - kLow; }
+  static constexpr int qchunk(int qs) { return qs < kLow ? qs : 16 - kLow + qs; }
+};
+static_assert(X1Layout::kTotal <= 163840, "LDS budget");
+
+// Direct loads of one bf16 unit (waves 0..3), the buffer ending after the
+// unit's `valid` tokens: rows past them read zeros.
+__device__ __forceinline__ void x1_issue(const uint8_t* src, int valid, uint8_t* dst, int wave, uint32_t off, int st) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, valid * st, kRawBufferWord3);
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int k = wave + kLoadWaves * j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off, 8 * wave * st + 128 * j, 0,
+                                             kPageLoadPolicy);
+  }
+}
+
+// S phase and softmax of one unit for this wave's 16 rows; P^T, rescale factor
+// and flag into the buffers of parity `par`.
+__device__ __forceinline__ void x1_s(const uint8_t* __restrict__ page, uint8_t* __restrict__ work, const XLane& ln,
+                                     int par, int L, int last_ok, int tok0, float scale_log2, int unit_id,
+                                     const bf16x8 (&qf)[X1Layout::kRegChunks], float& m_run, float& l_run) {
+  using X = X1Layout;
+  const int wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+  uint8_t* const lds = work - X::kP;
+  const uint8_t* qlds = lds + X::kQ;
+  auto qop = [&](int c) -> bf16x8 {
+    const int qs = X::qslot(c);
+    if (qs >= 0) return *reinterpret_cast<const bf16x8*>(qlds + qs * X::kQChunkBytes + xrow_off(16 * wave + r16, q4));
+    return qf[X::qreg(c)];
+  };
+  auto kload = [&](int c, int tt) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(page + ln.k_off[c & 1] + 16 * tt * 128 + 4096 * (c >> 1));
+  };
+  f32x4 s[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    bf16x8 kbuf[2][2], qbuf[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(0, tt);
+    qbuf[0] = qop(0);
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+      if (c + 1 < 18) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) kbuf[(c + 1) & 1][tt] = kload(c + 1, tt);
+        qbuf[(c + 1) & 1] = qop(c + 1);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c & 1][tt], qbuf[c & 1], s[tt], 0, 0, 0);
+    }
+  }
+  const int lim = min(L - 1, last_ok) - tok0 - 4 * q4;
+  float mx = kNegInf;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = (16 * tt + i <= lim) ? s[tt][i] * scale_log2 : kNegInf;
+      s[tt][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max4lanes(mx);
+  const bool grow = mx > m_run + kRescaleSlack;
+  const bool had = m_run != kNegInf;
+  const float alpha = (grow && had) ? fast_exp2(m_run - mx) : 1.f;
+  const bool rescaled = grow && had;
+  l_run *= alpha;
+  m_run = grow ? mx : m_run;
+  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+  bf16x8 pv;
+  float psum = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(s[tt][i] - m_use);
+      psum += e;
+      pv[4 * tt + i] = static_cast<__bf16>(e);
+    }
+  l_run += psum;
+  const int row = 16 * wave + r16;
+  *reinterpret_cast<bf16x8*>(lds + X::kP + par * X::kPBytes + xrow_off(row, q4)) = pv;
+  if (q4 == 0) reinterpret_cast<float*>(lds + X::kAlpha)[par * X::kRows + row] = alpha;
+  if (ln.lane == 0 && __builtin_amdgcn_ballot_w64(rescaled) != 0)
+    reinterpret_cast<int*>(lds + X::kFlag)[par] = unit_id;
+}
+
+// PV phase of one unit (parity `par`): O^T[dims 64 w + 16 dd + 4 q4 + i][rows 16 rr + r16].
+__device__ __forceinline__ void x1_pv(const uint8_t* __restrict__ page, uint8_t* __restrict__ work, const XLane& ln,
+                                      int par, int unit_id, f32x4 (&acc)[4][8]) {
+  using X = X1Layout;
+  const int wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+  uint8_t* const lds = work - X::kP;
+  {
+    // the flag word is read in inline asm (waited inside the block): the
+    // compiler cannot tell that this fixed LDS address is not a target of the
+    // direct loads in flight and would otherwise wait for all of them
+    int fl;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(fl)
+                 : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + X::kFlag + 4 * par)))
+                 : "memory");
+    if (__builtin_amdgcn_readfirstlane(fl) == unit_id) {
+      const float* alpha_buf = reinterpret_cast<const float*>(lds + X::kAlpha) + par * X::kRows;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const float a = alpha_buf[16 * rr + r16];
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) acc[dd][rr] *= a;
+      }
+    }
+  }
+  bf16x8 va[4];
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd) {
+    const uint8_t* a0 = page + ln.v_off[dd] + 4096 * wave;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * 128));
+    va[dd] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  const uint8_t* pbuf = lds + X::kP + par * X::kPBytes;
+  bf16x8 pb[2];
+  pb[0] = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(r16, q4));
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    if (rr + 1 < 8) pb[(rr + 1) & 1] = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(16 * (rr + 1) + r16, q4));
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+      acc[dd][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dd], pb[rr & 1], acc[dd][rr], 0, 0, 0);
+  }
+}
+
+__global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
+  using X = X1Layout;
+  constexpr int M_TILE = X::kRows;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[X::kTotal];
+
+  XLane ln;
+  ln.tid = threadIdx.x;
+  ln.lane = ln.tid & 63;
+  ln.wave = __builtin_amdgcn_readfirstlane(ln.tid >> 6);
+  ln.r16 = ln.lane & 15;
+  ln.q4 = ln.lane >> 4;
+  {
+    ln.k_off[0] = xk_off(ln.r16, ln.q4);
+    ln.k_off[1] = xk_off(ln.r16, 4 + ln.q4);
+    const int tok = 4 * ln.q4 + (ln.r16 >> 2);
+    const int hh = (ln.r16 & 3) >> 1, half8 = ln.r16 & 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ln.v_off[e] = xk_off(tok, 2 * e + hh) + 8 * half8;
+  }
+  const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+  const int st = static_cast<int>(p.kv_st);
+  const uint32_t ld_off = x_load_off<kFmtBf16>(0, ln.lane, st);
+
+  const int per_xcd = gridDim.x / 8;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= p.grid_wgs) return;
+  const int m_tiles = (p.rows + M_TILE - 1) / M_TILE;
+  const int mt = logical % m_tiles;
+  const int kvh = (logical / m_tiles) % p.h_kv;
+  const int part = logical / (m_tiles * p.h_kv);
+
+  Range r;
+  {
+    const int32_t* meta = p.meta + part * kMetaInts;
+    r.begin_b = ld_meta(meta + 0);
+    r.begin_page = ld_meta(meta + 1);
+    r.end_b = min(ld_meta(meta + 2), p.batch - 1);
+    r.end_page = ld_meta(meta + 3);
+    r.split0 = ld_meta(meta + 4);
+  }
+  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
+
+  if (tid < 2) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
+
+  const int srow = mt * M_TILE + 16 * wave + r16;
+  const bool srow_ok = srow < p.rows;
+  const int s_idx = srow_ok ? srow / p.group : 0;
+  const int shead = kvh * p.group + (srow_ok ? srow % p.group : 0);
+
+  const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
+  uint32_t win_lo = 0, win_hi = 0;
+  int win_b = -1, win_pi = 0;
+  const int64_t half_bytes = static_cast<int64_t>(kXHalf) * st;
+  auto unit_src = [&](const XUnit& u) -> const uint8_t* {
+    if (u.b != win_b || u.pi < win_pi || u.pi >= win_pi + 64) {
+      win_b = u.b;
+      win_pi = u.pi;
+      const int e = u.pi + ln.lane;
+      const int pg = e < p.max_blocks ? p.block_table[static_cast<int64_t>(u.b) * p.bt_stride + e] : -1;
+      const uint64_t a = (pg >= 0 && pg < p.num_pages)
+                             ? reinterpret_cast<uint64_t>(kv_head + static_cast<int64_t>(pg) * p.kv_sp)
+                             : 0ull;
+      win_lo = static_cast<uint32_t>(a);
+      win_hi = static_cast<uint32_t>(a >> 32);
+      wait_vm_all();
+    }
+    const uint32_t lo = __builtin_amdgcn_readlane(win_lo, u.pi - win_pi);
+    const uint32_t hi = __builtin_amdgcn_readlane(win_hi, u.pi - win_pi);
+    const uint64_t a = (static_cast<uint64_t>(hi) << 32) | lo;
+    if (a == 0) return nullptr;
+    return reinterpret_cast<const uint8_t*>(a) + (u.hf ? half_bytes : 0);
+  };
+  auto unit_valid = [&](const XUnit& u) { return min(u.L - (u.pi * kPage + u.hf * kXHalf), kXHalf); };
+
+  // ---- prime the ring: units 0 and 1 into slots 0 and 1 ---------------------------------
+  XUnit uq[2];
+  bool okq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i == 0)
+      uq[0] = x_seek(p, r, r.begin_b);
+    else
+      uq[1] = (uq[0].b <= r.end_b) ? x_next(p, r, uq[0]) : uq[0];
+    okq[i] = true;
+    if (uq[i].b <= r.end_b) {
+      const uint8_t* src = unit_src(uq[i]);
+      okq[i] = src != nullptr;
+      if (okq[i] && wave < kLoadWaves) x1_issue(src, unit_valid(uq[i]), lds + X::kRing + i * X::kSlot, wave, ld_off, st);
+    }
+  }
+  int slot = 0;
+  int unit_id = 0;
+  uint8_t* const work = lds + X::kP;
+
+  for (int b = r.begin_b; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    seq_pages(p, r, b, L, pg0, pg1);
+    const int split_idx = (b == r.begin_b) ? r.split0 : 0;
+    const int slot0 = ld_meta(p.num_splits + b);
+    const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
+    const int last_ok = p.causal ? (L - p.s_q + s_idx) : (L - 1);
+
+    bf16x8 qf[X::kRegChunks];
+    {
+      const uint16_t* qrow = p.q + b * p.q_sb + s_idx * p.q_ss + shead * p.q_sh;
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        if (X::qslot(c) >= 0) continue;
+        const u32x4 v = srow_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+        qf[X::qreg(c)] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    lds_barrier_keep_loads();                 // no wave still reads the previous sequence's Q^T chunks
+    {
+      const uint16_t* qb = p.q + b * p.q_sb;
+      const int q_bytes = 2 * static_cast<int>((p.s_q - 1) * p.q_ss + (p.h_q - 1) * p.q_sh + kDqk);
+      const __amdgpu_buffer_rsrc_t qrsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qb), 0, q_bytes, kRawBufferWord3);
+      const int lrow = ln.lane >> 2, pslot = ln.lane & 3;
+#pragma unroll
+      for (int j = 0; j < (X::kQChunks * 8 + kWW - 1) / kWW; ++j) {
+        const int k = wave + kWW * j;
+        if (k < X::kQChunks * 8) {
+          const int qs = k >> 3, i = k & 7;
+          const int row = 16 * i + lrow;
+          const int sl = pslot ^ ((row >> 1) & 3);
+          const int grow = mt * M_TILE + row;
+          uint32_t off = 0xFFFFFFF0u;
+          if (grow < p.rows) {
+            const int sg = grow / p.group, hg = kvh * p.group + grow % p.group;
+            off = static_cast<uint32_t>(2 * (sg * p.q_ss + hg * p.q_sh + 32 * X::qchunk(qs) + 8 * sl));
+          }
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, LDS_PTR(void, lds + X::kQ + qs * X::kQChunkBytes + 1024 * i),
+                                                   16, off, 0, 0, 0);
+        }
+      }
+    }
+    wait_vm_all();                            // Q, and every unit in flight, landed
+    lds_barrier();
+
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+
+    // Invariant at the top: unit uq[0] is in LDS and visible to every wave,
+    // the loads of uq[1] (if any) are in flight or landed.
+    while (uq[0].b == b) {
+      const XUnit u = uq[0];
+      bad |= !okq[0];
+      const int par = unit_id & 1;
+      uint8_t* const cur = lds + X::kRing + slot * X::kSlot;
+      const int tok0 = u.pi * kPage + u.hf * kXHalf;
+      x1_s(cur, work, ln, par, L, last_ok, tok0, p.scale_log2, unit_id, qf, m_run, l_run);
+      wait_vm_all();                          // this wave's loads of uq[1] landed
+      lds_barrier_keep_loads();               // P^T of u and uq[1] visible; every wave is past PV of u - 1
+      const XUnit un = (uq[1].b <= r.end_b) ? x_next(p, r, uq[1]) : uq[1];
+      bool ok_n = true;
+      if (un.b <= r.end_b) {
+        const uint8_t* src_n = unit_src(un);
+        ok_n = src_n != nullptr;
+        // the slot of u - 1: its last reader was PV of u - 1, before this barrier
+        if (ok_n && wave < kLoadWaves)
+          x1_issue(src_n, unit_valid(un), lds + X::kRing + ((slot + 2) % 3) * X::kSlot, wave, ld_off, st);
+      }
+      x1_pv(cur, work, ln, par, unit_id, acc);
+      ++unit_id;
+      slot = (slot + 1) % 3;
+      uq[0] = uq[1];
+      okq[0] = okq[1];
+      uq[1] = un;
+      okq[1] = ok_n;
+    }
+
+    // ---- epilogue: l of every row through LDS; each wave writes its 64 dims ----
+    lds_barrier_keep_loads();                 // every wave's PV is done: the P^T buffers are free
+    float* lrow = reinterpret_cast<float*>(lds + X::kP);
+    {
+      const float l_tot = sum4lanes(l_run);
+      if (q4 == 0) lrow[16 * wave + r16] = l_tot;
+      if (q4 == 0 && srow_ok) {
+        float lse = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+        if (bad) lse = __builtin_nanf("");
+        if (nsplit == 1)
+          p.lse[(static_cast<int64_t>(b) * p.h_q + shead) * p.s_q + s_idx] = lse;
+        else if (slot0 + split_idx < p.max_slots && split_idx < nsplit)
+          p.part_lse[(static_cast<int64_t>(slot0 + split_idx) * p.h_kv + kvh) * p.rows + srow] = lse;
+      }
+    }
+    lds_barrier_keep_loads();
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int row = mt * M_TILE + 16 * rr + r16;
+      if (row >= p.rows) continue;
+      const float l_row = lrow[16 * rr + r16];
+      const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
+      const int si = row / p.group, hh = kvh * p.group + row % p.group;
+      if (nsplit == 1) {
+        uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + si) * p.h_q + hh) * kDv + 64 * wave + 4 * q4;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = bad ? nan : acc[dd][rr][i] * inv;
+          u32x2 w;
+          w[0] = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+          w[1] = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+          *reinterpret_cast<u32x2*>(orow + 16 * dd) = w;
+        }
+      } else {
+        const int pslot = slot0 + split_idx;
+        if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
+          float* prow = p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv +
+                        64 * wave + 4 * q4;
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = bad ? nan : acc[dd][rr][i] * inv;
+            *reinterpret_cast<f32x4*>(prow + 16 * dd) = v;
+          }
+        }
+      }
+    }
+  }
+  wait_vm_all();
+}
+
 }  // namespace
 
 hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wave, int grid, hipStream_t stream,
@@ -671,7 +1072,7 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
   if (kv_format == kFmtFp8)
     hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
   else
-    hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtBf16>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL(splitkv_x1_kernel, g, blk, 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 
