@@ -171,7 +171,7 @@ def pmc_summary(args) -> str:
     counters read for the calibration copy of known size."""
     from workloads import named_workload
     w = named_workload(args.workload)
-    split_name = "splitkv_x_kernel" if w.heads_per_kv > 64 else "splitkv_kernel"
+    split_name = split_kernel_name(w)
     is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
     is_copy = lambda n: "elementwise" in n and "Mul" in n
     fr, wr = _pmc_rows(args.pmc_summary[0]), _pmc_rows(args.pmc_summary[1])
@@ -207,6 +207,14 @@ def pmc_summary(args) -> str:
         f"traffic_over_algorithmic: {(fetch + write) / byts:.3f}",
     ]
     return "\n".join(lines) + "\n"
+
+
+def split_kernel_name(w) -> str:
+    """Name of the split kernel a workload runs (128-row tiles above 64 rows per KV head:
+    the one-barrier kernel for bf16 pages, the two-barrier one for FP8)."""
+    if w.heads_per_kv > 64:
+        return "splitkv_x1_kernel" if w.kv_format == "bf16" else "splitkv_x_kernel"
+    return "splitkv_kernel"
 
 
 def percentiles(xs, ps):
@@ -334,7 +342,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(split_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(split_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
 
-    split_name = "splitkv_x_kernel" if w.heads_per_kv > 64 else "splitkv_kernel"
+    split_name = split_kernel_name(w)
     roof["traffic"] = stored_traffic(split_name, w.name)
 
     result = {

@@ -27,8 +27,9 @@ using namespace dev;
 //
 // Each workgroup covers 128 query rows with 8 wavefronts, two per SIMD, so
 // one wave's LDS waits, softmax and barrier waits overlap the other's MFMA
-// work. Work advances in units of 32 tokens (half a page) through a two-slot
-// LDS ring (the unit after the current one is in flight):
+// work. Work advances in units of 32 tokens (half a page); the phases below
+// are shared by both kernels (FP8 pages: a two-slot ring of raw records and
+// two barriers per unit; bf16 pages: a three-slot ring and one barrier):
 //   S phase  -- wave w owns rows 16w .. 16w + 15: S^T = K Q^T on MFMA
 //               16x16x32 bf16 (A = 16 tokens x 32 dims of K from LDS,
 //               B = Q^T); 9 of the 18 32-dim Q chunks stay in VGPRs, 9 in LDS.
@@ -38,7 +39,7 @@ using namespace dev;
 //               128 rows (128 accumulator registers): it reads only its
 //               eighth of V (transposed) and every wave's P^T.
 // FP8 pages (656-byte records) stream raw into the ring; one LDS pass per
-// unit turns the e4m3 codes into bf16 exactly (4 significant bits fit in 8)
+// unit (and one more barrier) turns the e4m3 codes into bf16 exactly (4 significant bits fit in 8)
 // and copies RoPE and the 4 per-128-dim scales. The S phase applies the fp32
 // scales to the per-group partial logits; in the PV phase wave w's dims lie
 // in scale group w / 2, so it multiplies its P^T operand by that group's
@@ -52,29 +53,27 @@ constexpr int kXHalf = 32;                                  // tokens per unit
 constexpr int kXHalfBytes = kXHalf * kRowBytes;             // 36864 = 36 x 1 KB: bf16 rows
 constexpr int kXRawBytes = kXHalf * kFp8Record;             // 20992: FP8 records
 
-// LDS layout (bytes): the ring of 32-token units (bf16 rows, or raw FP8
-// records); FP8 only: the converted unit (bf16 rows, the bf16 ring layout)
-// and the scales [4 groups][32 tokens]; then P^T, rescale factors, flags, and
-// the Q^T chunks kept in LDS for all 128 rows (chunks 0 .. 6, 16, 17; the
-// other chunks of each row stay in VGPRs).
-template <int FMT>
+// LDS layout of the FP8 kernel (bytes): the two-slot ring of raw 32-record
+// units; the converted unit (bf16 rows, the chunk-group-major layout below)
+// and the scales [4 groups][32 tokens]; then P^T, rescale factors, the flag
+// word, and the Q^T chunks kept in LDS for all 128 rows (chunks 0 .. 6, 16,
+// 17; the other chunks of each row stay in VGPRs).
 struct XLayout {
-  static constexpr bool kFp8 = (FMT == kFmtFp8);
   static constexpr int kRows = 128;                         // rows per tile
-  static constexpr int kSlot = kFp8 ? 21 * 1024 : kXHalfBytes;
+  static constexpr int kSlot = 21 * 1024;
   static constexpr int kSlots = 2;
   static constexpr int kRing = 0;
   static constexpr int kConv = kRing + kSlots * kSlot;
-  static constexpr int kScale = kConv + (kFp8 ? kXHalfBytes : 0);
-  static constexpr int kP = kScale + (kFp8 ? 4 * kXHalf * 4 : 0);
+  static constexpr int kScale = kConv + kXHalfBytes;
+  static constexpr int kP = kScale + 4 * kXHalf * 4;
   static constexpr int kAlpha = kP + kRows * kXHalf * 2;    // P^T: [rows][32 tokens] bf16
   static constexpr int kFlag = kAlpha + kRows * 4;          // alpha: [rows] fp32
   static constexpr int kQ = kFlag + 64;                     // rescale flag word (64 bytes reserved)
   static constexpr int kQChunks = 9;
   static constexpr int kQChunkBytes = kRows * 64;           // one 32-dim Q^T chunk of all rows
   static constexpr int kTotal = kQ + kQChunks * kQChunkBytes;
-  static constexpr int kLoads = kFp8 ? 21 : kXHalfBytes / 1024;   // 1 KB direct loads per unit (36 / 21)
-  static constexpr int kLoadsPerWave = (kLoads + kLoadWaves - 1) / kLoadWaves;   // 9 / 6
+  static constexpr int kLoads = 21;                         // 1 KB direct loads per unit
+  static constexpr int kLoadsPerWave = (kLoads + kLoadWaves - 1) / kLoadWaves;   // 6
   static constexpr int kLow = 7;                            // chunks 0 .. 6 in LDS, then 16, 17
   // LDS slot of Q^T chunk c, or -1 when it lives in VGPRs
   static constexpr int qslot(int c) { return c < kLow ? c : (c >= 16 ? c - 16 + kLow : -1); }
@@ -84,9 +83,8 @@ struct XLayout {
   // LDS chunk index qs -> Q chunk
   static constexpr int qchunk(int qs) { return qs < kLow ? qs : 16 - kLow + qs; }
 };
-static_assert(XLayout<kFmtBf16>::kTotal <= 163840 && XLayout<kFmtFp8>::kTotal <= 163840, "LDS budget");
-static_assert(XLayout<kFmtBf16>::kLoads % kLoadWaves == 0, "equal direct-load counts per wave (bf16)");
-static_assert(XLayout<kFmtFp8>::kSlot >= kXRawBytes, "FP8 slot holds a unit");
+static_assert(XLayout::kTotal <= 163840, "LDS budget");
+static_assert(XLayout::kSlot >= kXRawBytes, "FP8 slot holds a unit");
 
 // Q^T chunks and P^T rows in LDS: 64 bytes per row (4 x 16 B); the 16-byte
 // slot is XOR-swizzled with (row >> 1) & 3 so 8 consecutive rows hit 8
@@ -150,31 +148,22 @@ __device__ __forceinline__ uint32_t x_load_off(int k, int lane, int st) {
 // Buffer resource word 3 for raw (unformatted, stride 0) buffer access on gfx9-family GPUs.
 constexpr int kRawBufferWord3 = 0x00020000;
 
-// Issue the direct loads of one unit (32 tokens starting at `src`, token stride
-// `st`) into `dst` (waves 0 .. 3 issue them): MUBUF loads to LDS
+// Issue the direct loads of one FP8 unit (32 records starting at `src`, token
+// stride `st`) into `dst` (waves 0 .. 3 issue them): MUBUF loads to LDS
 // (buffer_load_dwordx4 ... lds), 16 bytes per lane, with the unit as the
-// buffer (offsets past its 32 rows read zeros). The buffer form keeps the LDS
-// read waits of the compute phases partial (the FLAT form makes every LDS
+// buffer (the part of the last load past the 32 records reads zeros). Load k
+// brings LDS bytes 1024 k .. + 1023 of the records. The buffer form keeps the
+// LDS read waits of the compute phases partial (the FLAT form makes every LDS
 // wait a full drain while a load is in flight).
-// bf16: load k = 4 g + w (wave w issues the loads of token block w) brings
-// tokens 8 w .. 8 w + 7 of column block g; FP8: load k brings LDS bytes
-// 1024 k .. + 1023 of the 32 records.
-template <int FMT>
 __device__ __forceinline__ void x_issue(const uint8_t* src, uint8_t* dst, int wave, const uint32_t (&off)[6], int st) {
-  using X = XLayout<FMT>;
+  using X = XLayout;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), 0, kXHalf * st, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < X::kLoadsPerWave; ++j) {
     const int k = wave + kLoadWaves * j;
-    if constexpr (FMT == kFmtFp8) {
-      if (k < X::kLoads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0,
-                                                 kPageLoadPolicy);
-    } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[0], 8 * wave * st + 128 * j,
-                                               0, kPageLoadPolicy);
-    }
+    if (k < X::kLoads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, off[j], 0, 0, kPageLoadPolicy);
   }
 }
 
@@ -186,30 +175,28 @@ struct XLane {
   int r16, q4;          // lane % 16, lane / 16
   int k_off[2];         // S phase: K row r16, logical chunks q4 and 4 + q4 (swizzled), bytes
   int v_off[4];         // PV phase: transposed V read offsets, by 16-dim block d & 3
-  uint32_t ld_off[6];   // direct loads: per-lane source offsets (bf16 uses [0] only)
+  uint32_t ld_off[6];   // FP8 direct loads: per-lane source offset of each load
 };
 
-// One unit of the pipeline. `cur` holds the unit (32 bf16 rows, or 32 FP8
-// records), `nxt` receives the next unit, `work` is the LDS after the ring
-// (FP8 conversion buffers, P^T, rescale factors, flags, Q^T chunks). The
-// regions are disjoint; the restrict qualifiers let the compiler see that the
-// LDS reads of this unit never touch the direct loads in flight into `nxt`.
-template <int FMT>
+// One unit of the FP8 pipeline. `cur` holds the unit (32 FP8 records), `nxt`
+// receives the next unit, `work` is the LDS after the ring (conversion
+// buffers, P^T, rescale factors, flag, Q^T chunks). The regions are disjoint;
+// the restrict qualifiers let the compiler see that the LDS reads of this
+// unit never touch the direct loads in flight into `nxt`.
 __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
                                        uint8_t* __restrict__ work, const uint8_t* next_src, int st, const XLane& ln,
                                        int L, int last_ok, int tok0, int valid, bool this_ok, float scale_log2,
-                                       int unit_id, const bf16x8 (&qf)[XLayout<FMT>::kRegChunks], f32x4 (&acc)[4][8],
+                                       int unit_id, const bf16x8 (&qf)[XLayout::kRegChunks], f32x4 (&acc)[4][8],
                                        float& m_run, float& l_run) {
-  using X = XLayout<FMT>;
-  constexpr bool kFp8 = X::kFp8;
+  using X = XLayout;
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   uint8_t* const lds = work - X::kConv;
-  const float* sct = reinterpret_cast<const float*>(lds + X::kScale);   // FP8: [group][token] scales
+  const float* sct = reinterpret_cast<const float*>(lds + X::kScale);   // [group][token] scales
 
-  // ---- stage the unit: FP8 conversion, or zero the bf16 rows past the end --------------
-  uint8_t* page;                                  // bf16 rows (chunk-group-major, swizzled)
-  if constexpr (kFp8) {
-    uint8_t* conv = lds + X::kConv;
+  // ---- stage the unit: codes -> bf16 rows, RoPE and scales copied; rows past the end -> 0 --
+  uint8_t* const page = lds + X::kConv;           // bf16 rows (chunk-group-major, swizzled)
+  {
+    uint8_t* conv = page;
     float* scw = reinterpret_cast<float*>(lds + X::kScale);
     if (tid < 4 * kXHalf) {
       const int g = tid >> 5, t = tid & 31;
@@ -247,21 +234,10 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
       *reinterpret_cast<u32x4*>(conv + xk_off(t, 64 + rr)) = w;
     }
     lds_barrier_keep_loads();
-    page = conv;
-  } else {
-    if (valid < kXHalf || !this_ok) {
-      const int z0 = this_ok ? valid : 0;
-      for (int idx = tid; idx < 72 * kXHalf; idx += kWThreads) {  // 16-byte chunks of the unit
-        const int t = (idx >> 3) & 31;                            // block idx / 256, token, chunk idx % 8
-        if (t >= z0) *reinterpret_cast<u32x4*>(cur + 4096 * (idx >> 8) + 128 * t + 16 * (idx & 7)) = u32x4{0u, 0u, 0u, 0u};
-      }
-      lds_barrier_keep_loads();
-    }
-    page = cur;
   }
 
   // ---- the next unit -> nxt (waves 0 .. 3) ------------------------------------------------
-  if (next_src != nullptr && wave < kLoadWaves) x_issue<FMT>(next_src, nxt, wave, ln.ld_off, st);
+  if (next_src != nullptr && wave < kLoadWaves) x_issue(next_src, nxt, wave, ln.ld_off, st);
 
   // ---- S phase: S^T[token 16 tt + 4 q4 + i][row 16 w + r16] --------------------------------
   const uint8_t* qlds = lds + X::kQ;
@@ -278,9 +254,9 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   f32x4 s[2];                                     // [token tile]
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // chunk order: bf16 0..17; FP8 the RoPE chunks 16, 17 first (unscaled), then
-  // the 4 latent groups of 4 chunks, each group's partial logits scaled and added
-  auto corder = [](int i) { return kFp8 ? (i < 2 ? 16 + i : i - 2) : i; };
+  // chunk order: the RoPE chunks 16, 17 first (unscaled), then the 4 latent
+  // groups of 4 chunks, each group's partial logits scaled and added
+  auto corder = [](int i) { return i < 2 ? 16 + i : i - 2; };
   // (padding rows of the last tile run through the phases like real rows: their
   // Q^T is zero and nothing of theirs is written)
   {
@@ -298,7 +274,7 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
         qbuf[(i + 1) & 1] = qop(corder(i + 1));
       }
       const bf16x8 qv = qbuf[i & 1];
-      if (!kFp8 || i < 2) {
+      if (i < 2) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i & 1][tt], qv, s[tt], 0, 0, 0);
       } else {
@@ -399,19 +375,14 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * 128));
     va[dd] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  f32x4 sa, sb;
-  if constexpr (kFp8) {
-    // this wave's dims are scale group w / 2: the per-token scales of its
-    // k-slot tokens (4 q4 + 0..3, 16 + 4 q4 + 0..3) are folded into P^T
-    sa = *reinterpret_cast<const f32x4*>(sct + (wave >> 1) * kXHalf + 4 * q4);
-    sb = *reinterpret_cast<const f32x4*>(sct + (wave >> 1) * kXHalf + 16 + 4 * q4);
-  }
+  // this wave's dims are scale group w / 2: the per-token scales of its
+  // k-slot tokens (4 q4 + 0..3, 16 + 4 q4 + 0..3) are folded into P^T
+  const f32x4 sa = *reinterpret_cast<const f32x4*>(sct + (wave >> 1) * kXHalf + 4 * q4);
+  const f32x4 sb = *reinterpret_cast<const f32x4*>(sct + (wave >> 1) * kXHalf + 16 + 4 * q4);
   auto pload = [&](int rr) -> bf16x8 {
     bf16x8 pb = *reinterpret_cast<const bf16x8*>(pbuf + xrow_off(16 * rr + r16, q4));
-    if constexpr (kFp8) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(static_cast<float>(pb[e]) * (e < 4 ? sa[e] : sb[e - 4]));
-    }
+    for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(static_cast<float>(pb[e]) * (e < 4 ? sa[e] : sb[e - 4]));
     return pb;
   };
   bf16x8 pb[2];
@@ -425,9 +396,8 @@ __device__ __forceinline__ void x_step(uint8_t* __restrict__ cur, uint8_t* __res
   }
 }
 
-template <int FMT>
 __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
-  using X = XLayout<FMT>;
+  using X = XLayout;
   constexpr int M_TILE = X::kRows;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[X::kTotal];
 
@@ -452,8 +422,8 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   const int st = static_cast<int>(p.kv_st);
 #pragma unroll
-  for (int j = 0; j < (X::kFp8 ? X::kLoadsPerWave : 1); ++j)
-    ln.ld_off[j] = x_load_off<FMT>((wave & (kLoadWaves - 1)) + kLoadWaves * j, ln.lane, st);
+  for (int j = 0; j < X::kLoadsPerWave; ++j)
+    ln.ld_off[j] = x_load_off<kFmtFp8>((wave & (kLoadWaves - 1)) + kLoadWaves * j, ln.lane, st);
 
   // XCD-aware order: consecutive logical workgroups share an XCD (and its L2)
   const int per_xcd = gridDim.x / 8;
@@ -521,7 +491,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
   if (uq.b <= r.end_b) {
     const uint8_t* src = unit_src(uq);
     okq = src != nullptr;
-    if (okq && wave < kLoadWaves) x_issue<FMT>(src, lds + X::kRing, wave, ln.ld_off, st);
+    if (okq && wave < kLoadWaves) x_issue(src, lds + X::kRing, wave, ln.ld_off, st);
   }
   int slot = 0;
   int unit_id = 0;
@@ -601,7 +571,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
       }
       const int tok0 = u.pi * kPage + u.hf * kXHalf;
       const int valid = min(L - tok0, kXHalf);
-      x_step<FMT>(lds + X::kRing + slot * X::kSlot, lds + X::kRing + (slot ^ 1) * X::kSlot, lds + X::kConv, src_n, st,
+      x_step(lds + X::kRing + slot * X::kSlot, lds + X::kRing + (slot ^ 1) * X::kSlot, lds + X::kConv, src_n, st,
                   ln, L, last_ok, tok0, valid, this_ok, p.scale_log2, unit_id, qf, acc, m_run, l_run);
       ++unit_id;
       slot ^= 1;
@@ -1070,7 +1040,7 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
   if (rows_per_wave != 32) return hipErrorInvalidValue;
   const dim3 g(grid), blk(kWThreads);
   if (kv_format == kFmtFp8)
-    hipExtLaunchKernelGGL((splitkv_x_kernel<kFmtFp8>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL(splitkv_x_kernel, g, blk, 0, stream, ev_start, ev_stop, 0, p);
   else
     hipExtLaunchKernelGGL(splitkv_x1_kernel, g, blk, 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
