@@ -229,6 +229,56 @@ def pmc_summary(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+SIMDS = 256 * 4
+XCDS = 8
+
+
+def mfma_summary(args) -> str:
+    """MFMA utilisation of the split kernel from one rocprofv3 --pmc run with MFMA_COUNTERS:
+    matrix-core busy cycles summed over the SIMDs / (GPU-active cycles x SIMDs), and the bf16 MFMA
+    work the counters saw against the algorithmic FLOPs. rocprofv3 reports GRBM_GUI_ACTIVE summed
+    over the 8 XCDs (each has its own); the per-dispatch medians are used (the first dispatch of a
+    run is cold)."""
+    from workloads import named_workload
+    w = named_workload(args.workload)
+    split_name = split_kernel_name(w)
+    is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
+    rows = _pmc_rows(args.mfma_summary)
+    busy = _per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", is_split)
+    mops = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16", is_split)
+    gui = _per_dispatch(rows, "GRBM_GUI_ACTIVE", is_split)
+    if not (busy and mops and gui):
+        raise SystemExit("missing split-kernel dispatches or MFMA counters in the counter files")
+    med = lambda xs: percentiles(xs, (50,))[0]
+    _, flops, _ = algorithmic_work(w)
+    active = med(gui) / XCDS
+    dur_ns = {}
+    for r in rows:
+        if is_split(r["Kernel_Name"]):
+            dur_ns[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    dur_us = med(list(dur_ns.values())) / 1e3
+    util = med(busy) / (active * SIMDS)
+    mfma_flops = med(mops) * 512.0
+    lines = [
+        f"# MFMA utilisation of {split_name} on workload {w.name} (rocprofv3 --pmc)",
+        f"kernel: {split_name}",
+        f"workload: {w.name}",
+        f"source_sha256: {source_sha256()}",
+        f"counters: {MFMA_COUNTERS}",
+        f"split_dispatches: {len(busy)}",
+        f"mfma_busy_cycles_per_dispatch (sum over {SIMDS} SIMDs): {med(busy):.0f}",
+        f"gpu_active_cycles_per_dispatch (GRBM_GUI_ACTIVE / {XCDS} XCDs): {active:.0f}",
+        f"mfma_util (busy / (active x {SIMDS})): {util:.4f}",
+        f"dispatch_duration_us (counter-run timestamps): {dur_us:.1f}",
+        f"implied_clock_ghz (active cycles / duration): {active / (dur_us * 1e3):.2f}",
+        f"bf16_mfma_flops_per_dispatch (MOPS x 512): {mfma_flops:.4e}",
+        f"algorithmic_flops_per_step: {flops:.4e}",
+        f"mfma_flops_over_algorithmic: {mfma_flops / flops:.3f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def split_kernel_name(w) -> str:
     """Name of the split kernel a workload runs (128-row tiles above 64 rows per KV head:
     the one-barrier kernel for bf16 pages, the two-barrier one for FP8)."""
@@ -258,9 +308,15 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench made with --calibrate-copy-mb, and print the traffic summary")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="no GPU run: summarise one rocprofv3 --pmc run of this bench with the counters "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(args), end="")
+        return
+    if args.mfma_summary:
+        print(mfma_summary(args), end="")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
