@@ -75,6 +75,14 @@ constexpr int kPageLoadPolicy = 2;
 // so the compiler's own wait-count tracking sees it.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (vmcnt, 6 bits on gfx950: low 4 in bits 3:0, high 2 in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Lane l and lane l ^ 32 (v_permlane32_swap: the pair it returns holds, in
 // every lane, the value of that lane and of its partner across the halves).
 __device__ __forceinline__ void pair32(float v, float& a, float& b) {

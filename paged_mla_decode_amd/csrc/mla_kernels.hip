@@ -413,14 +413,22 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     return kv_head + static_cast<int64_t>(pg) * p.kv_sp;
   };
 
-  // ---- pipeline: the page in flight always targets ring slot `slot` ------------
-  // (nb1, npi1) is the page after it, with its source src1 looked up one page
-  // early, so its loads are issued right after the barrier that frees the
-  // other slot.
+  // ---- pipeline: two pages in flight ------------------------------------------------
+  // q0 is the page computed next (ring slot `slot`), q1 the one after it (slot ^ 1).
+  // q1's loads go out as soon as its slot is free -- right after the barrier that
+  // ends the compute of the page before -- so q1 streams in while q0 lands; q0 is
+  // then waited with a count that leaves this wave's loads of q1 in flight (vmcnt
+  // falls in issue order). (nb2, npi2, src2) is the page after q1, looked up one
+  // page early so no lookup sits in front of an issue. At the last page of a
+  // sequence whose token groups are merged through LDS, the page after q1 is held
+  // back (its slot is the merge scratch) and issued when the next sequence starts.
+  constexpr bool kMergeScratch = (TG > 1) && !kFp8;
   int slot = 0;
-  bool load_ok = true;
-  int nb1 = r.end_b + 1, npi1 = 0;
-  const uint8_t* src1 = nullptr;
+  bool q0_ok = true, q1_ok = true;
+  int q1_state = 0;                  // 0: no page, 1: loads issued (none if !q1_ok), 2: held back
+  const uint8_t* q1_src = nullptr;
+  int nb2 = r.end_b + 1, npi2 = 0;
+  const uint8_t* src2 = nullptr;
   // the page after (b_, pi_) inside the range (b_ > r.end_b: none); e_ = end page of b_ if known (else -1)
   auto advance = [&](int b_, int pi_, int e_, int& nb, int& npi) {
     if (e_ < 0) {
@@ -434,15 +442,42 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       next_with_pages(p, r, b_ + 1, nb, npi);
     }
   };
+  // wait until q0 has landed, leaving this wave's loads of q1 (issued after q0's) in flight
+  auto wait_q0 = [&]() {
+    if (q1_state == 1 && q1_ok) {
+      if constexpr (kLoads % kWaves == 0) {
+        wait_vmcnt<kLoads / kWaves>();
+      } else {
+        if (wave < kLoads % kWaves)
+          wait_vmcnt<kLoads / kWaves + 1>();
+        else
+          wait_vmcnt<kLoads / kWaves>();
+      }
+    } else {
+      wait_vm_all();
+    }
+  };
   {
     int nb, npi;
     next_with_pages(p, r, r.begin_b, nb, npi);
     if (nb <= r.end_b) {
       const uint8_t* src = page_src(nb, npi);
-      load_ok = src != nullptr;
-      if (load_ok) issue_page<FMT>(src, page_extent, ring, ld_off, wave);
+      q0_ok = src != nullptr;
+      if (q0_ok) issue_page<FMT>(src, page_extent, ring, ld_off, wave);
+      int nb1, npi1;
       advance(nb, npi, -1, nb1, npi1);
-      if (nb1 <= r.end_b) src1 = page_src(nb1, npi1);
+      if (nb1 <= r.end_b) {
+        q1_src = page_src(nb1, npi1);
+        q1_ok = q1_src != nullptr;
+        if (kMergeScratch && nb != r.begin_b) {
+          q1_state = 2;                // sequences with no pages come first: their merges use slot 1
+        } else {
+          if (q1_ok) issue_page<FMT>(q1_src, page_extent, ring + kSlotBytes, ld_off, wave);
+          q1_state = 1;
+        }
+        advance(nb1, npi1, -1, nb2, npi2);
+        if (nb2 <= r.end_b) src2 = page_src(nb2, npi2);
+      }
     }
   }
 
@@ -467,6 +502,12 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       // would wait on every load in flight, the next page's included.
       wait_vm_all();
     }
+    // a page held back at the end of an earlier sequence: its slot is free again (the merge is
+    // done). Not for a sequence with no pages here: its merge still uses that slot.
+    if (q1_state == 2 && pg0 < pg1) {
+      if (q1_ok) issue_page<FMT>(q1_src, page_extent, ring + (slot ^ 1) * kSlotBytes, ld_off, wave);
+      q1_state = 1;
+    }
 
     float m_run = kNegInf, l_run = 0.f;
     f32x4 acc[32];
@@ -475,23 +516,33 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     bool bad = false;
 
     for (int pi = pg0; pi < pg1; ++pi) {
-      // page (b, pi) is in flight into `slot`
-      const bool this_ok = load_ok;
+      // page (b, pi) = q0 is in flight into `slot`, q1 (if any) into slot ^ 1
+      const bool this_ok = q0_ok;
       bad |= !this_ok;
-      wait_vm_all();
-      lds_barrier();                   // its bytes are in LDS; every wave is done with slot ^ 1
-      // the next page -> the other slot (direct to LDS; lands while this page is computed)
-      if (nb1 <= r.end_b) {
-        load_ok = src1 != nullptr;
-        if (load_ok) issue_page<FMT>(src1, page_extent, ring + (slot ^ 1) * kSlotBytes, ld_off, wave);
-        int nb2, npi2;
-        advance(nb1, npi1, nb1 == b ? pg1 : -1, nb2, npi2);
-        nb1 = nb2;
-        npi1 = npi2;
-        src1 = (nb1 <= r.end_b) ? page_src(nb1, npi1) : nullptr;
-      }
+      wait_q0();
+      lds_barrier();                   // q0's bytes are in LDS for every wave
       page_step<TG, FMT>(ring + slot * kSlotBytes, conv, ln, L, last_allowed, pi, this_ok, p.scale_log2, qf, acc,
                          m_run, l_run);
+      lds_barrier();                   // every wave is done with `slot`
+      // q1 becomes q0; the page after it becomes q1, its loads into `slot`
+      q0_ok = q1_ok;
+      if (q1_state != 0 && nb2 <= r.end_b) {
+        q1_src = src2;
+        q1_ok = src2 != nullptr;
+        if (kMergeScratch && pi + 1 == pg1) {
+          q1_state = 2;
+        } else {
+          if (q1_ok) issue_page<FMT>(src2, page_extent, ring + slot * kSlotBytes, ld_off, wave);
+          q1_state = 1;
+        }
+        int nb3, npi3;
+        advance(nb2, npi2, nb2 == b ? pg1 : -1, nb3, npi3);
+        nb2 = nb3;
+        npi2 = npi3;
+        src2 = (nb2 <= r.end_b) ? page_src(nb2, npi2) : nullptr;
+      } else {
+        q1_state = 0;
+      }
       slot ^= 1;
     }
 

@@ -174,7 +174,7 @@ def test_single_token_gives_value_row_exactly():
     compare(w, O, LSE, O_ref, LSE_ref, label="L=1")
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("h_q", [16, 32, 128])
 def test_empty_and_fully_masked_rows(h_q):
     w = make_workload(name="empty", batch=4, s_q=2, h_q=h_q, seqlens=[0, 1, 2, 70], causal=True, seed=59,
                       max_blocks=3)
@@ -184,6 +184,18 @@ def test_empty_and_fully_masked_rows(h_q):
         compare(w, O, LSE, O_ref, LSE_ref, label=f"empty rows parts={parts}")
         assert np.all(O[0] == 0) and np.all(np.isneginf(LSE[0]))
         assert np.all(O[1, 0] == 0) and np.all(np.isneginf(LSE[1, :, 0]))
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 64])
+def test_sequences_without_pages_between_pages(h_q):
+    # ranges that start with, and step over, sequences of length 0: the page ring keeps the
+    # next pages in flight across them while their (empty) outputs and merges are written
+    w = make_workload(name="gaps", batch=8, s_q=1, h_q=h_q, seqlens=[0, 0, 65, 0, 1, 0, 130, 0], seed=63,
+                      max_blocks=3)
+    O_ref, LSE_ref = oracle.mla_decode_workload(w)
+    for parts in (0, 1, 2, 3):
+        O, LSE = run_gpu(w, num_parts=parts)
+        compare(w, O, LSE, O_ref, LSE_ref, label=f"gaps h_q={h_q} parts={parts}")
 
 
 @pytest.mark.parametrize("h_q", [16, 128])
