@@ -118,8 +118,10 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int he
                             int32_t* num_splits_host, int* num_parts_out);
 
 /*
- * Bytes of device workspace mla_decode_kvcache needs for split partials
- * (fp32 O and LSE per piece of a sequence): at most batch + num_parts pieces.
+ * Bytes of device workspace mla_decode_kvcache needs for split partials: per
+ * piece of a sequence (at most batch + num_parts pieces) and row, the partial
+ * O (fp32; for heads_per_kv > 64, fp16 with a power-of-two fp32 scale per 64
+ * dims) and an fp32 LSE.
  * Returns 0 on invalid arguments.
  */
 size_t mla_workspace_bytes(int batch, int num_parts, int heads_per_kv, int h_kv);

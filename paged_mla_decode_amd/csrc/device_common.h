@@ -44,6 +44,57 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Partial O of a piece in the workspace: fp16 values, each 64-dim block of a
+// row divided by 2^(e - 15), where 2^e exceeds the largest finite magnitude in
+// the block. The values then stay below 2^15 (fp16 keeps 11 significant bits
+// of each), the power-of-two scale is exact both ways, and the combine
+// multiplies it back. Infinities and NaN pass through unchanged.
+constexpr int kPartBlocks = 8;                     // 64-dim blocks per row of 512
+
+__device__ __forceinline__ float finite_abs(float v) {
+  const float a = __builtin_fabsf(v);
+  return a < __builtin_inff() ? a : 0.f;          // NaN compares false: 0
+}
+
+// scale (the combine multiplies by it) and inv (the writer multiplies by it)
+// for a block whose largest finite magnitude is mx
+__device__ __forceinline__ void part_block_scale(float mx, float& scale, float& inv) {
+  int e = __builtin_amdgcn_frexp_expf(mx);         // mx < 2^e; 0 for mx = 0
+  e = e < -110 ? -110 : e;
+  scale = __builtin_amdgcn_ldexpf(1.f, e - 15);
+  inv = __builtin_amdgcn_ldexpf(1.f, 15 - e);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// One 32-dim span of a row's partial O, held as the MFMA output leaves it: lane
+// (r16, q4) has dims 4 q4 .. + 3 (a, fp16 x 4) and 16 + 4 q4 .. + 3 (b) of row
+// r16. Lanes q4 and q4 ^ 1 trade halves (v_permlane16_swap) so that each lane
+// holds 8 consecutive dims: q4 even the dims of a of lanes q4, q4 + 1 (from
+// 4 q4), q4 odd the dims of b of lanes q4 - 1, q4 (from 4 q4 + 12). The 4 lanes
+// of a row then store 64 contiguous bytes. Returns the 16 bytes; *off = the
+// lane's first dim within the span.
+__device__ __forceinline__ u32x4 span_f16x8(const u32x2& a, const u32x2& b, int q4, int* off) {
+  const auto a0 = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+  const auto a1 = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+  const auto b0 = __builtin_amdgcn_permlane16_swap(b[0], b[0], false, false);
+  const auto b1 = __builtin_amdgcn_permlane16_swap(b[1], b[1], false, false);
+  // element 0 of a swap result: the value of the even lane of the pair, 1: the odd one
+  const bool odd = (q4 & 1) != 0;
+  *off = 4 * q4 + (odd ? 12 : 0);
+  return odd ? u32x4{b0[0], b1[0], b0[1], b1[1]} : u32x4{a0[0], a1[0], a0[1], a1[1]};
+}
+
 // Swizzle of the 16-byte chunk index inside a token row: chunk j of token t is
 // stored at j ^ (t & 7), inside its aligned group of 8 chunks. Chosen by
 // measurement on gfx950 (a 1152-byte row puts consecutive tokens half a bank

@@ -27,7 +27,12 @@ struct DecodeParams {
   float scale_log2;           // softmax_scale * log2(e)
   uint16_t* o;                // bf16 bits [batch, s_q, h_q, 512]
   float* lse;                 // [batch, h_q, s_q]
-  float* part_o;              // [slots, h_kv, rows, 512]
+  // Partial O of the pieces, [slots, h_kv, rows, 512]: fp32 (part_o32) for tiles of up to 64
+  // rows; fp16 (part_o16) with a power-of-two scale per 64-dim block (part_scale,
+  // [slots, h_kv, rows, 8]) for 128-row tiles. The other pointer is null.
+  float* part_o32;
+  uint16_t* part_o16;
+  float* part_scale;
   float* part_lse;            // [slots, h_kv, rows]
   int max_slots;
   int max_splits;             // hint: largest piece count of any sequence (0 = unknown)

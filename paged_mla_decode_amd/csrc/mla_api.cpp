@@ -59,8 +59,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Partial O: fp32 for tiles of up to 64 rows; fp16 plus one fp32 scale per 64 dims for
+// 128-row tiles (rows > 64).
 size_t partial_o_bytes(int slots, int rows, int h_kv) {
-  return align256(static_cast<size_t>(slots) * h_kv * rows * mla::kDv * sizeof(float));
+  const size_t elem = rows > 64 ? sizeof(uint16_t) : sizeof(float);
+  return align256(static_cast<size_t>(slots) * h_kv * rows * mla::kDv * elem);
+}
+
+size_t partial_scale_bytes(int slots, int rows, int h_kv) {
+  if (rows <= 64) return 0;
+  return align256(static_cast<size_t>(slots) * h_kv * rows * (mla::kDv / 64) * sizeof(float));
 }
 
 size_t partial_lse_bytes(int slots, int rows, int h_kv) {
@@ -124,7 +132,8 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int he
 size_t mla_workspace_bytes(int batch, int num_parts, int heads_per_kv, int h_kv) {
   if (batch < 1 || num_parts < 1 || heads_per_kv < 1 || h_kv < 1) return 0;
   const int slots = batch + num_parts;
-  return partial_o_bytes(slots, heads_per_kv, h_kv) + partial_lse_bytes(slots, heads_per_kv, h_kv);
+  return partial_o_bytes(slots, heads_per_kv, h_kv) + partial_scale_bytes(slots, heads_per_kv, h_kv) +
+         partial_lse_bytes(slots, heads_per_kv, h_kv);
 }
 
 mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
@@ -222,8 +231,12 @@ mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
   p.o = static_cast<uint16_t*>(a->o);
   p.lse = a->lse;
   const int slots = a->batch + a->num_parts;
-  p.part_o = static_cast<float*>(a->workspace);
-  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + partial_o_bytes(slots, rows, a->h_kv));
+  char* const ws = static_cast<char*>(a->workspace);
+  p.part_o32 = plan.wide ? nullptr : reinterpret_cast<float*>(ws);
+  p.part_o16 = plan.wide ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+  p.part_scale = plan.wide ? reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv)) : nullptr;
+  p.part_lse = reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv) +
+                                        partial_scale_bytes(slots, rows, a->h_kv));
   p.max_slots = slots;
   p.max_splits = a->max_splits > 0 ? a->max_splits : 0;
   p.grid_wgs = static_cast<int>(wgs);

@@ -620,7 +620,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       } else {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
-          float* prow = p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv + 4 * q4;
+          float* prow = p.part_o32 + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv + 4 * q4;
           const float nan = __builtin_nanf("");
 #pragma unroll
           for (int d = 0; d < 32; ++d) {
@@ -713,6 +713,7 @@ constexpr int kCombGroup = 8;                   // pieces whose loads are in fli
 // loads in flight at once. (A two-pass kernel with 16 pieces per workgroup in
 // parallel, for sequences cut into many pieces, was slower on the ragged
 // workload: 24 us against 19 us.)
+template <bool F16>
 __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -735,23 +736,49 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) 
   }
   const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;
   const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
-  const float* o_in = p.part_o + (static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row) * kDv
-                      + dim0;
+  const int64_t row0 = static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   MergeState st;
   for (int i0 = 0; i0 < n; i0 += kCombGroup) {
     float lse[kCombGroup];
     f32x4 x0[kCombGroup], x1[kCombGroup];
+    if constexpr (F16) {
+      const uint16_t* o_in = p.part_o16 + row0 * kDv + dim0;
+      const float* sc_in = p.part_scale + row0 * kPartBlocks + (dim0 >> 6);
+      float sc[kCombGroup];
+      u32x4 h[kCombGroup];
+      // all loads of the group first (converting right after each load would wait for it)
 #pragma unroll
-    for (int j = 0; j < kCombGroup; ++j) {
-      const int i = i0 + j;
-      if (i < n) {
-        lse[j] = lse_in[i * stride];
-        x0[j] = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
-        x1[j] = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
-      } else {
-        lse[j] = kNegInf;
-        x0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        x1[j] = x0[j];
+      for (int j = 0; j < kCombGroup; ++j) {
+        const int i = i0 + j;
+        if (i < n) {
+          lse[j] = lse_in[i * stride];
+          h[j] = *reinterpret_cast<const u32x4*>(o_in + i * stride * kDv);
+          sc[j] = sc_in[i * stride * kPartBlocks];
+        } else {
+          lse[j] = kNegInf;
+          h[j] = u32x4{0u, 0u, 0u, 0u};
+          sc[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kCombGroup; ++j) {
+        x0[j] = f32x4{f16_lo(h[j][0]), f16_hi(h[j][0]), f16_lo(h[j][1]), f16_hi(h[j][1])} * sc[j];
+        x1[j] = f32x4{f16_lo(h[j][2]), f16_hi(h[j][2]), f16_lo(h[j][3]), f16_hi(h[j][3])} * sc[j];
+      }
+    } else {
+      const float* o_in = p.part_o32 + row0 * kDv + dim0;
+#pragma unroll
+      for (int j = 0; j < kCombGroup; ++j) {
+        const int i = i0 + j;
+        if (i < n) {
+          lse[j] = lse_in[i * stride];
+          x0[j] = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv);
+          x1[j] = *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + 4);
+        } else {
+          lse[j] = kNegInf;
+          x0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          x1[j] = x0[j];
+        }
       }
     }
     merge_group<kCombGroup>(st, lse, x0, x1, min(n - i0, kCombGroup));
@@ -797,7 +824,10 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   if (err != hipSuccess) return err;
   {
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
-    hipLaunchKernelGGL(combine_rows_kernel, cgrid, dim3(kThreads), 0, stream, p);
+    if (plan.wide)
+      hipLaunchKernelGGL(combine_rows_kernel<true>, cgrid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(combine_rows_kernel<false>, cgrid, dim3(kThreads), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

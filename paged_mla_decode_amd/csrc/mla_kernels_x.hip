@@ -619,15 +619,32 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
       } else {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
-          float* prow = p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv +
-                        64 * wave + 4 * q4;
+          // fp16 with a power-of-two scale per 64-dim block: this wave's dims are block `wave`
+          const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row;
+          f32x4 v[4];
+          float mx = 0.f;
 #pragma unroll
-          for (int dd = 0; dd < 4; ++dd) {
-            f32x4 v;
+          for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = bad ? nan : acc[dd][rr][i] * inv;
-            *reinterpret_cast<f32x4*>(prow + 16 * dd) = v;
+            for (int i = 0; i < 4; ++i) {
+              v[dd][i] = bad ? nan : acc[dd][rr][i] * inv;
+              mx = fmaxf(mx, finite_abs(v[dd][i]));
+            }
+          float scl, bi;
+          part_block_scale(max4lanes(mx), scl, bi);
+          uint16_t* const po = p.part_o16 + prow * kDv + 64 * wave;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x2 a, c;
+            a[0] = pack_f16x2(v[2 * h][0] * bi, v[2 * h][1] * bi);
+            a[1] = pack_f16x2(v[2 * h][2] * bi, v[2 * h][3] * bi);
+            c[0] = pack_f16x2(v[2 * h + 1][0] * bi, v[2 * h + 1][1] * bi);
+            c[1] = pack_f16x2(v[2 * h + 1][2] * bi, v[2 * h + 1][3] * bi);
+            int off;
+            const u32x4 w = span_f16x8(a, c, q4, &off);
+            *reinterpret_cast<u32x4*>(po + 32 * h + off) = w;
           }
+          if (q4 == 0) p.part_scale[prow * kPartBlocks + wave] = scl;
         }
       }
     }
@@ -1017,15 +1034,32 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
       } else {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
-          float* prow = p.part_o + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv +
-                        64 * wave + 4 * q4;
+          // fp16 with a power-of-two scale per 64-dim block: this wave's dims are block `wave`
+          const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row;
+          f32x4 v[4];
+          float mx = 0.f;
 #pragma unroll
-          for (int dd = 0; dd < 4; ++dd) {
-            f32x4 v;
+          for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = bad ? nan : acc[dd][rr][i] * inv;
-            *reinterpret_cast<f32x4*>(prow + 16 * dd) = v;
+            for (int i = 0; i < 4; ++i) {
+              v[dd][i] = bad ? nan : acc[dd][rr][i] * inv;
+              mx = fmaxf(mx, finite_abs(v[dd][i]));
+            }
+          float scl, bi;
+          part_block_scale(max4lanes(mx), scl, bi);
+          uint16_t* const po = p.part_o16 + prow * kDv + 64 * wave;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x2 a, c;
+            a[0] = pack_f16x2(v[2 * h][0] * bi, v[2 * h][1] * bi);
+            a[1] = pack_f16x2(v[2 * h][2] * bi, v[2 * h][3] * bi);
+            c[0] = pack_f16x2(v[2 * h + 1][0] * bi, v[2 * h + 1][1] * bi);
+            c[1] = pack_f16x2(v[2 * h + 1][2] * bi, v[2 * h + 1][3] * bi);
+            int off;
+            const u32x4 w = span_f16x8(a, c, q4, &off);
+            *reinterpret_cast<u32x4*>(po + 32 * h + off) = w;
           }
+          if (q4 == 0) p.part_scale[prow * kPartBlocks + wave] = scl;
         }
       }
     }

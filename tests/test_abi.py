@@ -64,8 +64,10 @@ def test_workspace_bytes():
     B, P, M = 64, 256, 128
     n = lib.mla_workspace_bytes(B, P, M, 1)
     slots = B + P
-    assert n >= slots * M * 512 * 4 + slots * M * 4
+    assert n >= slots * M * 512 * 2 + slots * M * 8 * 4 + slots * M * 4   # fp16 O, 8 block scales, LSE
     assert n % 256 == 0
+    n16 = lib.mla_workspace_bytes(B, P, 16, 1)                               # up to 64 rows: fp32 O
+    assert n16 >= slots * 16 * 512 * 4 + slots * 16 * 4 and n16 % 256 == 0
 
 
 def _valid_args():
