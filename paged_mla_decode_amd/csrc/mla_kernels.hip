@@ -713,9 +713,13 @@ constexpr int kCombGroup = 8;                   // pieces whose loads are in fli
 // loads in flight at once. (A two-pass kernel with 16 pieces per workgroup in
 // parallel, for sequences cut into many pieces, was slower on the ragged
 // workload: 24 us against 19 us.)
-template <bool F16>
-__global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) {
-  const int tid = threadIdx.x;
+// G piece groups of kThreads threads each: group g merges pieces 8 g .. 8 g + 7,
+// 8 (g + G) .., and group 0 merges the G states through LDS at the end (G > 1
+// for sequences cut into many pieces: fewer rounds of dependent loads).
+template <bool F16, int G>
+__global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams p) {
+  const int tid = threadIdx.x % kThreads;
+  const int grp = threadIdx.x / kThreads;
   const int b = blockIdx.x;
   const int row = blockIdx.y * 16 + tid / 16;
   const int l16 = tid & 15;
@@ -723,22 +727,28 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) 
   const int quarter = blockIdx.z % (kDv / kCombDims);
   const int slot0 = ld_meta(p.num_splits + b);
   const int n = ld_meta(p.num_splits + b + 1) - slot0;
-  if (n <= 1 || row >= p.rows) return;
-  const int s_idx = row / p.group;
-  const int head = kvh * p.group + row % p.group;
+  if (n <= 1) return;                            // the whole workgroup: one piece is written by the split kernel
+  if constexpr (G == 1) {
+    if (row >= p.rows) return;
+  }
+  const bool row_ok = row < p.rows;              // G > 1: every thread reaches the barrier below
+  const int s_idx = row_ok ? row / p.group : 0;
+  const int head = kvh * p.group + (row_ok ? row % p.group : 0);
   const int dim0 = quarter * kCombDims + 8 * l16;
   uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
   float* lse_out = p.lse + (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
-  if (slot0 < 0 || slot0 + n > p.max_slots) {
-    *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    if (l16 == 0 && quarter == 0) *lse_out = __builtin_nanf("");
+  if (slot0 < 0 || slot0 + n > p.max_slots) {   // uniform over the workgroup
+    if (row_ok && grp == 0) {
+      *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+      if (l16 == 0 && quarter == 0) *lse_out = __builtin_nanf("");
+    }
     return;
   }
   const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;
   const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   const int64_t row0 = static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   MergeState st;
-  for (int i0 = 0; i0 < n; i0 += kCombGroup) {
+  for (int i0 = grp * kCombGroup; row_ok && i0 < n; i0 += G * kCombGroup) {
     float lse[kCombGroup];
     f32x4 x0[kCombGroup], x1[kCombGroup];
     if constexpr (F16) {
@@ -783,6 +793,36 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) 
     }
     merge_group<kCombGroup>(st, lse, x0, x1, min(n - i0, kCombGroup));
   }
+  if constexpr (G > 1) {
+    __shared__ float xs[G - 1][10][kThreads];
+    if (grp > 0) {
+      float* x = &xs[grp - 1][0][tid];
+      x[0] = st.m;
+      x[kThreads] = st.l;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[(2 + i) * kThreads] = st.a0[i];
+        x[(6 + i) * kThreads] = st.a1[i];
+      }
+    }
+    __syncthreads();
+    if (grp > 0 || !row_ok) return;
+#pragma unroll
+    for (int g = 0; g < G - 1; ++g) {
+      const float* x = &xs[g][0][tid];
+      const float m2 = x[0], l2 = x[kThreads];
+      const float mn = fmaxf(st.m, m2);
+      const float s1 = (st.m == kNegInf) ? 0.f : __expf(st.m - mn);
+      const float s2 = (m2 == kNegInf) ? 0.f : __expf(m2 - mn);
+      st.l = st.l * s1 + l2 * s2;                 // NaN in either stays NaN
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.a0[i] = st.a0[i] * s1 + x[(2 + i) * kThreads] * s2;
+        st.a1[i] = st.a1[i] * s1 + x[(6 + i) * kThreads] * s2;
+      }
+      st.m = mn;
+    }
+  }
   const float inv = merge_inv(st.l);
   *reinterpret_cast<u32x4*>(orow) = pack_bf16x8(st.a0 * inv, st.a1 * inv);
   if (l16 == 0 && quarter == 0) *lse_out = merge_lse(st);
@@ -824,10 +864,16 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   if (err != hipSuccess) return err;
   {
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
-    if (plan.wide)
-      hipLaunchKernelGGL(combine_rows_kernel<true>, cgrid, dim3(kThreads), 0, stream, p);
+    // sequences cut into many pieces (the host metadata's largest piece count): 4 piece groups
+    const bool many = p.max_splits > 2 * kCombGroup;
+    if (plan.wide && many)
+      hipLaunchKernelGGL((combine_rows_kernel<true, 4>), cgrid, dim3(4 * kThreads), 0, stream, p);
+    else if (plan.wide)
+      hipLaunchKernelGGL((combine_rows_kernel<true, 1>), cgrid, dim3(kThreads), 0, stream, p);
+    else if (many)
+      hipLaunchKernelGGL((combine_rows_kernel<false, 4>), cgrid, dim3(4 * kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(combine_rows_kernel<false>, cgrid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((combine_rows_kernel<false, 1>), cgrid, dim3(kThreads), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
