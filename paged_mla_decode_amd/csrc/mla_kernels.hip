@@ -126,7 +126,7 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
       const float sv = *reinterpret_cast<const float*>(cur + t * kFp8Record + 512 + 4 * c);
       scales[tid] = (this_ok && t < valid) ? sv : 0.f;
     }
-    lds_barrier();
+    lds_barrier_keep_loads();
     page = conv;
     scale_tab = scales;
   } else {
@@ -136,7 +136,7 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
       const int z0 = this_ok ? valid : 0;
       for (int x = z0 * kRowBytes + 16 * tid; x < kPageBytes; x += 16 * kThreads)
         *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
-      lds_barrier();
+      lds_barrier_keep_loads();
     }
     page = cur;
   }
@@ -520,10 +520,10 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       const bool this_ok = q0_ok;
       bad |= !this_ok;
       wait_q0();
-      lds_barrier();                   // q0's bytes are in LDS for every wave
+      lds_barrier_keep_loads();                   // q0's bytes are in LDS for every wave
       page_step<TG, FMT>(ring + slot * kSlotBytes, conv, ln, L, last_allowed, pi, this_ok, p.scale_log2, qf, acc,
                          m_run, l_run);
-      lds_barrier();                   // every wave is done with `slot`
+      lds_barrier_keep_loads();                   // every wave is done with `slot`
       // q1 becomes q0; the page after it becomes q1, its loads into `slot`
       q0_ok = q1_ok;
       if (q1_state != 0 && nb2 <= r.end_b) {
@@ -550,12 +550,12 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     float l_row = sum4lanes(l_run);
     float m_fin = m_run;
     if constexpr (TG > 1) {
-      lds_barrier();                   // all waves done with the LDS page
+      lds_barrier_keep_loads();                   // all waves done with the LDS page
       if (lane < 16) {
         red_m[wave][r16] = m_run;
         red_l[wave][r16] = l_row;
       }
-      lds_barrier();
+      lds_barrier_keep_loads();
       float M = kNegInf;
 #pragma unroll
       for (int k = 0; k < TG; ++k) M = fmaxf(M, red_m[rb + RB * k][r16]);
@@ -569,32 +569,33 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       l_row = ltot;
       m_fin = M;
       // Sum the TG accumulators of each row block through LDS (fp32 [16 rows][512]),
-      // in the slot not receiving a page (bf16) or the converted page (fp8).
+      // in the slot not receiving a page (bf16) or the converted page (fp8). The
+      // 16-byte chunk 4 d + q4 of row r16 sits at chunk (4 d + q4) ^ r16: with
+      // 2 KB rows, the 16 rows of one store would otherwise all hit the same banks.
       float* red = reinterpret_cast<float*>(kFp8 ? conv : ring + (slot ^ 1) * kSlotBytes);
+      auto red_at = [&](int sl, int d) { return red + sl * (16 * 512) + r16 * 512 + 4 * ((4 * d + q4) ^ r16); };
       auto put = [&](int sl) {
 #pragma unroll
-        for (int d = 0; d < 32; ++d)
-          *reinterpret_cast<f32x4*>(red + sl * (16 * 512) + r16 * 512 + 16 * d + 4 * q4) = acc[d];
+        for (int d = 0; d < 32; ++d) *reinterpret_cast<f32x4*>(red_at(sl, d)) = acc[d];
       };
       auto add = [&](int sl) {
 #pragma unroll
-        for (int d = 0; d < 32; ++d)
-          acc[d] += *reinterpret_cast<const f32x4*>(red + sl * (16 * 512) + r16 * 512 + 16 * d + 4 * q4);
+        for (int d = 0; d < 32; ++d) acc[d] += *reinterpret_cast<const f32x4*>(red_at(sl, d));
       };
       if constexpr (TG == 4) {                 // RB == 1: waves 0..3 hold the same rows
         if (wave >= 2) put(wave - 2);
-        lds_barrier();
+        lds_barrier_keep_loads();
         if (wave < 2) add(wave);
-        lds_barrier();
+        lds_barrier_keep_loads();
         if (wave == 1) put(0);
-        lds_barrier();
+        lds_barrier_keep_loads();
         if (wave == 0) add(0);
       } else {                                  // TG == 2, RB == 2
         if (tg == 1) put(rb);
-        lds_barrier();
+        lds_barrier_keep_loads();
         if (tg == 0) add(rb);
       }
-      lds_barrier();                            // scratch free again before the next page lands
+      lds_barrier_keep_loads();                            // scratch free again before the next page lands
     }
 
     if (tg == 0 && row_ok) {
