@@ -223,6 +223,60 @@ __device__ __forceinline__ void lds_barrier() {
 // keeps the compiler from moving memory accesses across it. The caller
 // orders the direct loads itself (s_waitcnt vmcnt before the barrier that
 // publishes them).
+// 16-byte LDS store in inline asm, for LDS regions that the compiler cannot tell
+// apart from direct loads in flight (a plain store would wait for all of them).
+// Completion is ordered by lgkmcnt (lds_barrier_keep_loads waits for it).
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ptr));
+}
+__device__ __forceinline__ void lds_store16(uint32_t addr, const f32x4& v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// N 16-byte LDS reads in one inline-asm block, waited inside it (lgkmcnt(0)), for
+// reads the compiler would otherwise hold back behind every direct load in flight.
+// Outputs are early-clobber: no address register is reused while a read is in flight.
+template <int N>
+__device__ __forceinline__ void lds_read16_block(const uint32_t (&a)[N], bf16x8 (&v)[N]);
+template <>
+__device__ __forceinline__ void lds_read16_block<3>(const uint32_t (&a)[3], bf16x8 (&v)[3]) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2])
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read16_block<6>(const uint32_t (&a)[6], bf16x8 (&v)[6]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read16_block<8>(const uint32_t (&a)[8], bf16x8 (&v)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+// 8 transposed 8-byte LDS reads (ds_read_b64_tr_b16) in one asm block, waited inside it.
+__device__ __forceinline__ void lds_read_tr8_block(const uint32_t (&a)[8], u32x2 (&v)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\tds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\tds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 __device__ __forceinline__ void lds_barrier_keep_loads() {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");

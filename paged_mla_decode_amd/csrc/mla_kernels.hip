@@ -134,8 +134,9 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
       // zero the rows past the sequence end (all rows of a bad page) so that
       // stale bytes never meet a zero weight in P V (0 * NaN = NaN)
       const int z0 = this_ok ? valid : 0;
+      // (asm stores: see merge_put)
       for (int x = z0 * kRowBytes + 16 * tid; x < kPageBytes; x += 16 * kThreads)
-        *reinterpret_cast<u32x4*>(cur + x) = u32x4{0u, 0u, 0u, 0u};
+        lds_store16(lds_addr(cur + x), f32x4{0.f, 0.f, 0.f, 0.f});
       lds_barrier_keep_loads();
     }
     page = cur;
@@ -173,37 +174,37 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
       }
     }
   } else {
-    // NT tiles x CH partial chains = 4 independent accumulations in flight;
-    // the K operands of chunk c + 1 are read while chunk c multiplies.
+    // NT tiles x CH partial chains = 4 independent accumulations in flight. The K
+    // operands are read in inline asm, KB chunks per block, each block waited inside
+    // it: a plain LDS read here made the compiler wait for the next page's loads in
+    // flight (it cannot tell the two slots of the ring apart). The MFMAs of a block
+    // run while the next block's reads are in flight.
     constexpr int CH = (NT >= 4) ? 1 : 4 / NT;
+    constexpr int KB = (NT >= 4) ? 2 : 3;            // chunks per read block (18 % KB == 0)
     f32x4 part[NT][CH];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < CH; ++h) part[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* krow0 = page + (16 * tg * NT + r16) * kRowBytes;
-    auto kload = [&](int c, int t) -> bf16x8 {
-      return *reinterpret_cast<const bf16x8*>(krow0 + 16 * t * kRowBytes + 128 * (c >> 1) + ((c & 1) ? kb1 : kb0));
+    const uint32_t kbase = lds_addr(page + (16 * tg * NT + r16) * kRowBytes);
+    auto kaddr = [&](int c, int t) -> uint32_t {
+      return kbase + 16 * t * kRowBytes + 128 * (c >> 1) + ((c & 1) ? kb1 : kb0);
     };
-    // three-slot rotation: reads run two chunks ahead of the MFMAs
-    constexpr int kDepth = 3;
-    bf16x8 kbuf[kDepth][NT];
 #pragma unroll
-    for (int c = 0; c < kDepth - 1; ++c)
+    for (int c0 = 0; c0 < 18; c0 += KB) {
+      bf16x8 kv[KB * NT];
+      uint32_t ka[KB * NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) kbuf[c][t] = kload(c, t);
-    __builtin_amdgcn_sched_group_barrier(0x100, (kDepth - 1) * NT, 0);
+      for (int j = 0; j < KB; ++j)
 #pragma unroll
-    for (int c = 0; c < 18; ++c) {
-      if (c + kDepth - 1 < 18) {
+        for (int t = 0; t < NT; ++t) ka[j * NT + t] = kaddr(c0 + j, t);
+      lds_read16_block<KB * NT>(ka, kv);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) kbuf[(c + kDepth - 1) % kDepth][t] = kload(c + kDepth - 1, t);
-      }
+      for (int j = 0; j < KB; ++j)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        part[t][c % CH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c % kDepth][t], qf[c], part[t][c % CH], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);     // MFMAs of chunk c ...
-      if (c + kDepth - 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);   // ... then reads of chunk c + 2
+        for (int t = 0; t < NT; ++t)
+          part[t][(c0 + j) % CH] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[j * NT + t], qf[c0 + j], part[t][(c0 + j) % CH], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -253,7 +254,6 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
   int vb[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) vb[r] = 16 * ((2 * r + ln.tr_hh) ^ ln.sw_v) + 8 * ln.tr_half;
-  constexpr int kAhead = 4;                  // transposed reads issued ahead of their MFMA
   if constexpr (NT >= 2) {
 #pragma unroll
     for (int u = 0; u < NT / 2; ++u) {
@@ -274,20 +274,45 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
           pb[g][4 + j] = static_cast<__bf16>(x1);
         }
       }
-      auto vload = [&](int d) -> bf16x8 {
-        const uint8_t* a0 = v0 + 128 * (d >> 2) + vb[d & 3];
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 va[kAhead];
+      if constexpr (kFp8) {
+        // the dequantised page sits in its own buffer (no load in flight to it)
+        auto vload = [&](int d) -> bf16x8 {
+          const uint8_t* a0 = v0 + 128 * (d >> 2) + vb[d & 3];
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * kRowBytes));
+          return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        constexpr int kAhead = 4;
+        bf16x8 va[kAhead];
 #pragma unroll
-      for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
+        for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
 #pragma unroll
-      for (int d = 0; d < 32; ++d) {
-        const bf16x8 a = va[d % kAhead];
-        if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
-        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kFp8 ? (d >> 3) : 0], acc[d], 0, 0, 0);
+        for (int d = 0; d < 32; ++d) {
+          const bf16x8 a = va[d % kAhead];
+          if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
+          acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[d >> 3], acc[d], 0, 0, 0);
+        }
+        continue;  // next pair of token tiles
+      }
+      // transposed V reads in inline asm, 4 dims (8 reads) per asm block, as the K reads
+      const uint32_t vbase = lds_addr(v0);
+#pragma unroll
+      for (int d0 = 0; d0 < 32; d0 += 4) {
+        uint32_t va[8];
+        u32x2 vr[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          va[2 * j] = vbase + 128 * ((d0 + j) >> 2) + vb[(d0 + j) & 3];
+          va[2 * j + 1] = va[2 * j] + 16 * kRowBytes;
+        }
+        lds_read_tr8_block(va, vr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x4 lo = __builtin_bit_cast(bf16x4, vr[2 * j]), hi = __builtin_bit_cast(bf16x4, vr[2 * j + 1]);
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const int d = d0 + j;
+          acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], acc[d], 0, 0, 0);
+        }
       }
     }
   } else {
@@ -303,19 +328,72 @@ __device__ __forceinline__ void page_step(uint8_t* __restrict__ cur, uint8_t* __
         pb[g][j] = static_cast<short>(f32_to_bf16(x));
       }
     }
-    auto vload = [&](int d) -> s16x4 {
-      return __builtin_bit_cast(
-          s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + 128 * (d >> 2) + vb[d & 3])));
-    };
-    s16x4 va[kAhead];
+    if constexpr (kFp8) {
+      auto vload = [&](int d) -> s16x4 {
+        return __builtin_bit_cast(
+            s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, v0 + 128 * (d >> 2) + vb[d & 3])));
+      };
+      constexpr int kAhead = 4;
+      s16x4 va[kAhead];
 #pragma unroll
-    for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
+      for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const s16x4 a = va[d % kAhead];
-      if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
-      acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[kFp8 ? (d >> 3) : 0], acc[d], 0, 0, 0);
+      for (int d = 0; d < 32; ++d) {
+        const s16x4 a = va[d % kAhead];
+        if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
+        acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[d >> 3], acc[d], 0, 0, 0);
+      }
+      return;
     }
+    // transposed V reads in inline asm, 8 dims per asm block, as the K reads
+    const uint32_t vbase = lds_addr(v0);
+#pragma unroll
+    for (int d0 = 0; d0 < 32; d0 += 8) {
+      uint32_t va[8];
+      u32x2 vr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) va[j] = vbase + 128 * ((d0 + j) >> 2) + vb[(d0 + j) & 3];
+      lds_read_tr8_block(va, vr);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = d0 + j;
+        acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vr[j]), pb[0], acc[d], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Token-group merge through LDS (fp32 [16 rows][512] per slot sl of the scratch
+// `red`): the 16-byte chunk 4 d + q4 of row r16 sits at chunk (4 d + q4) ^ r16 --
+// with 2 KB rows the 16 rows of one store would otherwise all hit the same
+// banks. The accesses are inline asm: the compiler cannot tell them from the
+// page loads in flight (which write LDS) and would wait for all of those first.
+// The reads wait for their own data inside the asm block (early-clobber
+// outputs, so no address register is reused while a read is in flight).
+__device__ __forceinline__ void merge_put(float* red, int sl, int r16, int q4, const f32x4 (&acc)[32]) {
+  const uint32_t base = lds_addr(red + sl * (16 * 512) + r16 * 512);
+#pragma unroll
+  for (int d = 0; d < 32; ++d) lds_store16(base + 16 * ((4 * d + q4) ^ r16), acc[d]);
+}
+__device__ __forceinline__ void merge_add(const float* red, int sl, int r16, int q4, f32x4 (&acc)[32]) {
+  const uint32_t base = lds_addr(red + sl * (16 * 512) + r16 * 512);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    f32x4 x0, x1, x2, x3;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+        : "v"(base + 16 * ((4 * (4 * g + 0) + q4) ^ r16)), "v"(base + 16 * ((4 * (4 * g + 1) + q4) ^ r16)),
+          "v"(base + 16 * ((4 * (4 * g + 2) + q4) ^ r16)), "v"(base + 16 * ((4 * (4 * g + 3) + q4) ^ r16))
+        : "memory");
+    acc[4 * g + 0] += x0;
+    acc[4 * g + 1] += x1;
+    acc[4 * g + 2] += x2;
+    acc[4 * g + 3] += x3;
   }
 }
 
@@ -568,32 +646,21 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       for (int d = 0; d < 32; ++d) acc[d] *= f;
       l_row = ltot;
       m_fin = M;
-      // Sum the TG accumulators of each row block through LDS (fp32 [16 rows][512]),
-      // in the slot not receiving a page (bf16) or the converted page (fp8). The
-      // 16-byte chunk 4 d + q4 of row r16 sits at chunk (4 d + q4) ^ r16: with
-      // 2 KB rows, the 16 rows of one store would otherwise all hit the same banks.
+      // Sum the TG accumulators of each row block through LDS, in the slot not
+      // receiving a page (bf16) or the converted page (fp8).
       float* red = reinterpret_cast<float*>(kFp8 ? conv : ring + (slot ^ 1) * kSlotBytes);
-      auto red_at = [&](int sl, int d) { return red + sl * (16 * 512) + r16 * 512 + 4 * ((4 * d + q4) ^ r16); };
-      auto put = [&](int sl) {
-#pragma unroll
-        for (int d = 0; d < 32; ++d) *reinterpret_cast<f32x4*>(red_at(sl, d)) = acc[d];
-      };
-      auto add = [&](int sl) {
-#pragma unroll
-        for (int d = 0; d < 32; ++d) acc[d] += *reinterpret_cast<const f32x4*>(red_at(sl, d));
-      };
       if constexpr (TG == 4) {                 // RB == 1: waves 0..3 hold the same rows
-        if (wave >= 2) put(wave - 2);
+        if (wave >= 2) merge_put(red, wave - 2, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (wave < 2) add(wave);
+        if (wave < 2) merge_add(red, wave, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (wave == 1) put(0);
+        if (wave == 1) merge_put(red, 0, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (wave == 0) add(0);
+        if (wave == 0) merge_add(red, 0, r16, q4, acc);
       } else {                                  // TG == 2, RB == 2
-        if (tg == 1) put(rb);
+        if (tg == 1) merge_put(red, rb, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (tg == 0) add(rb);
+        if (tg == 0) merge_add(red, rb, r16, q4, acc);
       }
       lds_barrier_keep_loads();                            // scratch free again before the next page lands
     }

@@ -599,9 +599,10 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-      const int row = mt * M_TILE + 16 * rr + r16;
+      const int rloc = 16 * rr + r16;
+      const int row = mt * M_TILE + rloc;
       if (row >= p.rows) continue;
-      const float l_row = lrow[16 * rr + r16];
+      const float l_row = lrow[rloc];
       const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
       const int si = row / p.group, hh = kvh * p.group + row % p.group;
       if (nsplit == 1) {
@@ -620,7 +621,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
           // fp16 with a power-of-two scale per 64-dim block: this wave's dims are block `wave`
-          const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row;
+          const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + mt * M_TILE + rloc;
           f32x4 v[4];
           float mx = 0.f;
 #pragma unroll
@@ -1012,11 +1013,17 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
     }
     lds_barrier_keep_loads();
     const float nan = __builtin_nanf("");
+    // The lane's row is made opaque here so that the row-dependent address arithmetic
+    // below is done here: hoisted out of the sequence loop it was spilled, and every
+    // reload of a spilled value waited for all the stores in flight.
+    int lane_row = r16;
+    asm volatile("" : "+v"(lane_row));
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-      const int row = mt * M_TILE + 16 * rr + r16;
+      const int rloc = 16 * rr + lane_row;
+      const int row = mt * M_TILE + rloc;
       if (row >= p.rows) continue;
-      const float l_row = lrow[16 * rr + r16];
+      const float l_row = lrow[rloc];
       const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
       const int si = row / p.group, hh = kvh * p.group + row % p.group;
       if (nsplit == 1) {
@@ -1035,7 +1042,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
           // fp16 with a power-of-two scale per 64-dim block: this wave's dims are block `wave`
-          const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row;
+          const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + mt * M_TILE + rloc;
           f32x4 v[4];
           float mx = 0.f;
 #pragma unroll
