@@ -774,15 +774,15 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const f32x4& a0, const f32x4& a1) {
 }
 
 constexpr int kCombDims = 128;                  // dims per workgroup
-constexpr int kCombGroup = 8;                   // pieces whose loads are in flight together
+constexpr int kCombGroup = 4;                   // pieces whose loads are in flight together
 
 // One workgroup per (sequence, 16 rows, KV head, 128-dim quarter); 16 lanes
 // per row, 8 dims per lane, the pieces in groups of kCombGroup with all their
 // loads in flight at once. (A two-pass kernel with 16 pieces per workgroup in
 // parallel, for sequences cut into many pieces, was slower on the ragged
 // workload: 24 us against 19 us.)
-// G piece groups of kThreads threads each: group g merges pieces 8 g .. 8 g + 7,
-// 8 (g + G) .., and group 0 merges the G states through LDS at the end (G > 1
+// G piece groups of kThreads threads each: group g merges pieces 4 g .. 4 g + 3,
+// 4 (g + G) .., and group 0 merges the G states through LDS at the end (G > 1
 // for sequences cut into many pieces: fewer rounds of dependent loads).
 template <bool F16, int G>
 __global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams p) {
