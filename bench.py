@@ -3,16 +3,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pass of the whole decode path over one batch: the host tile
-scheduler (mla_get_metadata) with its upload, then mla_decode_kvcache (split-KV
-kernel + combine kernel). Inputs are resident in HBM before timing starts. The
-KV pool is replicated R times and steps rotate through the copies so that the
-working set exceeds the 256 MB Infinity Cache and the numbers are HBM numbers.
+The default workload is mtp (batch 128, s_q 2, h_q 128, causal, L ~ U[3072, 5120]):
+the largest configuration, with 256 query rows per KV head. One step is one pass
+of the whole decode path over one batch: the host tile scheduler
+(mla_get_metadata) with its upload, then mla_decode_kvcache (split-KV kernel +
+combine kernel). Inputs are resident in HBM before timing starts. The KV pool is
+replicated R times and steps rotate through the copies so that the working set
+exceeds the 256 MB Infinity Cache and the numbers are HBM numbers.
 
 Prints one JSON line. `value` is achieved algorithmic HBM GB/s of the whole
 step; TFLOPS and roofline fractions ride along. `roofline` is measured on the
-split-KV kernel alone with HIP events on the decode stream. `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+split-KV kernel alone with HIP events attached to its launch on the decode
+stream; `roofline_split_combine` prices the same work over both kernels of the
+call. `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload (plus 1-core samples of the small workloads).
 """
 from __future__ import annotations
 
@@ -99,18 +103,35 @@ class HipEvents:
         self.lib.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(w, target_s: float = 15.0):
-    """Time the oracle on the first sequences of the workload (bounded sample)."""
-    import numpy as np
-    import oracle
+def host_cores() -> int:
+    """CPU threads this process may use: its affinity set, capped by OMP_NUM_THREADS when set
+    (the share of a shared host that the job is given)."""
+    n = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_sample(w, target_s: float):
+    """Oracle decodes of one sequence at a time, cycling through the batch, until target_s of
+    oracle time is spent; returns (sequences done, seconds, algorithmic bytes of them)."""
+    import oracle
     a = w.as_numpy()
     done, t_total, n = [], 0.0, 0
-    while t_total < target_s and n < 64 * w.batch:      # cycle through the batch until the time target
+    while t_total < target_s and n < max(64 * w.batch, 4096):
         b = n % w.batch
         t0 = time.perf_counter()
         oracle.mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
@@ -120,12 +141,30 @@ def cpu_baseline(w, target_s: float = 15.0):
         n += 1
     L = [int(a["cache_seqlens"][b]) for b in done]
     bpt = 1152 if w.kv_format == "bf16" else 656
-    S, H = w.s_q, w.h_q
-    byts = sum(w.h_kv * l * bpt for l in L) + len(done) * S * H * (576 * 2 + 512 * 2 + 4) \
+    byts = sum(w.h_kv * l * bpt for l in L) + len(done) * w.s_q * w.h_q * (576 * 2 + 512 * 2 + 4) \
         + sum((l + 63) // 64 for l in L) * 4 + 4 * len(done)
-    return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} sequence decodes cycling through the {w.batch} sequences in batch order "
-                      f"({sum(L)} cached tokens), {t_total:.2f} s, numpy float64"}
+    return done, t_total, byts, sum(L)
+
+
+def cpu_baseline(w, target_s: float = 15.0, one_core=("tiny", "compute_heavy", "ragged"), one_core_s: float = 3.0):
+    """Time the oracle (as it stands) on a bounded sample of the workload with every host core the
+    job may use (BLAS threads set to match), plus 1-core samples of the small workloads."""
+    from threadpoolctl import threadpool_limits
+    from workloads import named_workload
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
+        done, t_total, byts, toks = _oracle_sample(w, target_s)
+    res = {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{len(done)} sequence decodes cycling through the {w.batch} sequences of {w.name} in batch "
+                     f"order ({toks} cached tokens), {t_total:.2f} s, numpy float64",
+           "cpu_model": cpu_model(), "one_core": {}}
+    for name in one_core:
+        w1 = w if name == w.name else named_workload(name)
+        with threadpool_limits(limits=1):
+            d1, t1, b1, k1 = _oracle_sample(w1, one_core_s)
+        res["one_core"][name] = {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
+                                 "sample": f"{len(d1)} sequence decodes ({k1} cached tokens), {t1:.2f} s"}
+    return res
 
 
 def source_sha256() -> str:
@@ -287,6 +326,19 @@ def split_kernel_name(w) -> str:
     return "splitkv_kernel"
 
 
+def roofline(byts: int, flops: int, ms: float) -> dict:
+    """Algorithmic bytes or FLOPs over a kernel time, against the roofline that bounds the
+    workload: HBM below the ridge (2.5 PFLOP/s / 8 TB/s = 312.5 FLOP/B), dense bf16 MFMA above."""
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / byts < ridge:
+        gbs = byts / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+
 def percentiles(xs, ps):
     """Nearest-rank percentiles of a list of floats."""
     ys = sorted(xs)
@@ -298,7 +350,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="compute_heavy")
+    ap.add_argument("--workload", default="mtp")
     ap.add_argument("--copies", type=int, default=0, help="KV pool replicas to rotate through (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -348,7 +400,9 @@ def main():
     out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.h_q, w.s_q), dtype=torch.float32, device=dev)
     ws = torch.empty((mla.mla_workspace_bytes(w.batch, parts, M, w.h_kv),), dtype=torch.uint8, device=dev)
-    _, s_host = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts)
+    max_blocks = int(w.block_table.shape[1])
+    _, s_host = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts,
+                                          max_blocks_per_seq=max_blocks)
     max_splits = mla.max_splits_of(s_host)
     decoders = [mla.MlaDecoder(q, kv, bt, L_dev, w.dv, meta_dev, splits_dev, w.causal, w.softmax_scale,
                                out=out, lse=lse, workspace=ws, max_splits=max_splits) for kv in kvs]
@@ -367,7 +421,7 @@ def main():
         if stage_done[k] is not None:
             hip.synchronize(stage_done[k])
         m_h, _ = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts,
-                                           out=stage[k])
+                                           max_blocks_per_seq=max_blocks, out=stage[k])
         flat_dev.copy_(stage[k], non_blocking=True)
         if stage_done[k] is None:
             stage_done[k] = hip.create(timing=False)
@@ -409,20 +463,12 @@ def main():
 
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    split_gbs = byts / (split_avg * 1e-3) / 1e9
-    split_tflops = flops / (split_avg * 1e-3) / 1e12
-    intensity = flops / byts
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    bound = "hbm" if intensity < ridge else "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        roof = {"bound": "mfma", "achieved": round(split_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(split_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
-
+    roof = roofline(byts, flops, split_avg)
     split_name = split_kernel_name(w)
     roof["traffic"] = stored_traffic(split_name, w.name)
+    # the same algorithmic work over the decode call's two kernels (split + combine)
+    roof_call = roofline(byts, flops, split_avg + comb_avg)
+    roof_call.pop("traffic")
 
     result = {
         "metric": "paged MLA decode achieved HBM GB/s and TFLOPS (+% of roofline), 1 MI355X",
@@ -449,6 +495,7 @@ def main():
         "algorithmic_bytes": byts,
         "algorithmic_flops": flops,
         "roofline": roof,
+        "roofline_split_combine": roof_call,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

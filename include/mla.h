@@ -93,6 +93,11 @@ int mla_num_parts(int batch, int heads_per_kv, int h_kv, int kv_format, int num_
  *
  *   cache_seqlens_host  int32 [batch], 0 <= L_b (host memory)
  *   heads_per_kv        rows per KV head, s_q * h_q / h_kv (>= 1)
+ *   max_blocks_per_seq  block-table entries per sequence: every L_b must be
+ *                       <= 64 * max_blocks_per_seq, else
+ *                       MLA_ERR_INVALID_ARGUMENT. 0 = not checked here (the
+ *                       decode then returns NaN o and lse for such a sequence;
+ *                       it never reads past the block-table row).
  *   num_cus             0 = query the current device; else plan for this many CUs
  *   num_parts           0 = mla_num_parts(...); else exactly this many ranges (>= 1)
  *   tile_metadata_host  int32 [num_parts][MLA_META_INTS], written. Row p:
@@ -101,7 +106,14 @@ int mla_num_parts(int batch, int heads_per_kv, int h_kv, int kv_format, int num_
  *                         [2] end_b     last sequence (inclusive)
  *                         [3] end_page  one past the last page of end_b
  *                         [4] begin_split index of this piece among begin_b's pieces
- *                         [5..7] 0
+ *                         [5] checksum of the page counts of sequences
+ *                             begin_b .. end_b (0 for an empty range)
+ *                         [6] batch
+ *                         [7] 0
+ *                       The decode recomputes [5] and [6] from its own lengths
+ *                       and batch; a range whose values differ (metadata built
+ *                       for other page counts) gives NaN o and lse for its
+ *                       sequences instead of a silently wrong result.
  *   num_splits_host     int32 [batch + 1], written: prefix sums of the number
  *                       of pieces per sequence (num_splits[0] = 0); sequence b
  *                       owns partial slots [num_splits[b], num_splits[b+1]).
@@ -114,8 +126,8 @@ int mla_num_parts(int batch, int heads_per_kv, int h_kv, int kv_format, int num_
  * when num_parts = 0).
  */
 mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int heads_per_kv, int h_kv,
-                            int kv_format, int num_cus, int num_parts, int32_t* tile_metadata_host,
-                            int32_t* num_splits_host, int* num_parts_out);
+                            int kv_format, int max_blocks_per_seq, int num_cus, int num_parts,
+                            int32_t* tile_metadata_host, int32_t* num_splits_host, int* num_parts_out);
 
 /*
  * Bytes of device workspace mla_decode_kvcache needs for split partials: per
@@ -165,9 +177,9 @@ typedef struct mla_decode_args {
   size_t workspace_bytes;
 
   /* Optional hint: 0 = unknown, else the largest number of pieces of any
-     sequence (max_b num_splits[b+1] - num_splits[b]). Accepted for
-     compatibility; the current combine kernel handles any piece count and
-     does not use it (results never depend on it). */
+     sequence (max_b num_splits[b+1] - num_splits[b]). It selects the combine
+     kernel's shape (more piece groups per workgroup when some sequence has
+     many pieces); any value gives the same results. */
   int max_splits;
 
   /* Optional timing hooks (hipEvent_t or NULL): events[0] and events[1] take
@@ -184,8 +196,12 @@ typedef struct mla_decode_args {
  * Launches the split-KV kernel, then the combine kernel, on `hip_stream`
  * (a hipStream_t; NULL = the null stream). Asynchronous.
  * Rows with no allowed key (L_b = 0, or causal with L_b < s_q) give o = 0,
- * lse = -inf. A block_table entry outside [0, num_pages) is never
- * dereferenced: the affected sequence's o and lse become NaN instead.
+ * lse = -inf. Data-dependent errors that only the device sees are reported in
+ * the outputs, never by a fault: a block_table entry outside [0, num_pages)
+ * is never dereferenced, a length outside [0, 64 * max_blocks_per_seq] never
+ * reads past the block-table row, and metadata built for other page counts
+ * is detected (tile_metadata fields 5 and 6); each of these turns the o and
+ * lse of the affected sequences into NaN.
  */
 mla_status mla_decode_kvcache(const mla_decode_args* args, void* hip_stream);
 

@@ -69,13 +69,15 @@ def _i32p(t: torch.Tensor):
 
 
 def mla_get_metadata_host(cache_seqlens_host: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *,
-                          kv_format="bf16", num_parts: int = 0, num_cus: int = 0,
+                          kv_format="bf16", max_blocks_per_seq: int = 0, num_parts: int = 0, num_cus: int = 0,
                           pin: bool = False, out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Host tile scheduler: int32 CPU tensors (tile_metadata [P, 8], num_splits [B + 1]).
 
-    `out` (optional): a contiguous int32 CPU tensor of P * 8 + B + 1 elements (pinned, say) that
-    receives [tile_metadata | num_splits]; the returned tensors are views of it. The caller must
-    not overwrite a buffer whose previous contents are still being copied to the device."""
+    `max_blocks_per_seq` (the block table's width; 0 = unchecked): a length above 64 times it
+    raises ValueError. `out` (optional): a contiguous int32 CPU tensor of P * 8 + B + 1 elements
+    (pinned, say) that receives [tile_metadata | num_splits]; the returned tensors are views of
+    it. The caller must not overwrite a buffer whose previous contents are still being copied to
+    the device."""
     lib = _lib.load()
     L = cache_seqlens_host
     if L.device.type != "cpu":
@@ -102,8 +104,8 @@ def mla_get_metadata_host(cache_seqlens_host: torch.Tensor, heads_per_kv: int, h
     meta = flat[:parts * META_INTS].view(parts, META_INTS)
     splits = flat[parts * META_INTS:]
     got = ctypes.c_int(0)
-    _lib.check(lib.mla_get_metadata(_i32p(L), B, int(heads_per_kv), int(h_kv), fmt, int(num_cus), parts,
-                                    _i32p(meta), _i32p(splits), ctypes.byref(got)))
+    _lib.check(lib.mla_get_metadata(_i32p(L), B, int(heads_per_kv), int(h_kv), fmt, int(max_blocks_per_seq),
+                                    int(num_cus), parts, _i32p(meta), _i32p(splits), ctypes.byref(got)))
     return meta, splits
 
 
@@ -123,16 +125,19 @@ def packed_metadata(meta: torch.Tensor) -> torch.Tensor:
 
 
 def mla_get_metadata(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *, kv_format="bf16",
-                     num_parts: int = 0, num_cus: int = 0,
+                     max_blocks_per_seq: int = 0, num_parts: int = 0, num_cus: int = 0,
                      device: Optional[torch.device] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Tile-scheduler metadata for one decode step, on `device` (default: the device of
     cache_seqlens, or the current CUDA device for a CPU tensor). Reuse it for every layer.
-    A device-resident cache_seqlens is read back to the host (a synchronising copy)."""
+    A device-resident cache_seqlens is read back to the host (a synchronising copy).
+    `max_blocks_per_seq`: the block table's width, to reject lengths it cannot hold (0: the
+    decode reports such a sequence as NaN instead)."""
     if device is None:
         device = cache_seqlens.device if cache_seqlens.device.type != "cpu" else torch.device("cuda")
     pin = torch.device(device).type == "cuda"
     meta, splits = mla_get_metadata_host(cache_seqlens, heads_per_kv, h_kv, kv_format=kv_format,
-                                         num_parts=num_parts, num_cus=num_cus, pin=pin)
+                                         max_blocks_per_seq=max_blocks_per_seq, num_parts=num_parts,
+                                         num_cus=num_cus, pin=pin)
     flat_d = packed_metadata(meta).to(device, non_blocking=True)
     meta_d, splits_d = split_metadata(flat_d, int(splits.shape[0]) - 1)
     # host-side fact carried along for the decode call's combine-shape hint

@@ -85,7 +85,7 @@ def load() -> ctypes.CDLL:
     lib.mla_num_parts.argtypes = [ctypes.c_int] * 5
     lib.mla_get_metadata.restype = ctypes.c_int
     lib.mla_get_metadata.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_int, i32p, i32p, ctypes.POINTER(ctypes.c_int)]
+                                     ctypes.c_int, ctypes.c_int, i32p, i32p, ctypes.POINTER(ctypes.c_int)]
     lib.mla_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.mla_decode_kvcache.restype = ctypes.c_int

@@ -180,17 +180,46 @@ __device__ __forceinline__ int ld_meta(const int32_t* ptr) {
 
 struct Range {
   int begin_b, begin_page, end_b, end_page, split0;
+  bool stale;             // the metadata was built for other page counts: outputs become NaN
 };
 
-__device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1) {
+// Row `part` of the tile metadata. Returns false for an empty range. Sets
+// r.stale when the range's checksum of page counts (field 5) or the batch
+// (field 6) differs from what this call's lengths give (plan.h, chk_step).
+__device__ __forceinline__ bool read_range(const DecodeParams& p, int part, Range& r) {
+  const int32_t* meta = p.meta + part * kMetaInts;
+  r.begin_b = ld_meta(meta + 0);
+  r.begin_page = ld_meta(meta + 1);
+  r.end_b = min(ld_meta(meta + 2), p.batch - 1);
+  r.end_page = ld_meta(meta + 3);
+  r.split0 = ld_meta(meta + 4);
+  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return false;
+  uint32_t chk = kChkSeed;
+  for (int b = r.begin_b; b <= r.end_b; ++b) chk = chk_step(chk, seq_npages(ld_meta(p.seqlens + b)));
+  r.stale = static_cast<int32_t>(chk) != ld_meta(meta + 5) || ld_meta(meta + 6) != p.batch ||
+            ld_meta(meta + 2) != r.end_b;
+  return true;
+}
+
+// Length and page span of sequence b inside range r. A length outside
+// [0, 64 * max_blocks] is clamped into it (no block-table read past the row)
+// and reported through len_ok; its outputs become NaN.
+__device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1,
+                                          bool& len_ok) {
   const int max_len = p.max_blocks * kPage;
   int len = ld_meta(p.seqlens + b);
+  len_ok = len >= 0 && len <= max_len;
   len = len < 0 ? 0 : (len > max_len ? max_len : len);
   L = len;
   const int np = (len + kPage - 1) / kPage;
   pg0 = (b == r.begin_b) ? max(r.begin_page, 0) : 0;
   pg1 = (b == r.end_b) ? min(r.end_page, np) : np;
   if (pg0 > pg1) pg0 = pg1;
+}
+
+__device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1) {
+  bool len_ok;
+  seq_pages(p, r, b, L, pg0, pg1, len_ok);
 }
 
 // First (sequence, page) at or after sequence b that has a page in the range; nb = end_b + 1 if none.

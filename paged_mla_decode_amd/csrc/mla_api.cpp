@@ -102,8 +102,8 @@ int mla_num_parts(int batch, int heads_per_kv, int h_kv, int kv_format, int num_
 }
 
 mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int heads_per_kv, int h_kv,
-                            int kv_format, int num_cus, int num_parts, int32_t* tile_metadata_host,
-                            int32_t* num_splits_host, int* num_parts_out) {
+                            int kv_format, int max_blocks_per_seq, int num_cus, int num_parts,
+                            int32_t* tile_metadata_host, int32_t* num_splits_host, int* num_parts_out) {
   if (!cache_seqlens_host || !tile_metadata_host || !num_splits_host)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata: null pointer");
   if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata: batch must be >= 1 (got %d)", batch);
@@ -112,10 +112,18 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int he
   if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata: unknown kv_format %d", kv_format);
   if (num_parts < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata: num_parts must be >= 0");
-  for (int b = 0; b < batch; ++b)
+  if (max_blocks_per_seq < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata: max_blocks_per_seq must be >= 0 (0: unchecked)");
+  const int64_t max_len = static_cast<int64_t>(max_blocks_per_seq) * mla::kPage;
+  for (int b = 0; b < batch; ++b) {
     if (cache_seqlens_host[b] < 0)
       return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata: cache_seqlens[%d] = %d is negative", b,
                   cache_seqlens_host[b]);
+    if (max_blocks_per_seq > 0 && cache_seqlens_host[b] > max_len)
+      return fail(MLA_ERR_INVALID_ARGUMENT,
+                  "mla_get_metadata: cache_seqlens[%d] = %d exceeds the block table (%d entries x 64 tokens)", b,
+                  cache_seqlens_host[b], max_blocks_per_seq);
+  }
   const mla::Plan plan = mla::make_plan(heads_per_kv, kv_format);
   int parts = num_parts;
   if (parts == 0) {
@@ -156,6 +164,8 @@ mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
   if (a->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: num_pages must be >= 1");
   if (a->max_blocks_per_seq < 1 || a->bt_stride < a->max_blocks_per_seq)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: need max_blocks_per_seq >= 1 and bt_stride >= it");
+  if (a->max_blocks_per_seq > (1 << 25))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: max_blocks_per_seq above 2^25 (lengths past 2^31 tokens)");
   if (a->num_parts < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: num_parts must be >= 1");
   if (static_cast<int64_t>(a->batch) * a->s_q * a->h_q > (int64_t{1} << 31) / mla::kDv)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: output too large");

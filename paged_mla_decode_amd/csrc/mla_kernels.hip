@@ -438,15 +438,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   const int part = logical / (m_tiles * p.h_kv);
 
   Range r;
-  {
-    const int32_t* meta = p.meta + part * kMetaInts;
-    r.begin_b = ld_meta(meta + 0);
-    r.begin_page = ld_meta(meta + 1);
-    r.end_b = min(ld_meta(meta + 2), p.batch - 1);
-    r.end_page = ld_meta(meta + 3);
-    r.split0 = ld_meta(meta + 4);
-  }
-  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
+  if (!read_range(p, part, r)) return;
 
   const int row = mt * M_TILE + rb * 16 + r16;   // this lane's query row within the KV head
   const bool row_ok = row < p.rows;
@@ -561,7 +553,8 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
 
   for (int b = r.begin_b; b <= r.end_b; ++b) {
     int L, pg0, pg1;
-    seq_pages(p, r, b, L, pg0, pg1);
+    bool len_ok;
+    seq_pages(p, r, b, L, pg0, pg1, len_ok);
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = ld_meta(p.num_splits + b);
     const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
@@ -591,7 +584,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
     f32x4 acc[32];
 #pragma unroll
     for (int d = 0; d < 32; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
+    bool bad = r.stale || !len_ok;
 
     for (int pi = pg0; pi < pg1; ++pi) {
       // page (b, pi) = q0 is in flight into `slot`, q1 (if any) into slot ^ 1
@@ -795,7 +788,7 @@ __global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams
   const int quarter = blockIdx.z % (kDv / kCombDims);
   const int slot0 = ld_meta(p.num_splits + b);
   const int n = ld_meta(p.num_splits + b + 1) - slot0;
-  if (n <= 1) return;                            // the whole workgroup: one piece is written by the split kernel
+  if (n == 1) return;                            // the whole workgroup: one piece is written by the split kernel
   if constexpr (G == 1) {
     if (row >= p.rows) return;
   }
@@ -805,7 +798,9 @@ __global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams
   const int dim0 = quarter * kCombDims + 8 * l16;
   uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
   float* lse_out = p.lse + (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
-  if (slot0 < 0 || slot0 + n > p.max_slots) {   // uniform over the workgroup
+  // no piece (num_splits inconsistent with the ranges) or slots outside the workspace: NaN, never
+  // a read of partials nobody wrote (uniform over the workgroup)
+  if (n <= 0 || slot0 < 0 || slot0 + n > p.max_slots) {
     if (row_ok && grp == 0) {
       *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
       if (l16 == 0 && quarter == 0) *lse_out = __builtin_nanf("");

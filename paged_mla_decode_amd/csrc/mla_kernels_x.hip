@@ -435,15 +435,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
   const int part = logical / (m_tiles * p.h_kv);
 
   Range r;
-  {
-    const int32_t* meta = p.meta + part * kMetaInts;
-    r.begin_b = ld_meta(meta + 0);
-    r.begin_page = ld_meta(meta + 1);
-    r.end_b = min(ld_meta(meta + 2), p.batch - 1);
-    r.end_page = ld_meta(meta + 3);
-    r.split0 = ld_meta(meta + 4);
-  }
-  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
+  if (!read_range(p, part, r)) return;
 
   if (tid == 0) reinterpret_cast<int*>(lds + X::kFlag)[0] = -1;
 
@@ -498,7 +490,8 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
 
   for (int b = r.begin_b; b <= r.end_b; ++b) {
     int L, pg0, pg1;
-    seq_pages(p, r, b, L, pg0, pg1);
+    bool len_ok;
+    seq_pages(p, r, b, L, pg0, pg1, len_ok);
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = ld_meta(p.num_splits + b);
     const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
@@ -554,7 +547,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x_kernel(DecodeParams p) {
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
+    bool bad = r.stale || !len_ok;
 
     while (uq.b == b) {
       const XUnit u = uq;
@@ -851,15 +844,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
   const int part = logical / (m_tiles * p.h_kv);
 
   Range r;
-  {
-    const int32_t* meta = p.meta + part * kMetaInts;
-    r.begin_b = ld_meta(meta + 0);
-    r.begin_page = ld_meta(meta + 1);
-    r.end_b = min(ld_meta(meta + 2), p.batch - 1);
-    r.end_page = ld_meta(meta + 3);
-    r.split0 = ld_meta(meta + 4);
-  }
-  if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return;
+  if (!read_range(p, part, r)) return;
 
   if (tid < 2) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
 
@@ -915,7 +900,8 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
 
   for (int b = r.begin_b; b <= r.end_b; ++b) {
     int L, pg0, pg1;
-    seq_pages(p, r, b, L, pg0, pg1);
+    bool len_ok;
+    seq_pages(p, r, b, L, pg0, pg1, len_ok);
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = ld_meta(p.num_splits + b);
     const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
@@ -965,7 +951,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) acc[dd][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
+    bool bad = r.stale || !len_ok;
 
     // Invariant at the top: unit uq[0] is in LDS and visible to every wave,
     // the loads of uq[1] (if any) are in flight or landed.

@@ -71,6 +71,20 @@ inline int default_parts(const Plan& p, int h_kv, int num_cus) {
   return static_cast<int>(parts);
 }
 
+// Pages of a sequence of length len (>= 0); -1 for a negative length.
+constexpr int32_t seq_npages(int32_t len) { return len < 0 ? -1 : (len >> 6) + ((len & 63) != 0 ? 1 : 0); }
+
+// Checksum of the page counts of the sequences a range covers (tile_metadata
+// field 5), folded in sequence order: each step is a bijection of the running
+// value for a fixed page count, so a change in the page count of any one
+// sequence always changes the result. The decode recomputes it from the
+// device lengths and poisons the range's sequences (NaN) when it differs:
+// the metadata was built for other lengths.
+constexpr uint32_t kChkSeed = 0x6D6C6131u;
+constexpr uint32_t chk_step(uint32_t h, int32_t npages) {
+  return (h ^ static_cast<uint32_t>(npages)) * 0x9E3779B1u + 0x7F4A7C15u;
+}
+
 // Host scheduler (scheduler.cpp). Lengths must be >= 0; num_parts >= 1.
 // Returns the total number of pieces (num_splits[batch]).
 int schedule(const int32_t* seqlens, int batch, int num_parts, int split_cost, int min_pages,

@@ -63,6 +63,7 @@ bool fill(const std::vector<int64_t>& npages, int num_parts, int split_cost, int
     }
     if (meta == nullptr) continue;
     int32_t* m = meta + static_cast<size_t>(p) * kMetaInts;
+    m[6] = batch;
     if (b0 == b && i0 == i) {                              // empty range
       m[0] = -1; m[1] = 0; m[2] = -2; m[3] = 0; m[4] = 0;
       continue;
@@ -81,7 +82,12 @@ bool fill(const std::vector<int64_t>& npages, int num_parts, int split_cost, int
     m[2] = end_b;
     m[3] = static_cast<int32_t>(end_page);
     m[4] = (*pieces)[b0];
-    for (int s = b0; s <= end_b; ++s) (*pieces)[s] += 1;
+    uint32_t chk = kChkSeed;
+    for (int s = b0; s <= end_b; ++s) {
+      (*pieces)[s] += 1;
+      chk = chk_step(chk, static_cast<int32_t>(npages[s]));
+    }
+    m[5] = static_cast<int32_t>(chk);
   }
   return b >= batch;
 }

@@ -33,7 +33,7 @@ def test_args_struct_layout_matches():
     assert b"gfx950" in lib.mla_version()
 
 
-def _meta(L, M=16, hkv=1, fmt=0, cus=256, parts=0):
+def _meta(L, M=16, hkv=1, fmt=0, cus=256, parts=0, maxb=0):
     lib = _lib.load()
     B = len(L)
     Ls = (ctypes.c_int32 * B)(*L)
@@ -43,7 +43,7 @@ def _meta(L, M=16, hkv=1, fmt=0, cus=256, parts=0):
     meta = (ctypes.c_int32 * (parts * 8))()
     splits = (ctypes.c_int32 * (B + 1))()
     got = ctypes.c_int(0)
-    st = lib.mla_get_metadata(Ls, B, M, hkv, fmt, cus, parts, meta, splits, ctypes.byref(got))
+    st = lib.mla_get_metadata(Ls, B, M, hkv, fmt, maxb, cus, parts, meta, splits, ctypes.byref(got))
     return st, [list(meta[p * 8:(p + 1) * 8]) for p in range(parts)], list(splits), got.value
 
 
@@ -57,6 +57,23 @@ def test_get_metadata_rejects_bad_arguments():
     assert st == _lib.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_num_parts(0, 16, 1, 0, 256) == -1
     assert lib.mla_workspace_bytes(0, 4, 16, 1) == 0
+
+
+def test_python_metadata_rejects_lengths_beyond_the_block_table():
+    import torch
+    import paged_mla_decode_amd as mla
+    L = torch.tensor([100, 200], dtype=torch.int32)
+    mla.mla_get_metadata_host(L, 16, 1, num_cus=256, max_blocks_per_seq=4)
+    with pytest.raises(ValueError, match="exceeds the block table"):
+        mla.mla_get_metadata_host(L, 16, 1, num_cus=256, max_blocks_per_seq=3)
+
+
+def test_decode_rejects_huge_block_table_width():
+    lib = _lib.load()
+    a = _valid_args()
+    a.max_blocks_per_seq = (1 << 25) + 1
+    a.bt_stride = a.max_blocks_per_seq
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == _lib.MLA_ERR_UNSUPPORTED
 
 
 def test_workspace_bytes():

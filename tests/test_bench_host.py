@@ -54,3 +54,20 @@ def test_committed_counter_summaries_parse():
         assert 0.9 < ratio < 3.0, f"{os.path.basename(f)}: traffic / algorithmic bytes = {ratio:.3f}"
         got = bench.stored_traffic(kv["kernel"], kv["workload"])
         assert got is None or got == int(kv["hbm_bytes_per_launch"])
+
+
+def test_roofline_picks_the_bound_of_the_workload():
+    # below the ridge (312.5 FLOP/B) the bound is HBM, above it dense bf16 MFMA
+    r = bench.roofline(8_000_000, 8_000_000 * 100, 0.001)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and abs(r["achieved"] - 8000.0) < 1e-6 and r["frac"] == 1.0
+    r = bench.roofline(1_000_000, 2_500_000_000, 0.001)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and abs(r["achieved"] - 2500.0) < 1e-6
+
+
+def test_host_cores_follow_affinity_and_thread_cap(monkeypatch):
+    n = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.host_cores() == 1
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_cores() == n
+    assert isinstance(bench.cpu_model(), str)

@@ -21,10 +21,22 @@ TOL_LSE = 1e-3
 DEV = "cuda"
 
 
-def run_gpu(w, num_parts=0, causal=None):
+def run_gpu(w, num_parts=0, causal=None, meta_lengths=None, edit_splits=None):
+    """Decode `w` on the GPU. meta_lengths: build the metadata for these lengths instead
+    (unchecked against the block table); edit_splits(num_splits_host) may rewrite num_splits."""
     import paged_mla_decode_amd as mla
-    meta, splits = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, w.h_kv, kv_format=w.kv_format,
-                                        num_parts=num_parts, device=torch.device(DEV))
+    dev = torch.device(DEV)
+    if meta_lengths is None and edit_splits is None:
+        meta, splits = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, w.h_kv, kv_format=w.kv_format,
+                                            max_blocks_per_seq=int(w.block_table.shape[1]), num_parts=num_parts,
+                                            device=dev)
+    else:
+        L = w.cache_seqlens if meta_lengths is None else torch.tensor(meta_lengths, dtype=torch.int32)
+        meta_h, splits_h = mla.mla_get_metadata_host(L, w.heads_per_kv, w.h_kv, kv_format=w.kv_format,
+                                                     num_parts=num_parts)
+        if edit_splits is not None:
+            edit_splits(splits_h)
+        meta, splits = meta_h.to(dev), splits_h.to(dev)
     o, lse = mla.mla_decode_kvcache(w.q.to(DEV), w.kvcache.to(DEV), w.block_table.to(DEV), w.cache_seqlens.to(DEV),
                                     w.dv, meta, splits, causal=w.causal if causal is None else causal,
                                     softmax_scale=w.softmax_scale)
@@ -33,12 +45,14 @@ def run_gpu(w, num_parts=0, causal=None):
 
 
 def compare(w, O, LSE, O_ref, LSE_ref, batches=None, label=""):
+    # every output is checked for NaN/inf before any subset is taken
+    assert not np.any(np.isnan(O)) and not np.any(np.isinf(O)), f"{label}: non-finite O"
+    assert not np.any(np.isnan(LSE)) and not np.any(np.isposinf(LSE)), f"{label}: NaN or +inf LSE"
     if batches is not None:
         b = np.asarray(list(batches))
         O, LSE, O_ref, LSE_ref = O[b], LSE[b], O_ref[b], LSE_ref[b]
     empty = np.isneginf(LSE_ref)
     assert np.array_equal(np.isneginf(LSE), empty), f"{label}: -inf LSE pattern differs"
-    assert np.all(np.isfinite(O)), f"{label}: non-finite O"
     dO = float(np.max(np.abs(O - O_ref))) if O.size else 0.0
     fin = ~empty
     dL = float(np.max(np.abs(LSE[fin] - LSE_ref[fin]))) if fin.any() else 0.0
@@ -69,8 +83,18 @@ SMALL = [
     ("hkv2_rows128", 2, 1, 256, 2, [65, 320], False, "bf16"),
     ("hkv2", 2, 1, 32, 2, [90, 400], False, "bf16"),
     ("fp8_rows16", 3, 1, 16, 1, [64, 200, 1025], False, "fp8"),
+    ("fp8_rows8", 2, 1, 8, 1, [129, 3], False, "fp8"),
+    ("fp8_rows32_causal", 3, 2, 16, 1, [2, 130, 777], True, "fp8"),
+    ("fp8_rows48", 2, 1, 48, 1, [70, 500], False, "fp8"),
+    ("fp8_rows64", 2, 1, 64, 1, [65, 900], False, "fp8"),
+    ("fp8_rows64_causal", 2, 2, 32, 1, [3, 600], True, "fp8"),
+    ("fp8_rows80", 2, 1, 80, 1, [33, 97], False, "fp8"),
     ("fp8_rows128", 2, 1, 128, 1, [33, 1100], False, "fp8"),
+    ("fp8_rows192_causal", 2, 3, 64, 1, [31, 161], True, "fp8"),
     ("fp8_rows256_causal", 2, 2, 128, 1, [3, 700], True, "fp8"),
+    ("fp8_hkv2", 2, 1, 32, 2, [90, 400], False, "fp8"),
+    ("fp8_hkv2_rows64", 2, 1, 128, 2, [200, 70], False, "fp8"),
+    ("fp8_hkv2_rows128", 2, 1, 256, 2, [65, 320], False, "fp8"),
 ]
 
 
@@ -96,26 +120,21 @@ def full(name):
     return _FULL[name]
 
 
-# (workload, sequences the oracle checks: None = all)
-FULL_CASES = [
-    ("tiny", None),
-    ("compute_heavy", None),
-    ("mtp", [0, 1, 37, 64, 100, 127]),
-    ("ragged", None),
-    ("uniform_long", [0, 5, 63, 64, 100, 127]),
-    ("fp8", [0, 1, 31, 62, 63]),
-]
+FULL_CASES = ["tiny", "compute_heavy", "mtp", "ragged", "uniform_long", "fp8"]
 
 
-@pytest.mark.parametrize("name,batches", FULL_CASES, ids=[c[0] for c in FULL_CASES])
-def test_full_size_workloads(name, batches):
+@pytest.mark.parametrize("name", FULL_CASES)
+def test_full_size_workloads(name):
+    """Every sequence of every full-size workload against the oracle, in the launch
+    configuration the benchmark times (default number of ranges); a second run must be
+    bitwise identical."""
     w = full(name)
     print(f"[case] full {name}: {w.meta.get('text')} pages={w.num_pages}", flush=True)
     O, LSE = run_gpu(w)
-    if name == "ragged":
-        batches = None
-    O_ref, LSE_ref = oracle.mla_decode_workload(w, batches=batches)
-    compare(w, O, LSE, O_ref, LSE_ref, batches=batches, label=f"full {name}")
+    O2, LSE2 = run_gpu(w)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2), f"full {name}: run-to-run results differ"
+    O_ref, LSE_ref = oracle.mla_decode_workload(w)
+    compare(w, O, LSE, O_ref, LSE_ref, label=f"full {name} (all {w.batch} sequences)")
     if name == "ragged":
         long_b = int(np.argmax(w.cache_seqlens.numpy()))
         compare(w, O, LSE, O_ref, LSE_ref, batches=[long_b], label="full ragged, the 32768-token sequence")
@@ -152,7 +171,7 @@ def test_page_permutation_and_determinism(fmt):
     assert bitwise
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_poisoned_tails_and_unused_pages(fmt, h_q):
     w = make_workload(name="poison", batch=3, s_q=2, h_q=h_q, seqlens=[100, 37, 640], causal=True, kv_format=fmt,
@@ -175,9 +194,10 @@ def test_single_token_gives_value_row_exactly():
 
 
 @pytest.mark.parametrize("h_q", [16, 32, 128])
-def test_empty_and_fully_masked_rows(h_q):
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_empty_and_fully_masked_rows(fmt, h_q):
     w = make_workload(name="empty", batch=4, s_q=2, h_q=h_q, seqlens=[0, 1, 2, 70], causal=True, seed=59,
-                      max_blocks=3)
+                      max_blocks=3, kv_format=fmt)
     for parts in (0, 1, 9):
         O, LSE = run_gpu(w, num_parts=parts)
         O_ref, LSE_ref = oracle.mla_decode_workload(w)
@@ -186,27 +206,86 @@ def test_empty_and_fully_masked_rows(h_q):
         assert np.all(O[1, 0] == 0) and np.all(np.isneginf(LSE[1, :, 0]))
 
 
-@pytest.mark.parametrize("h_q", [16, 32, 64])
-def test_sequences_without_pages_between_pages(h_q):
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_sequences_without_pages_between_pages(fmt, h_q):
     # ranges that start with, and step over, sequences of length 0: the page ring keeps the
     # next pages in flight across them while their (empty) outputs and merges are written
     w = make_workload(name="gaps", batch=8, s_q=1, h_q=h_q, seqlens=[0, 0, 65, 0, 1, 0, 130, 0], seed=63,
-                      max_blocks=3)
+                      max_blocks=3, kv_format=fmt)
     O_ref, LSE_ref = oracle.mla_decode_workload(w)
     for parts in (0, 1, 2, 3):
         O, LSE = run_gpu(w, num_parts=parts)
         compare(w, O, LSE, O_ref, LSE_ref, label=f"gaps h_q={h_q} parts={parts}")
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
-def test_invalid_block_table_entry_poisons_only_its_sequence(h_q):
-    w = make_workload(name="badpage", batch=3, s_q=1, h_q=h_q, seqlens=[100, 200, 50], seed=60)
+def _compare_except(w, O, LSE, nan_batches, label):
+    """The sequences in nan_batches must be NaN everywhere; every other one matches the oracle."""
+    nan_batches = sorted(set(nan_batches))
+    for b in nan_batches:
+        assert np.all(np.isnan(O[b])) and np.all(np.isnan(LSE[b])), f"{label}: sequence {b} must be NaN"
+    ok = [b for b in range(w.batch) if b not in nan_batches]
+    O_ref, LSE_ref = oracle.mla_decode_workload(w, batches=ok)
+    if ok:
+        compare(w, O[ok], LSE[ok], O_ref[ok], LSE_ref[ok], label=label)
+
+
+@pytest.mark.parametrize("h_q", [16, 48, 128])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_invalid_block_table_entry_poisons_only_its_sequence(fmt, h_q):
+    w = make_workload(name="badpage", batch=3, s_q=1, h_q=h_q, seqlens=[100, 200, 50], seed=60, kv_format=fmt)
+    w_ok = make_workload(name="badpage", batch=3, s_q=1, h_q=h_q, seqlens=[100, 200, 50], seed=60, kv_format=fmt)
     w.block_table[1, 2] = 10_000
     O, LSE = run_gpu(w)
-    assert np.all(np.isnan(O[1])) and np.all(np.isnan(LSE[1]))
-    w_ok = make_workload(name="badpage", batch=3, s_q=1, h_q=h_q, seqlens=[100, 200, 50], seed=60)
-    O_ref, LSE_ref = oracle.mla_decode_workload(w_ok, batches=[0, 2])
-    compare(w_ok, O, LSE, O_ref, LSE_ref, batches=[0, 2], label="sequences next to a bad page")
+    _compare_except(w_ok, O, LSE, [1], f"sequences next to a bad page ({fmt}, h_q={h_q})")
+
+
+@pytest.mark.parametrize("h_q", [16, 48, 128])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_length_beyond_the_block_table_poisons_only_its_sequence(fmt, h_q):
+    # metadata built without the block-table check: the decode must not read past the row
+    # (4 entries = 256 tokens) and must report the sequence as NaN
+    w = make_workload(name="toolong", batch=3, s_q=1, h_q=h_q, seqlens=[100, 256, 50], seed=64, kv_format=fmt,
+                      max_blocks=4)
+    w_ok = make_workload(name="toolong", batch=3, s_q=1, h_q=h_q, seqlens=[100, 256, 50], seed=64, kv_format=fmt,
+                         max_blocks=4)
+    w.cache_seqlens[1] = 300
+    O, LSE = run_gpu(w, meta_lengths=[100, 300, 50], num_parts=5)
+    _compare_except(w_ok, O, LSE, [1], f"next to an over-long sequence ({fmt}, h_q={h_q})")
+
+
+@pytest.mark.parametrize("h_q", [16, 48, 128])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_stale_metadata_is_detected(fmt, h_q):
+    # metadata built for other page counts: every sequence is either NaN or correct for the
+    # lengths the decode was given, and the sequence whose page count changed is NaN
+    w = make_workload(name="stale", batch=4, s_q=1, h_q=h_q, seqlens=[100, 300, 50, 700], seed=65, kv_format=fmt,
+                      max_blocks=12)
+    for parts in (0, 3):
+        O, LSE = run_gpu(w, meta_lengths=[100, 200, 50, 700], num_parts=parts)
+        nan_b = [b for b in range(4) if np.all(np.isnan(O[b]))]
+        print(f"[stale] {fmt} h_q={h_q} parts={parts}: NaN sequences {nan_b}", flush=True)
+        assert 1 in nan_b
+        _compare_except(w, O, LSE, nan_b, f"stale metadata ({fmt}, h_q={h_q}, parts={parts})")
+    # lengths that change within the same page counts keep the metadata valid
+    O, LSE = run_gpu(w, meta_lengths=[70, 257, 1, 641], num_parts=3)
+    O_ref, LSE_ref = oracle.mla_decode_workload(w)
+    compare(w, O, LSE, O_ref, LSE_ref, label=f"same page counts ({fmt}, h_q={h_q})")
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_sequence_without_pieces_is_nan(h_q):
+    # num_splits that gives a sequence no piece: nothing is written for it by the split
+    # kernel, and the combine reports NaN instead of leaving the outputs unwritten
+    w = make_workload(name="nopiece", batch=3, s_q=1, h_q=h_q, seqlens=[100, 2000, 50], seed=66)
+
+    def edit(splits):
+        d = (splits[1:] - splits[:-1]).tolist()
+        assert d[0] == 1 and d[2] == 1 and d[1] > 1, d
+        splits[:] = torch.tensor([0, 1, 1, 2], dtype=torch.int32)
+
+    O, LSE = run_gpu(w, num_parts=7, edit_splits=edit)
+    _compare_except(w, O, LSE, [1], f"sequence without pieces (h_q={h_q})")
 
 
 @pytest.mark.parametrize("h_q", [32, 128])
@@ -218,7 +297,8 @@ def test_noncontiguous_q_and_custom_scale(h_q):
     w.q = big[:, :, 4:4 + h_q]                   # head stride 576, batch stride 2*(h_q+8)*576
     assert not w.q.is_contiguous()
     import paged_mla_decode_amd as mla
-    meta, splits = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, 1, device=torch.device(DEV))
+    meta, splits = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, 1, max_blocks_per_seq=w.block_table.shape[1],
+                                        device=torch.device(DEV))
     o, lse = mla.mla_decode_kvcache(big.to(DEV)[:, :, 4:4 + h_q], w.kvcache.to(DEV), w.block_table.to(DEV),
                                     w.cache_seqlens.to(DEV), 512, meta, splits, causal=True, softmax_scale=0.07)
     torch.cuda.synchronize()

@@ -13,7 +13,7 @@ import pytest
 from paged_mla_decode_amd import _lib
 
 
-def schedule(L, M=16, hkv=1, fmt=0, cus=256, parts=0):
+def schedule(L, M=16, hkv=1, fmt=0, cus=256, parts=0, maxb=0):
     lib = _lib.load()
     B = len(L)
     Ls = (ctypes.c_int32 * B)(*[int(x) for x in L])
@@ -22,10 +22,20 @@ def schedule(L, M=16, hkv=1, fmt=0, cus=256, parts=0):
     meta = (ctypes.c_int32 * (parts * 8))()
     splits = (ctypes.c_int32 * (B + 1))()
     got = ctypes.c_int(0)
-    st = lib.mla_get_metadata(Ls, B, M, hkv, fmt, cus, parts, meta, splits, ctypes.byref(got))
+    st = lib.mla_get_metadata(Ls, B, M, hkv, fmt, maxb, cus, parts, meta, splits, ctypes.byref(got))
     assert st == _lib.MLA_OK, lib.mla_last_error()
     assert got.value == parts
     return np.array(meta, dtype=np.int64).reshape(parts, 8), np.array(splits, dtype=np.int64)
+
+
+def range_checksum(npages):
+    """Field 5 of a non-empty range: the page counts of its sequences folded in
+    order with h = (h ^ n) * 0x9E3779B1 + 0x7F4A7C15 (mod 2^32) from 0x6D6C6131,
+    as a signed int32."""
+    h = 0x6D6C6131
+    for n in npages:
+        h = (((h ^ (int(n) & 0xFFFFFFFF)) * 0x9E3779B1) + 0x7F4A7C15) & 0xFFFFFFFF
+    return h - (1 << 32) if h >= (1 << 31) else h
 
 
 def check_schedule(L, meta, splits):
@@ -37,10 +47,13 @@ def check_schedule(L, meta, splits):
     last = (-1, -1)
     for p, m in enumerate(meta):
         bb, bp, eb, ep, s0 = (int(x) for x in m[:5])
-        assert all(int(x) == 0 for x in m[5:])
+        assert int(m[6]) == B and int(m[7]) == 0
         if bb < 0:
+            assert int(m[5]) == 0
             continue
         assert 0 <= bb <= eb < B
+        assert int(m[5]) == range_checksum(npg[bb:eb + 1]), f"range {p}: checksum"
+
         for b in range(bb, eb + 1):
             p0 = bp if b == bb else 0
             p1 = ep if b == eb else int(npg[b])
@@ -135,3 +148,33 @@ def test_default_parts_fill_the_chip():
     assert lib.mla_num_parts(64, 128, 1, 1, 256) == 256
     assert lib.mla_num_parts(64, 256, 1, 1, 256) == 128
     assert lib.mla_num_parts(64, 16, 1, 0, 0) in (-1, 256, lib.mla_device_cu_count(0))
+
+
+def test_checksum_detects_any_single_page_count_change():
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        n = rng.integers(0, 300, size=int(rng.integers(1, 8)))
+        k = int(rng.integers(0, len(n)))
+        m = n.copy()
+        m[k] += int(rng.integers(1, 50)) * (1 if rng.random() < 0.5 or m[k] == 0 else -1)
+        m[k] = max(m[k], 0)
+        if m[k] == n[k]:
+            continue
+        assert range_checksum(n) != range_checksum(m)
+
+
+def test_lengths_beyond_the_block_table_are_rejected():
+    lib = _lib.load()
+    B = 3
+    for L, ok in (([64, 128, 0], True), ([64, 129, 0], False), ([0, 0, 128], True)):
+        Ls = (ctypes.c_int32 * B)(*L)
+        meta = (ctypes.c_int32 * (4 * 8))()
+        splits = (ctypes.c_int32 * (B + 1))()
+        st = lib.mla_get_metadata(Ls, B, 16, 1, 0, 2, 256, 4, meta, splits, None)
+        assert (st == _lib.MLA_OK) == ok, (L, lib.mla_last_error())
+        if not ok:
+            assert st == _lib.MLA_ERR_INVALID_ARGUMENT and b"exceeds the block table" in lib.mla_last_error()
+        # unchecked (0): accepted; the decode reports such a sequence as NaN
+        assert lib.mla_get_metadata(Ls, B, 16, 1, 0, 0, 256, 4, meta, splits, None) == _lib.MLA_OK
+    Ls = (ctypes.c_int32 * B)(1, 2, 3)
+    assert lib.mla_get_metadata(Ls, B, 16, 1, 0, -1, 256, 4, meta, splits, None) == _lib.MLA_ERR_INVALID_ARGUMENT
