@@ -205,6 +205,28 @@ typedef struct mla_decode_args {
  */
 mla_status mla_decode_kvcache(const mla_decode_args* args, void* hip_stream);
 
+/* Capacity of the library's static device scratch (bytes per device). */
+#define MLA_SCRATCH_BYTES (128u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as mla_decode_kvcache, with the split partials in a static device
+ * array of MLA_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends, so nothing is allocated: no hipMalloc, no hipFree,
+ * no allocating library call. args->workspace and args->workspace_bytes are
+ * ignored; every other field means what it does for mla_decode_kvcache, and
+ * the caller still supplies the inputs, o and lse.
+ * A call whose workspace (mla_workspace_bytes for its batch, num_parts,
+ * s_q * h_q / h_kv and h_kv) exceeds MLA_SCRATCH_BYTES returns
+ * MLA_ERR_WORKSPACE_TOO_SMALL before anything is launched.
+ * All calls on one device share that device's scratch, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that may
+ * overlap on one device -- on different streams without ordering, or from
+ * several threads -- race and give wrong results. Order them on one stream.
+ */
+mla_status mla_decode_kvcache_noalloc(const mla_decode_args* args, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,7 +170,8 @@ class MlaDecoder:
     repeatedly (one per layer of a decode step, or a benchmark loop)."""
 
     def __init__(self, q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal=False,
-                 softmax_scale=None, *, out=None, lse=None, workspace=None, events=None, max_splits=None):
+                 softmax_scale=None, *, out=None, lse=None, workspace=None, events=None, max_splits=None,
+                 no_alloc=False):
         dev = q.device
         if dev.type != "cuda":
             raise ValueError("q must be a CUDA (HIP) tensor")
@@ -208,7 +209,7 @@ class MlaDecoder:
         if tuple(out.shape) != (B, S, H, int(dv)) or tuple(lse.shape) != (B, H, S):
             raise ValueError("out must be [batch, s_q, h_q, dv] and lse [batch, h_q, s_q]")
         need = mla_workspace_bytes(B, parts, rows, Hk) if H % max(Hk, 1) == 0 else 0
-        if workspace is None:
+        if workspace is None and not no_alloc:
             workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
         self.tensors = (q, kvcache, block_table, cache_seqlens, tile_metadata, num_splits, out, lse, workspace)
         self.out, self.lse, self.workspace = out, lse, workspace
@@ -232,8 +233,8 @@ class MlaDecoder:
         a.softmax_scale = float(softmax_scale)
         a.o = out.data_ptr()
         a.lse = lse.data_ptr()
-        a.workspace = workspace.data_ptr()
-        a.workspace_bytes = workspace.numel() * workspace.element_size()
+        a.workspace = workspace.data_ptr() if workspace is not None else None
+        a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         if max_splits is None:
             max_splits = getattr(num_splits, "_mla_max_splits", 0)
         a.max_splits = int(max_splits)
@@ -242,6 +243,8 @@ class MlaDecoder:
             self.set_events(events)
         self._args_ref = ctypes.byref(a)
         self._lib = _lib.load()
+        # no_alloc: the library's static scratch replaces the workspace (mla_decode_kvcache_noalloc)
+        self._entry = self._lib.mla_decode_kvcache_noalloc if no_alloc else self._lib.mla_decode_kvcache
         self.device = dev
 
     def set_events(self, events: Sequence) -> None:
@@ -252,7 +255,7 @@ class MlaDecoder:
 
     def run(self, stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
         s = torch.cuda.current_stream(self.device) if stream is None else stream
-        _lib.check(self._lib.mla_decode_kvcache(self._args_ref, ctypes.c_void_p(s.cuda_stream)))
+        _lib.check(self._entry(self._args_ref, ctypes.c_void_p(s.cuda_stream)))
         return self.out, self.lse
 
 

@@ -24,8 +24,9 @@ META_INTS = 8
 
 EXPORTED_SYMBOLS = (
     "mla_last_error", "mla_version", "mla_decode_args_size", "mla_device_cu_count", "mla_num_parts",
-    "mla_get_metadata", "mla_workspace_bytes", "mla_decode_kvcache",
+    "mla_get_metadata", "mla_workspace_bytes", "mla_decode_kvcache", "mla_decode_kvcache_noalloc",
 )
+SCRATCH_BYTES = 128 << 20      # MLA_SCRATCH_BYTES
 
 
 class MlaDecodeArgs(ctypes.Structure):
@@ -90,6 +91,8 @@ def load() -> ctypes.CDLL:
     lib.mla_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.mla_decode_kvcache.restype = ctypes.c_int
     lib.mla_decode_kvcache.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
+    lib.mla_decode_kvcache_noalloc.restype = ctypes.c_int
+    lib.mla_decode_kvcache_noalloc.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     if lib.mla_decode_args_size() != ctypes.sizeof(MlaDecodeArgs):
         raise ImportError(f"mla_decode_args layout mismatch: library {lib.mla_decode_args_size()} bytes, "
                           f"binding {ctypes.sizeof(MlaDecodeArgs)} bytes")

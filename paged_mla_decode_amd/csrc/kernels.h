@@ -49,4 +49,11 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]);
 
+// The library's static device scratch (mla_kernels.hip), the workspace of
+// mla_decode_kvcache_noalloc: kScratchBytes per device, held until the process
+// ends. *ptr receives its device address on the current device (looked up once
+// per device with hipGetSymbolAddress, then cached).
+constexpr size_t kScratchBytes = static_cast<size_t>(128) << 20;
+hipError_t scratch_workspace(void** ptr);
+
 }  // namespace mla

@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
+#include <unordered_map>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -905,6 +907,31 @@ hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStrea
 }
 
 }  // namespace
+
+// Workspace for callers that cannot allocate (mla_decode_kvcache_noalloc):
+// one static array per device, so no call allocates. Host code never uses the
+// array's name as an address (on the host it only names the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_workspace(void** ptr) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;     // device -> address of its copy of `scratch`
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]) {

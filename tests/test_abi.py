@@ -191,3 +191,29 @@ def test_metadata_into_caller_buffer():
     assert m2.data_ptr() == buf.data_ptr()
     with pytest.raises(ValueError):
         mla.mla_get_metadata_host(L, 16, 1, num_cus=256, num_parts=7, out=torch.empty(10, dtype=torch.int32))
+
+
+def test_noalloc_entry_validates_before_launch():
+    # the same argument checks as mla_decode_kvcache; the workspace fields are ignored
+    lib = _lib.load()
+    a = _valid_args()
+    a.d_qk = 512
+    assert lib.mla_decode_kvcache_noalloc(ctypes.byref(a), None) == _lib.MLA_ERR_UNSUPPORTED
+    a = _valid_args()
+    a.h_kv = 3
+    assert lib.mla_decode_kvcache_noalloc(ctypes.byref(a), None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_kvcache_noalloc(None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_entry_rejects_work_beyond_the_scratch():
+    lib = _lib.load()
+    a = _valid_args()
+    a.workspace = None
+    a.workspace_bytes = 0
+    # 1024 sequences x 1024 ranges of 128 rows: far more partials than the static scratch holds
+    a.batch, a.h_q, a.num_parts = 1024, 128, 1024
+    a.q_stride[:] = [128 * 576, 128 * 576, 576]
+    need = lib.mla_workspace_bytes(1024, 1024, 128, 1)
+    assert need > _lib.SCRATCH_BYTES
+    assert lib.mla_decode_kvcache_noalloc(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert b"static scratch holds" in lib.mla_last_error()
