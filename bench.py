@@ -322,7 +322,7 @@ def split_kernel_name(w) -> str:
     """Name of the split kernel a workload runs (128-row tiles above 64 rows per KV head:
     the one-barrier kernel for bf16 pages, the two-barrier one for FP8)."""
     if w.heads_per_kv > 64:
-        return "splitkv_x1_kernel" if w.kv_format == "bf16" else "splitkv_x_kernel"
+        return "splitkv_x1_kernel"
     return "splitkv_kernel"
 
 
