@@ -352,6 +352,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mtp")
     ap.add_argument("--copies", type=int, default=0, help="KV pool replicas to rotate through (0: auto)")
+    ap.add_argument("--metadata", choices=("host", "device"), default="host",
+                    help="where each step's tile-scheduler metadata is computed: on the host (then uploaded) or "
+                         "by the device scheduler kernel from the device lengths (no host work, no copy; the "
+                         "combine then runs without the host's piece-count hint)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -414,7 +418,26 @@ def main():
     stage = [torch.empty((parts * 8 + w.batch + 1,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     stage_done = [None, None]
 
+    if args.metadata == "device":
+        for d in decoders:
+            d.args.max_splits = 0                 # the device path has no host-side piece count
+    meta_ev = []
+
     def step(i, ev=None):
+        if args.metadata == "device":
+            # a1 on the device: the scheduler kernel reads the device lengths, writes the metadata
+            if ev is not None:
+                e0, e1 = hip.create(), hip.create()
+                hip.record(e0, stream)
+            mla.mla_get_metadata_device(L_dev, M, w.h_kv, kv_format=w.kv_format, num_parts=parts, out=flat_dev,
+                                        stream=stream)
+            if ev is not None:
+                hip.record(e1, stream)
+                meta_ev.append((e0, e1))
+            d = decoders[i % copies]
+            d.set_events(ev if ev is not None else (None, None, None))
+            d.run(stream)
+            return
         # a1: host tile scheduler for this step's lengths, uploaded on the decode stream
         # (metadata rows and num_splits share one pinned buffer: one copy)
         k = i & 1
@@ -452,6 +475,10 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     split_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
     comb_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    meta_ms = [hip.elapsed_ms(a, b) for a, b in meta_ev]
+    for a, b in meta_ev:
+        hip.destroy(a)
+        hip.destroy(b)
     for e in evs:
         for x in e:
             hip.destroy(x)
@@ -492,11 +519,14 @@ def main():
         "split_kernel_ms": round(split_avg, 5),
         "split_kernel_ms_p10_p50_p90": [round(x, 5) for x in percentiles(split_ms, (10, 50, 90))],
         "combine_kernel_ms": round(comb_avg, 5),
+        "metadata": args.metadata,
         "algorithmic_bytes": byts,
         "algorithmic_flops": flops,
         "roofline": roof,
         "roofline_split_combine": roof_call,
     }
+    if meta_ms:
+        result["metadata_kernel_ms"] = round(sum(meta_ms) / len(meta_ms), 5)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -130,6 +130,27 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int he
                             int32_t* tile_metadata_host, int32_t* num_splits_host, int* num_parts_out);
 
 /*
+ * The tile scheduler on the device, for lengths that live in device memory
+ * (no copy to the host, no synchronisation: the call only queues one kernel
+ * on hip_stream). Its outputs are those of mla_get_metadata, bit for bit, for
+ * the same lengths, heads_per_kv, h_kv, kv_format and number of ranges.
+ *   cache_seqlens       int32 [batch], device memory
+ *   heads_per_kv, h_kv, kv_format, num_cus, num_parts   as for mla_get_metadata
+ *   tile_metadata       int32 [num_parts][MLA_META_INTS], device memory, written
+ *   num_splits          int32 [batch + 1], device memory, written
+ *   num_parts_out       the number of rows written (host memory; may be NULL)
+ * Limits, checked before the launch (else MLA_ERR_UNSUPPORTED): batch <= 1023
+ * and num_parts <= 1024. Lengths are not checked (the device cannot return a
+ * status): a negative length is scheduled as an empty sequence, and a
+ * sequence of more than 2^20 pages (67,108,864 tokens) makes every range
+ * empty and every piece count 0; the decode reports the sequences concerned
+ * as NaN, as it does for lengths past the block table.
+ */
+mla_status mla_get_metadata_device(const int32_t* cache_seqlens, int batch, int heads_per_kv, int h_kv,
+                                   int kv_format, int num_cus, int num_parts, int32_t* tile_metadata,
+                                   int32_t* num_splits, int* num_parts_out, void* hip_stream);
+
+/*
  * Bytes of device workspace mla_decode_kvcache needs for split partials: per
  * piece of a sequence (at most batch + num_parts pieces) and row, the partial
  * O (fp32; for heads_per_kv > 64, fp16 with a power-of-two fp32 scale per 64
@@ -179,7 +200,9 @@ typedef struct mla_decode_args {
   /* Optional hint: 0 = unknown, else the largest number of pieces of any
      sequence (max_b num_splits[b+1] - num_splits[b]). It selects the combine
      kernel's shape (more piece groups per workgroup when some sequence has
-     many pieces); any value gives the same results. */
+     more than 8 pieces); that changes the order in which such a sequence's
+     pieces are merged, so results for different hints agree to rounding, not
+     bit for bit. The same hint always gives the same bits. */
   int max_splits;
 
   /* Optional timing hooks (hipEvent_t or NULL): events[0] and events[1] take

@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import D_QK, D_V, FP8_RECORD_BYTES, META_INTS, PAGE_TOKENS, MlaDecodeArgs, MlaError
 
 __all__ = [
-    "mla_get_metadata", "mla_decode_kvcache", "mla_workspace_bytes", "mla_num_parts", "MlaDecoder",
+    "mla_get_metadata", "mla_get_metadata_device", "mla_decode_kvcache", "mla_workspace_bytes", "mla_num_parts", "MlaDecoder",
     "MlaError", "kv_format_of", "library_path",
 ]
 
@@ -143,6 +143,41 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int =
     # host-side fact carried along for the decode call's combine-shape hint
     splits_d._mla_max_splits = max_splits_of(splits)
     return meta_d, splits_d
+
+
+def mla_get_metadata_device(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv: int = 1, *, kv_format="bf16",
+                            num_parts: int = 0, num_cus: int = 0, out: Optional[torch.Tensor] = None,
+                            stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The tile scheduler on the device: (tile_metadata [P, 8], num_splits [B + 1]) computed by one
+    kernel from device-resident int32 cache_seqlens, queued on `stream` (default: the current one);
+    nothing is copied to the host. Equal, bit for bit, to mla_get_metadata for the same lengths.
+    `out`: optional contiguous int32 device tensor of P * 8 + B + 1 elements that receives
+    [tile_metadata | num_splits] (the returned tensors are views of it)."""
+    L = cache_seqlens
+    if L.device.type != "cuda" or L.dtype != torch.int32 or L.dim() != 1 or not L.is_contiguous():
+        raise ValueError("cache_seqlens must be a contiguous 1-D int32 device tensor")
+    lib = _lib.load()
+    B = int(L.shape[0])
+    fmt = _fmt_code(kv_format)
+    parts = int(num_parts)
+    if parts == 0:
+        parts = lib.mla_num_parts(B, int(heads_per_kv), int(h_kv), fmt, int(num_cus))
+        if parts < 0:
+            raise ValueError(_lib.last_error())
+    n = parts * META_INTS + B + 1
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int32, device=L.device)
+    elif (out.device != L.device or out.dtype != torch.int32 or not out.is_contiguous() or out.dim() != 1
+          or int(out.shape[0]) != n):
+        raise ValueError(f"out must be a contiguous 1-D int32 tensor of {n} elements on {L.device}")
+    meta, splits = split_metadata(out, B)
+    s = torch.cuda.current_stream(L.device) if stream is None else stream
+    got = ctypes.c_int(0)
+    _lib.check(lib.mla_get_metadata_device(ctypes.c_void_p(L.data_ptr()), B, int(heads_per_kv), int(h_kv), fmt,
+                                           int(num_cus), parts, ctypes.c_void_p(meta.data_ptr()),
+                                           ctypes.c_void_p(splits.data_ptr()), ctypes.byref(got),
+                                           ctypes.c_void_p(s.cuda_stream)))
+    return meta, splits
 
 
 def max_splits_of(num_splits_host: torch.Tensor) -> int:

@@ -24,7 +24,8 @@ META_INTS = 8
 
 EXPORTED_SYMBOLS = (
     "mla_last_error", "mla_version", "mla_decode_args_size", "mla_device_cu_count", "mla_num_parts",
-    "mla_get_metadata", "mla_workspace_bytes", "mla_decode_kvcache", "mla_decode_kvcache_noalloc",
+    "mla_get_metadata", "mla_get_metadata_device", "mla_workspace_bytes", "mla_decode_kvcache",
+    "mla_decode_kvcache_noalloc",
 )
 SCRATCH_BYTES = 128 << 20      # MLA_SCRATCH_BYTES
 
@@ -87,6 +88,10 @@ def load() -> ctypes.CDLL:
     lib.mla_get_metadata.restype = ctypes.c_int
     lib.mla_get_metadata.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, i32p, i32p, ctypes.POINTER(ctypes.c_int)]
+    lib.mla_get_metadata_device.restype = ctypes.c_int
+    lib.mla_get_metadata_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
     lib.mla_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.mla_decode_kvcache.restype = ctypes.c_int

@@ -17,7 +17,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.cpp", "scheduler.cpp", "mla_kernels.hip", "mla_kernels_x.hip"]
+SOURCES = ["mla_api.cpp", "scheduler.cpp", "scheduler_device.hip", "mla_kernels.hip", "mla_kernels_x.hip"]
 # Per-file flags. The 128-row kernel keeps 256 fp32 accumulators per lane next
 # to its Q operands; selecting the VGPR form of MFMA lets the register
 # allocator place accumulators in either register file, which removes the

@@ -49,6 +49,12 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]);
 
+// The tile scheduler on the device (scheduler_device.hip): the same metadata
+// as schedule() in scheduler.cpp, from device lengths, by one workgroup.
+bool schedule_device_supported(int batch, int num_parts, int split_cost, int min_pages);
+hipError_t launch_schedule_device(const int32_t* seqlens, int batch, int num_parts, int split_cost, int32_t* meta,
+                                  int32_t* num_splits, hipStream_t stream);
+
 // The library's static device scratch (mla_kernels.hip), the workspace of
 // mla_decode_kvcache_noalloc: kScratchBytes per device, held until the process
 // ends. *ptr receives its device address on the current device (looked up once

@@ -267,6 +267,34 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens_host, int batch, int he
   return MLA_OK;
 }
 
+mla_status mla_get_metadata_device(const int32_t* cache_seqlens, int batch, int heads_per_kv, int h_kv,
+                                   int kv_format, int num_cus, int num_parts, int32_t* tile_metadata,
+                                   int32_t* num_splits, int* num_parts_out, void* hip_stream) {
+  if (!cache_seqlens || !tile_metadata || !num_splits)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_device: null pointer");
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_device: batch must be >= 1 (got %d)", batch);
+  if (heads_per_kv < 1 || h_kv < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_device: heads_per_kv and h_kv must be >= 1");
+  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_device: unknown kv_format %d", kv_format);
+  if (num_parts < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_device: num_parts must be >= 0");
+  const mla::Plan plan = mla::make_plan(heads_per_kv, kv_format);
+  int parts = num_parts;
+  if (parts == 0) {
+    const int cus = resolve_cus(num_cus);
+    if (cus <= 0) return fail(MLA_ERR_HIP, "mla_get_metadata_device: cannot query the CU count (pass num_cus > 0)");
+    parts = mla::default_parts(plan, h_kv, cus);
+  }
+  if (!mla::schedule_device_supported(batch, parts, plan.split_cost, plan.min_pages))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_get_metadata_device: supports batch <= 1023 and num_parts <= 1024 "
+                "(got %d and %d); use mla_get_metadata", batch, parts);
+  const hipError_t err = mla::launch_schedule_device(cache_seqlens, batch, parts, plan.split_cost, tile_metadata,
+                                                     num_splits, static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return fail(MLA_ERR_HIP, "mla_get_metadata_device: %s", hipGetErrorString(err));
+  if (num_parts_out) *num_parts_out = parts;
+  return MLA_OK;
+}
+
 size_t mla_workspace_bytes(int batch, int num_parts, int heads_per_kv, int h_kv) {
   if (batch < 1 || num_parts < 1 || heads_per_kv < 1 || h_kv < 1) return 0;
   const int slots = batch + num_parts;

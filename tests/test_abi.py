@@ -217,3 +217,16 @@ def test_noalloc_entry_rejects_work_beyond_the_scratch():
     assert need > _lib.SCRATCH_BYTES
     assert lib.mla_decode_kvcache_noalloc(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE_TOO_SMALL
     assert b"static scratch holds" in lib.mla_last_error()
+
+
+def test_device_scheduler_checks_before_launch():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(1 << 20)     # never dereferenced: every case fails before a launch
+    args = lambda B, parts: (fake, B, 16, 1, 0, 256, parts, fake, fake, None, None)
+    assert lib.mla_get_metadata_device(None, 4, 16, 1, 0, 256, 4, fake, fake, None, None) == \
+        _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_get_metadata_device(*args(1024, 4)) == _lib.MLA_ERR_UNSUPPORTED
+    assert b"batch <= 1023" in lib.mla_last_error()
+    assert lib.mla_get_metadata_device(*args(8, 1025)) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_get_metadata_device(fake, 4, 16, 1, 9, 256, 4, fake, fake, None, None) == \
+        _lib.MLA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,92 @@
+"""The tile scheduler on the device (mla_get_metadata_device) against the host one: integer
+work, so the metadata must be identical bit for bit, and a decode with either gives
+bitwise-identical outputs."""
+import numpy as np
+import pytest
+import torch
+
+from workloads import WORKLOAD_SPECS, make_workload, named_workload
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda")
+
+
+def _both(L, M, h_kv=1, fmt="bf16", parts=0):
+    import paged_mla_decode_amd as mla
+    Lt = torch.tensor(np.asarray(L, dtype=np.int32))
+    mh, sh = mla.mla_get_metadata_host(Lt, M, h_kv, kv_format=fmt, num_parts=parts)
+    md, sd = mla.mla_get_metadata_device(Lt.to(DEV), M, h_kv, kv_format=fmt, num_parts=parts)
+    torch.cuda.synchronize()
+    return mh, sh, md.cpu(), sd.cpu()
+
+
+def _same(L, M, h_kv=1, fmt="bf16", parts=0, label=""):
+    mh, sh, md, sd = _both(L, M, h_kv, fmt, parts)
+    assert torch.equal(mh, md), f"{label}: tile_metadata differs"
+    assert torch.equal(sh, sd), f"{label}: num_splits differs"
+
+
+@pytest.mark.parametrize("name", list(WORKLOAD_SPECS))
+def test_device_metadata_equals_host_on_the_workloads(name):
+    spec = WORKLOAD_SPECS[name]
+    w = named_workload(name)
+    print(f"[sched] {name}", flush=True)
+    _same(w.cache_seqlens.numpy(), w.heads_per_kv, 1, w.kv_format, 0, name)
+
+
+def test_device_metadata_equals_host_on_random_lengths():
+    rng = np.random.default_rng(2024)
+    for trial in range(300):
+        B = int(rng.integers(1, 1024))
+        kind = trial % 5
+        if kind == 0:
+            L = rng.integers(0, 5000, size=B)
+        elif kind == 1:
+            L = rng.integers(0, 300, size=B)
+        elif kind == 2:
+            L = np.full(B, int(rng.integers(0, 20000)))
+        elif kind == 3:
+            L = rng.integers(256, 1025, size=B)
+            L[rng.integers(0, B)] = 32768
+        else:
+            L = rng.integers(0, 200000, size=B)
+        if rng.random() < 0.2:
+            L[rng.random(B) < 0.3] = 0
+        M = int(rng.choice([8, 16, 32, 64, 128, 256]))
+        fmt = "fp8" if rng.random() < 0.3 else "bf16"
+        parts = int(rng.choice([0, 1, 2, 3, 7, 64, 255, 1024]))
+        _same(L, M, 1, fmt, parts, f"trial {trial}: B={B} M={M} parts={parts}")
+
+
+@pytest.mark.parametrize("L,parts", [([0], 1), ([0] * 9, 4), ([1], 1024), ([5, 0, 7], 1024), ([64] * 1023, 1),
+                                     ([32768], 1024), ([1, 2, 3], 0)])
+def test_device_metadata_edge_cases(L, parts):
+    _same(L, 128, 1, "bf16", parts, f"L={L[:5]} parts={parts}")
+    _same(L, 16, 1, "bf16", parts, f"L={L[:5]} parts={parts}")
+
+
+@pytest.mark.parametrize("name", ["compute_heavy", "ragged"])
+def test_decode_with_device_metadata_is_bitwise_equal(name):
+    import paged_mla_decode_amd as mla
+    w = named_workload(name)
+    q, kv, bt, L = w.q.to(DEV), w.kvcache.to(DEV), w.block_table.to(DEV), w.cache_seqlens.to(DEV)
+    mh, sh = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, 1, device=DEV)
+    md, sd = mla.mla_get_metadata_device(L, w.heads_per_kv, 1)
+    # the same combine shape for both (the piece-count hint is a host-side fact)
+    hint = int(getattr(sh, "_mla_max_splits", 0))
+    o1, l1 = mla.MlaDecoder(q, kv, bt, L, 512, mh, sh, w.causal, max_splits=hint).run()
+    o2, l2 = mla.MlaDecoder(q, kv, bt, L, 512, md, sd, w.causal, max_splits=hint).run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_device_metadata_for_lengths_past_its_limit_is_empty():
+    # more than 2^20 pages in one sequence: every range empty and no pieces (the decode then
+    # reports every sequence as NaN) -- the host scheduler has no such limit
+    import paged_mla_decode_amd as mla
+    L = torch.tensor([100, (1 << 26) + 64, 5], dtype=torch.int32, device=DEV)
+    md, sd = mla.mla_get_metadata_device(L, 128, 1, num_parts=8)
+    torch.cuda.synchronize()
+    md, sd = md.cpu(), sd.cpu()
+    assert torch.all(md[:, 0] == -1) and torch.all(md[:, 6] == 3) and torch.all(sd == 0)

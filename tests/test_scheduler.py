@@ -178,3 +178,81 @@ def test_lengths_beyond_the_block_table_are_rejected():
         assert lib.mla_get_metadata(Ls, B, 16, 1, 0, 0, 256, 4, meta, splits, None) == _lib.MLA_OK
     Ls = (ctypes.c_int32 * B)(1, 2, 3)
     assert lib.mla_get_metadata(Ls, B, 16, 1, 0, -1, 256, 4, meta, splits, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def cost_line_schedule(L, split_cost, parts):
+    """The device scheduler's algorithm (scheduler_device.hip), in plain Python: on the cost
+    line where sequence b spans [S_b, S_b+1) with S_b+1 - S_b = split_cost + pages_b, a range
+    starting at V ends at E = V + budget and the next one starts at S_e if E - S_e <= split_cost
+    (e: the sequence holding E), else at E - split_cost; the budget is the smallest in
+    [ceil(W / P), ceil(W / P) + split_cost] that places all the work."""
+    import bisect
+    B = len(L)
+    npg = [(int(x) + 63) // 64 for x in L]
+    S = [0]
+    for n in npg:
+        S.append(S[-1] + split_cost + n)
+    W = S[-1]
+    lo = max(1, -(-W // parts))
+    for c in range(split_cost + 1):
+        bd, v, V, ok = lo + c, 0, [], True
+        while v < W:
+            if len(V) == parts or bd <= split_cost:
+                ok = False
+                break
+            V.append(v)
+            E = v + bd
+            if E >= W:
+                nv = W
+            else:
+                e = bisect.bisect_right(S, E) - 1
+                nv = S[e] if E - S[e] <= split_cost else E - split_cost
+            v = nv
+        if ok:
+            break
+    assert ok, "the window always holds a feasible budget"
+    n = len(V)
+    V = V + [W]
+    meta = np.zeros((parts, 8), dtype=np.int64)
+    meta[:, 6] = B
+    seq_at = lambda x: bisect.bisect_right(S[:B], x) - 1
+    count_le = lambda x: bisect.bisect_right(V[:n], x)
+    count_lt = lambda x: bisect.bisect_left(V[:n], x)
+    for p in range(parts):
+        if p >= n:
+            meta[p, :5] = [-1, 0, -2, 0, 0]
+            continue
+        v0, v1 = V[p], V[p + 1]
+        bb = seq_at(v0)
+        if v1 >= W:
+            eb, ep = B - 1, npg[B - 1]
+        else:
+            a = seq_at(v1)
+            eb, ep = (a - 1, npg[a - 1]) if v1 == S[a] else (a, v1 - S[a])
+        meta[p, :6] = [bb, v0 - S[bb], eb, ep, p - (count_le(S[bb]) - 1), range_checksum(npg[bb:eb + 1])]
+    pieces = [count_lt(S[b + 1]) - (count_le(S[b]) - 1) for b in range(B)]
+    return meta, np.concatenate([[0], np.cumsum(pieces)]).astype(np.int64)
+
+
+def test_cost_line_algorithm_matches_the_greedy_scheduler():
+    # the device scheduler's formulation must give the host scheduler's metadata bit for bit
+    rng = np.random.default_rng(21)
+    for trial in range(400):
+        B = int(rng.integers(1, 300))
+        kind = trial % 4
+        if kind == 0:
+            L = rng.integers(0, 5000, size=B)
+        elif kind == 1:
+            L = rng.integers(0, 200, size=B)
+        elif kind == 2:
+            L = np.full(B, int(rng.integers(0, 9000)))
+        else:
+            L = rng.integers(256, 1025, size=B)
+            L[rng.integers(0, B)] = 32768
+        if rng.random() < 0.2:
+            L[rng.random(B) < 0.3] = 0
+        M = int(rng.choice([16, 32, 64, 128, 256]))
+        P = int(rng.choice([1, 2, 3, 7, 64, 128, 256, 1024]))
+        meta, splits = schedule(L, M=M, parts=P)
+        m2, s2 = cost_line_schedule(L, 8 if M > 64 else 3, P)
+        assert np.array_equal(meta, m2) and np.array_equal(splits, s2), (B, M, P)
