@@ -17,5 +17,6 @@ from .mla_oracle import (  # noqa: F401
     attend,
     combine_partials,
     mla_decode,
+    mla_decode_sparse,
     mla_decode_workload,
 )

@@ -228,8 +228,83 @@ def mla_decode(
     return O, LSE
 
 
+def mla_decode_sparse(
+    q_bits: np.ndarray,
+    kvcache: np.ndarray,
+    kv_format: str,
+    block_table: np.ndarray,
+    cache_seqlens: np.ndarray,
+    indices: np.ndarray,
+    *,
+    dv: int = D_V,
+    causal: bool = False,
+    softmax_scale: Optional[float] = None,
+    batches: Optional[Iterable[int]] = None,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """Token-level sparse decode: query token s of sequence b attends only to the cached
+    tokens that indices[b, s, :] names.
+
+    The pages give the call (flash_mla_with_kvcache with is_fp8_kvcache and indices, and
+    get_mla_metadata with topk: section "解码阶段使用示例" of the wmrh.cn FlashMLA深度解析 page)
+    and name it token-level sparse attention over an FP8 KV cache (section "实际性能表现与优化效果");
+    they do not define the indices. Readings taken here:
+      * indices int [B, S, topk]: entry j is a token position t of sequence b's cache
+        (0 <= t < L_b), found through the block table like any cached token; -1 is padding
+        and selects nothing; any other value is an error (ValueError);
+      * the selected keys are the listed entries: a position listed twice counts twice
+        (the softmax runs over the topk list, not over a set);
+      * with causal, keys past L_b - S + s are dropped as in dense decode;
+      * no selected key: O = 0, LSE = -inf.
+    Returns O float64 [B, S, H, dv] and LSE float64 [B, H, S] (the sequences not in
+    `batches` are NaN)."""
+    q = np.asarray(q_bits)
+    B, S, H, _ = q.shape
+    kv = np.asarray(kvcache)
+    Hk = kv.shape[2]
+    if H % Hk:
+        raise ValueError("h_q must be a multiple of h_kv")
+    G = H // Hk
+    idx = np.asarray(indices).astype(np.int64)
+    if idx.ndim != 3 or idx.shape[:2] != (B, S):
+        raise ValueError("indices must be [batch, s_q, topk]")
+    scale = (1.0 / np.sqrt(D_QK)) if softmax_scale is None else float(softmax_scale)
+    seqlens = np.asarray(cache_seqlens).astype(np.int64)
+    bt = np.asarray(block_table)
+    O = np.full((B, S, H, dv), np.nan)
+    LSE = np.full((B, H, S), np.nan)
+    todo = range(B) if batches is None else [int(b) for b in batches]
+    for b in todo:
+        L = int(seqlens[b])
+        if L < 0 or L > bt.shape[1] * PAGE:
+            raise ValueError(f"sequence length {L} outside [0, {bt.shape[1] * PAGE}]")
+        for s in range(S):
+            row = idx[b, s]
+            sel = row[row != -1]
+            if sel.size and (sel.min() < 0 or sel.max() >= L):
+                raise ValueError(f"indices[{b}, {s}] names a position outside [0, {L}) (or below -1)")
+            if causal:
+                sel = sel[sel <= L - S + s]
+            pages = bt[b, sel // PAGE].astype(np.int64)
+            if sel.size and (pages.min() < 0 or pages.max() >= kv.shape[0]):
+                raise ValueError("block_table entry outside the page pool")
+            K = decode_kv_rows(kv[pages, sel % PAGE], kv_format)                # [n, Hk, 576]
+            for kvh in range(Hk):
+                Kh = K[:, kvh, :]
+                heads = slice(kvh * G, (kvh + 1) * G)                          # the G heads of KV head kvh
+                Qs = bf16_bits_to_f64(q[b, s, heads, :])
+                o, lse = attend(Qs, Kh, Kh[:, :dv], scale)
+                O[b, s, heads, :] = o
+                LSE[b, heads, s] = lse
+    return O, LSE
+
+
 def mla_decode_workload(w, batches: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """mla_decode on an object with the fields of workloads.Workload."""
+    """mla_decode (mla_decode_sparse when it carries indices) on an object with the fields of
+    workloads.Workload."""
     a = w.as_numpy()
+    if getattr(w, "indices", None) is not None:
+        return mla_decode_sparse(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
+                                 w.indices.numpy(), dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale,
+                                 batches=batches)
     return mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
                       dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=batches)

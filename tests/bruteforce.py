@@ -80,3 +80,43 @@ def brute_force_decode(q_bits, kv, kv_format, block_table, seqlens, *, dv=512, c
                                   for d in range(dv)]
                     LSE[b][h][s] = math.log(tot)
     return O, LSE
+
+
+def brute_force_sparse_decode(q_bits, kv, kv_format, block_table, seqlens, indices, *, dv=512, causal=False,
+                              scale=None):
+    """Token-level sparse decode by the definition: query token s of sequence b attends to the
+    entries of indices[b][s] (a position t names token t of the sequence: page
+    block_table[b][t // 64], slot t % 64; -1 names nothing; a repeated position counts again;
+    with causal, positions past L_b - S + s are dropped)."""
+    B, S, H = len(q_bits), len(q_bits[0]), len(q_bits[0][0])
+    Hk = len(kv[0][0])
+    G = H // Hk
+    if scale is None:
+        scale = 1.0 / math.sqrt(576.0)
+
+    def row(page, slot, kvh):
+        raw = kv[page][slot][kvh]
+        if kv_format == "bf16":
+            return [bf16_bits_to_float(x) for x in raw]
+        return fp8_record_to_floats(bytes(int(x) for x in raw))
+
+    O = [[[None] * H for _ in range(S)] for _ in range(B)]
+    LSE = [[[None] * S for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        L = int(seqlens[b])
+        for s in range(S):
+            sel = [int(t) for t in indices[b][s] if int(t) != -1 and ((not causal) or int(t) <= L - S + s)]
+            for kvh in range(Hk):
+                keys = [row(int(block_table[b][t // 64]), t % 64, kvh) for t in sel]
+                for g in range(G):
+                    h = kvh * G + g
+                    if not keys:
+                        O[b][s][h] = [0.0] * dv
+                        LSE[b][h][s] = -math.inf
+                        continue
+                    q = [bf16_bits_to_float(x) for x in q_bits[b][s][h]]
+                    e = [math.exp(scale * math.fsum(q[d] * k[d] for d in range(576))) for k in keys]
+                    tot = math.fsum(e)
+                    O[b][s][h] = [math.fsum(e[i] * keys[i][d] for i in range(len(keys))) / tot for d in range(dv)]
+                    LSE[b][h][s] = math.log(tot)
+    return O, LSE

@@ -9,6 +9,9 @@ from .gen import (  # noqa: F401
     Workload,
     WORKLOAD_SPECS,
     make_workload,
+    make_sparse_workload,
+    draw_indices,
+    dense_as_sparse,
     named_workload,
     poison_unused,
     permute_pages,

@@ -56,6 +56,11 @@ class Workload:
     dv: int = D_V
     seed: int = 0
     meta: Dict[str, object] = field(default_factory=dict)
+    indices: Optional[torch.Tensor] = None   # int32 [B, S, topk] for token-level sparse decode (-1: padding)
+
+    @property
+    def topk(self) -> int:
+        return 0 if self.indices is None else int(self.indices.shape[2])
 
     @property
     def batch(self) -> int:
@@ -198,6 +203,42 @@ def make_workload(
     )
 
 
+def draw_indices(L: Sequence[int], s_q: int, topk: int, causal: bool, rng: np.random.Generator,
+                 duplicates: float = 0.0, padding: float = 0.0) -> torch.Tensor:
+    """Seeded token selections for sparse decode: int32 [B, s_q, topk].
+
+    Row (b, s) draws topk distinct positions uniformly, in random order, from the tokens the
+    query may see ([0, L_b), or [0, L_b - s_q + s] when causal); when there are fewer than
+    topk the row lists all of them and pads with -1. `duplicates` is the share of entries
+    then overwritten by another entry of the same row, `padding` the share set to -1."""
+    B = len(L)
+    out = np.full((B, s_q, topk), -1, dtype=np.int64)
+    for b in range(B):
+        for s in range(s_q):
+            n = int(L[b]) - (s_q - 1 - s if causal else 0)
+            n = max(n, 0)
+            k = min(n, topk)
+            if k:
+                out[b, s, :k] = rng.choice(n, size=k, replace=False)
+            if duplicates and k > 1:
+                m = rng.random(topk) < duplicates
+                m[:1] = False
+                src = rng.integers(0, k, size=topk)
+                out[b, s, m & (np.arange(topk) < k)] = out[b, s, src[m & (np.arange(topk) < k)]]
+            if padding:
+                out[b, s, rng.random(topk) < padding] = -1
+            out[b, s] = out[b, s, rng.permutation(topk)]
+    return torch.from_numpy(out.astype(np.int32))
+
+
+def make_sparse_workload(*, topk: int, duplicates: float = 0.0, padding: float = 0.0, **kwargs) -> Workload:
+    """make_workload plus indices drawn by draw_indices from the same seed (after the values)."""
+    w = make_workload(**kwargs)
+    rng = np.random.Generator(np.random.PCG64(int(kwargs.get("seed", 0)) + 7919))
+    w.indices = draw_indices(w.cache_seqlens.tolist(), w.s_q, topk, w.causal, rng, duplicates, padding)
+    return w
+
+
 # The six workloads: the five stated decode configurations, the fourth with
 # its ragged and its uniform run. Lengths are drawn from the seeded rng.
 WORKLOAD_SPECS: Dict[str, Dict[str, object]] = {
@@ -219,6 +260,12 @@ WORKLOAD_SPECS: Dict[str, Dict[str, object]] = {
     "fp8": dict(batch=64, s_q=1, h_q=128, causal=False, kv_format="fp8", seed=5,
                 lengths=("fixed", [8192] * 64),
                 text="batch=64, s_q=1, h_q=128, all L=8192, FP8 656 B/token"),
+    # token-level sparse decode over an FP8 cache: every query token attends to 2048 of its
+    # sequence's 16384 cached tokens
+    "sparse_fp8": dict(batch=64, s_q=1, h_q=128, causal=False, kv_format="fp8", seed=6,
+                       lengths=("fixed", [16384] * 64), topk=2048,
+                       text="batch=64, s_q=1, h_q=128, all L=16384, topk=2048 of them per query token, "
+                            "FP8 656 B/token"),
 }
 
 
@@ -247,6 +294,9 @@ def named_workload(name: str, **overrides) -> Workload:
                       h_kv=1, seqlens=L.tolist(), kv_format=str(spec["kv_format"]),
                       causal=bool(spec["causal"]), seed=int(spec["seed"]),
                       pool_pages=spec.get("pool_pages"), rng=rng)
+    if spec.get("topk"):
+        irng = np.random.Generator(np.random.PCG64(int(spec["seed"]) + 7919))
+        w.indices = draw_indices(w.cache_seqlens.tolist(), w.s_q, int(spec["topk"]), w.causal, irng)
     w.meta["text"] = spec["text"]
     return w
 
@@ -296,3 +346,14 @@ def permute_pages(w: Workload, seed: int) -> Workload:
         n = (Lb + PAGE - 1) // PAGE
         bt[b, :n] = perm[w.block_table[b, :n].long()].to(torch.int32)
     return replace(w, kvcache=kv2, block_table=bt, name=w.name + "+permuted")
+
+
+def dense_as_sparse(w: Workload) -> Workload:
+    """Copy of `w` whose indices list every cached token of each sequence once, in order
+    (topk = the longest sequence, shorter rows padded with -1)."""
+    L = w.cache_seqlens.tolist()
+    topk = max(max(L), 1)
+    idx = torch.full((w.batch, w.s_q, topk), -1, dtype=torch.int32)
+    for b, Lb in enumerate(L):
+        idx[b, :, :Lb] = torch.arange(Lb, dtype=torch.int32)
+    return replace(w, indices=idx, name=w.name + "+as-sparse")
