@@ -44,6 +44,17 @@ def algorithmic_work(w):
     L = [int(x) for x in w.cache_seqlens.tolist()]
     B, S, H, Hk = w.batch, w.s_q, w.h_q, w.h_kv
     bpt = 1152 if w.kv_format == "bf16" else 656
+    if getattr(w, "indices", None) is not None:
+        # sparse: the attended entries of each query token (listed, not -1, inside the causal
+        # mask); each one moves its cached row and its block-table entry; the indices are read
+        import numpy as np
+        idx = w.indices.numpy().astype(np.int64)
+        Lb = np.asarray(L, dtype=np.int64)[:, None, None]
+        s_ = np.arange(S)[None, :, None]
+        att = (idx >= 0) & ((not w.causal) | (idx <= Lb - S + s_))
+        n_att = int(att.sum())
+        byts = (n_att * Hk * bpt + B * S * H * (576 * 2 + 512 * 2 + 4) + n_att * 4 + idx.size * 4 + B * 4)
+        return byts, 2 * (576 + 512) * H * n_att, n_att * Hk * bpt
     kv = sum(Hk * l * bpt for l in L)
     q = B * S * H * 576 * 2
     o = B * S * H * 512 * 2
@@ -127,20 +138,37 @@ def cpu_model() -> str:
 
 def _oracle_sample(w, target_s: float):
     """Oracle decodes of one sequence at a time, cycling through the batch, until target_s of
-    oracle time is spent; returns (sequences done, seconds, algorithmic bytes of them)."""
+    oracle time is spent; returns (sequences done, seconds, algorithmic bytes of them, cached
+    tokens they read)."""
+    import numpy as np
     import oracle
     a = w.as_numpy()
+    sparse = getattr(w, "indices", None) is not None
+    idx = w.indices.numpy() if sparse else None
     done, t_total, n = [], 0.0, 0
     while t_total < target_s and n < max(64 * w.batch, 4096):
         b = n % w.batch
         t0 = time.perf_counter()
-        oracle.mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
-                          dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
+        if sparse:
+            oracle.mla_decode_sparse(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
+                                     idx, dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
+        else:
+            oracle.mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
+                              dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
         t_total += time.perf_counter() - t0
         done.append(b)
         n += 1
-    L = [int(a["cache_seqlens"][b]) for b in done]
     bpt = 1152 if w.kv_format == "bf16" else 656
+    if sparse:
+        # tokens a sequence reads: its attended entries (the accounting of algorithmic_work)
+        L = np.asarray(a["cache_seqlens"], dtype=np.int64)[:, None, None]
+        att = (idx >= 0) & ((not w.causal) | (idx <= L - w.s_q + np.arange(w.s_q)[None, :, None]))
+        per_b = att.reshape(w.batch, -1).sum(axis=1)
+        toks = [int(per_b[b]) for b in done]
+        byts = sum(w.h_kv * t * bpt + 4 * t for t in toks) + len(done) * w.s_q * (
+            w.h_q * (576 * 2 + 512 * 2 + 4) + 4 * w.topk) + 4 * len(done)
+        return done, t_total, byts, sum(toks)
+    L = [int(a["cache_seqlens"][b]) for b in done]
     byts = sum(w.h_kv * l * bpt for l in L) + len(done) * w.s_q * w.h_q * (576 * 2 + 512 * 2 + 4) \
         + sum((l + 63) // 64 for l in L) * 4 + 4 * len(done)
     return done, t_total, byts, sum(L)
@@ -398,26 +426,46 @@ def main():
     L_host = w.cache_seqlens.clone().pin_memory()
     kvs = [w.kvcache.to(dev) for _ in range(copies)]
     M = w.heads_per_kv
-    parts = mla.mla_num_parts(w.batch, M, w.h_kv, w.kv_format)
-    flat_dev = torch.empty((parts * 8 + w.batch + 1,), dtype=torch.int32, device=dev)
-    meta_dev, splits_dev = mla.split_metadata(flat_dev, w.batch)
+    sparse = getattr(w, "indices", None) is not None
+    nseq = w.batch * w.s_q if sparse else w.batch
+    parts = mla.mla_num_parts(nseq, w.h_q // w.h_kv if sparse else M, w.h_kv, w.kv_format)
+    flat_dev = torch.empty((parts * 8 + nseq + 1,), dtype=torch.int32, device=dev)
+    meta_dev, splits_dev = mla.split_metadata(flat_dev, nseq)
+    idx_dev = w.indices.to(dev) if sparse else None
     out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.h_q, w.s_q), dtype=torch.float32, device=dev)
-    ws = torch.empty((mla.mla_workspace_bytes(w.batch, parts, M, w.h_kv),), dtype=torch.uint8, device=dev)
+    from paged_mla_decode_amd import _lib as mla_lib
+    ws_bytes = (mla_lib.load().mla_workspace_bytes_sparse(w.batch, w.s_q, parts, w.h_q, w.h_kv) if sparse
+                else mla.mla_workspace_bytes(w.batch, parts, M, w.h_kv))
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     max_blocks = int(w.block_table.shape[1])
-    _, s_host = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts,
-                                          max_blocks_per_seq=max_blocks)
+
+    def host_metadata(out_buf=None):
+        """a1 on the host: the scheduler's metadata for this step (sparse: from the sizes alone)"""
+        if sparse:
+            m_h, s_h = mla.mla_get_metadata_sparse(w.batch, w.s_q, w.topk, w.h_q, w.h_kv, kv_format=w.kv_format,
+                                                   num_parts=parts, host=True)
+            if out_buf is not None:
+                out_buf.copy_(mla.packed_metadata(m_h))
+            return m_h, s_h
+        return mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts,
+                                         max_blocks_per_seq=max_blocks, out=out_buf)
+
+    _, s_host = host_metadata()
     max_splits = mla.max_splits_of(s_host)
     decoders = [mla.MlaDecoder(q, kv, bt, L_dev, w.dv, meta_dev, splits_dev, w.causal, w.softmax_scale,
-                               out=out, lse=lse, workspace=ws, max_splits=max_splits) for kv in kvs]
+                               out=out, lse=lse, workspace=ws, max_splits=max_splits, indices=idx_dev)
+                for kv in kvs]
     stream = torch.cuda.current_stream(dev)
     hip = HipEvents()
 
     # two pinned staging buffers for the host scheduler's output, used in turn; a buffer is
     # rewritten only after the upload that read it two steps earlier has finished
-    stage = [torch.empty((parts * 8 + w.batch + 1,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    stage = [torch.empty((parts * 8 + nseq + 1,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     stage_done = [None, None]
 
+    if args.metadata == "device" and sparse:
+        raise SystemExit("--metadata device: the sparse metadata depends only on the sizes (host)")
     if args.metadata == "device":
         for d in decoders:
             d.args.max_splits = 0                 # the device path has no host-side piece count
@@ -443,8 +491,7 @@ def main():
         k = i & 1
         if stage_done[k] is not None:
             hip.synchronize(stage_done[k])
-        m_h, _ = mla.mla_get_metadata_host(L_host, M, w.h_kv, kv_format=w.kv_format, num_parts=parts,
-                                           max_blocks_per_seq=max_blocks, out=stage[k])
+        host_metadata(stage[k])
         flat_dev.copy_(stage[k], non_blocking=True)
         if stage_done[k] is None:
             stage_done[k] = hip.create(timing=False)
@@ -512,7 +559,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
                    "d_qk": 576, "d_v": 512, "page": 64, "kv_format": w.kv_format, "causal": w.causal,
-                   "total_kv_tokens": int(w.cache_seqlens.sum()), "num_parts": parts, "kv_copies": copies},
+                   "total_kv_tokens": int(w.cache_seqlens.sum()), "num_parts": parts, "kv_copies": copies,
+                   **({"topk": w.topk} if sparse else {})},
         "tflops": round(tflops, 2),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),

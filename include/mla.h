@@ -151,6 +151,24 @@ mla_status mla_get_metadata_device(const int32_t* cache_seqlens, int batch, int 
                                    int32_t* num_splits, int* num_parts_out, void* hip_stream);
 
 /*
+ * Tile-scheduler metadata for token-level sparse decode (get_mla_metadata
+ * with topk on the wmrh.cn FlashMLA深度解析 page, "解码阶段使用示例"): the
+ * batch * s_q (sequence, query token) pairs are scheduled as sequences of
+ * topk entries with h_q / h_kv query rows each. Fills tile_metadata_host
+ * [num_parts][MLA_META_INTS] and num_splits_host [batch * s_q + 1] as
+ * mla_get_metadata does for those sequences (num_parts = 0: mla_num_parts(
+ * batch * s_q, h_q / h_kv, h_kv, kv_format, num_cus) rows). The metadata
+ * depends only on these sizes: one result serves every step with the same
+ * batch, s_q and topk.
+ */
+mla_status mla_get_metadata_sparse(int batch, int s_q, int topk, int h_q, int h_kv, int kv_format, int num_cus,
+                                   int num_parts, int32_t* tile_metadata_host, int32_t* num_splits_host,
+                                   int* num_parts_out);
+
+/* Bytes of device workspace a sparse mla_decode_kvcache call needs (0 on invalid arguments). */
+size_t mla_workspace_bytes_sparse(int batch, int s_q, int num_parts, int h_q, int h_kv);
+
+/*
  * Bytes of device workspace mla_decode_kvcache needs for split partials: per
  * piece of a sequence (at most batch + num_parts pieces) and row, the partial
  * O (fp32; for heads_per_kv > 64, fp16 with a power-of-two fp32 scale per 64
@@ -209,6 +227,23 @@ typedef struct mla_decode_args {
      the split-KV kernel's own start and end timestamps (the kernel is launched
      with hipExtLaunchKernel), events[2] is recorded after the combine kernel. */
   void* events[3];
+
+  /* Token-level sparse decode (the indices argument of flash_mla_with_kvcache
+     and the topk of get_mla_metadata on the wmrh.cn FlashMLA深度解析 page,
+     "解码阶段使用示例"; "token级稀疏注意力" in "实际性能表现与优化效果").
+     NULL: dense decode. Otherwise int32 [batch, s_q, topk] (last dim
+     contiguous, strides in elements): query token s of sequence b attends only
+     to the cached positions indices[b, s, 0..topk) of sequence b (each found
+     through block_table like any cached token); -1 is padding and selects
+     nothing; a position listed twice counts twice; with causal, positions past
+     L_b - s_q + s are dropped. An entry outside [-1, L_b) gives NaN o and lse
+     for that query token. Every (b, s) pair is then scheduled on its own: the
+     metadata comes from mla_get_metadata_sparse, the workspace size from
+     mla_workspace_bytes_sparse. Needs q's sequence stride to equal s_q times
+     its token stride, and the KV pool of a head to span less than 2^31 bytes. */
+  const int32_t* indices;
+  int64_t idx_stride[2];
+  int topk;
 } mla_decode_args;
 
 /*

@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import D_QK, D_V, FP8_RECORD_BYTES, META_INTS, PAGE_TOKENS, MlaDecodeArgs, MlaError
 
 __all__ = [
-    "mla_get_metadata", "mla_get_metadata_device", "mla_decode_kvcache", "mla_workspace_bytes", "mla_num_parts", "MlaDecoder",
+    "mla_get_metadata", "mla_get_metadata_device", "mla_get_metadata_sparse", "mla_decode_kvcache", "mla_workspace_bytes", "mla_num_parts", "MlaDecoder",
     "MlaError", "kv_format_of", "library_path",
 ]
 
@@ -180,6 +180,34 @@ def mla_get_metadata_device(cache_seqlens: torch.Tensor, heads_per_kv: int, h_kv
     return meta, splits
 
 
+def mla_get_metadata_sparse(batch: int, s_q: int, topk: int, h_q: int, h_kv: int = 1, *, kv_format="bf16",
+                            num_parts: int = 0, num_cus: int = 0, device: Optional[torch.device] = None,
+                            host: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tile-scheduler metadata for token-level sparse decode (every (sequence, query token)
+    pair scheduled as a sequence of topk entries): (tile_metadata [P, 8], num_splits
+    [batch * s_q + 1]) on `device` (default: the current CUDA device), or int32 CPU tensors
+    with host=True."""
+    lib = _lib.load()
+    fmt = _fmt_code(kv_format)
+    parts = int(num_parts)
+    vb = int(batch) * int(s_q)
+    if parts == 0:
+        parts = lib.mla_num_parts(vb, max(int(h_q) // max(int(h_kv), 1), 1), int(h_kv), fmt, int(num_cus))
+        if parts < 0:
+            raise ValueError(_lib.last_error())
+    flat = torch.empty((parts * META_INTS + vb + 1,), dtype=torch.int32, pin_memory=not host)
+    meta, splits = split_metadata(flat, vb)
+    got = ctypes.c_int(0)
+    _lib.check(lib.mla_get_metadata_sparse(int(batch), int(s_q), int(topk), int(h_q), int(h_kv), fmt, int(num_cus),
+                                           parts, _i32p(meta), _i32p(splits), ctypes.byref(got)))
+    if host:
+        return meta, splits
+    flat_d = flat.to(torch.device("cuda") if device is None else device, non_blocking=True)
+    meta_d, splits_d = split_metadata(flat_d, vb)
+    splits_d._mla_max_splits = max_splits_of(splits)
+    return meta_d, splits_d
+
+
 def max_splits_of(num_splits_host: torch.Tensor) -> int:
     """Largest number of pieces of any sequence, from host num_splits [batch + 1]."""
     d = num_splits_host[1:] - num_splits_host[:-1]
@@ -206,7 +234,7 @@ class MlaDecoder:
 
     def __init__(self, q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal=False,
                  softmax_scale=None, *, out=None, lse=None, workspace=None, events=None, max_splits=None,
-                 no_alloc=False):
+                 no_alloc=False, indices=None):
         dev = q.device
         if dev.type != "cuda":
             raise ValueError("q must be a CUDA (HIP) tensor")
@@ -227,8 +255,14 @@ class MlaDecoder:
         Hk = int(kvcache.shape[2])
         if kvcache.shape[1] != PAGE_TOKENS:
             raise ValueError(f"kvcache pages must hold {PAGE_TOKENS} tokens")
-        if num_splits.shape[0] != B + 1 or cache_seqlens.shape[0] != B or block_table.shape[0] != B:
-            raise ValueError("cache_seqlens [batch], block_table [batch, n] and num_splits [batch + 1] must agree with q")
+        nseq = B * S if indices is not None else B
+        if num_splits.shape[0] != nseq + 1 or cache_seqlens.shape[0] != B or block_table.shape[0] != B:
+            raise ValueError("cache_seqlens [batch], block_table [batch, n] and num_splits [batch + 1] (sparse: "
+                             "[batch * s_q + 1]) must agree with q")
+        if indices is not None:
+            _check_tensor("indices", indices, torch.int32, 3, dev)
+            if tuple(indices.shape[:2]) != (B, S) or indices.shape[2] < 1 or indices.stride(-1) != 1:
+                raise ValueError("indices must be int32 [batch, s_q, topk] with a contiguous last dimension")
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(D)
         rows = S * H // max(Hk, 1)
@@ -243,10 +277,16 @@ class MlaDecoder:
             raise ValueError("out and lse must be contiguous")
         if tuple(out.shape) != (B, S, H, int(dv)) or tuple(lse.shape) != (B, H, S):
             raise ValueError("out must be [batch, s_q, h_q, dv] and lse [batch, h_q, s_q]")
-        need = mla_workspace_bytes(B, parts, rows, Hk) if H % max(Hk, 1) == 0 else 0
+        if H % max(Hk, 1) != 0:
+            need = 0
+        elif indices is not None:
+            need = int(_lib.load().mla_workspace_bytes_sparse(B, S, parts, H, Hk))
+        else:
+            need = mla_workspace_bytes(B, parts, rows, Hk)
         if workspace is None and not no_alloc:
             workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-        self.tensors = (q, kvcache, block_table, cache_seqlens, tile_metadata, num_splits, out, lse, workspace)
+        self.tensors = (q, kvcache, block_table, cache_seqlens, tile_metadata, num_splits, out, lse, workspace,
+                        indices)
         self.out, self.lse, self.workspace = out, lse, workspace
         a = MlaDecodeArgs()
         a.q = q.data_ptr()
@@ -273,6 +313,10 @@ class MlaDecoder:
         if max_splits is None:
             max_splits = getattr(num_splits, "_mla_max_splits", 0)
         a.max_splits = int(max_splits)
+        if indices is not None:
+            a.indices = indices.data_ptr()
+            a.idx_stride[:] = [indices.stride(0), indices.stride(1)]
+            a.topk = int(indices.shape[2])
         self.args = a
         if events is not None:
             self.set_events(events)
@@ -296,15 +340,17 @@ class MlaDecoder:
 
 def mla_decode_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
                        dv: int, tile_metadata: torch.Tensor, num_splits: torch.Tensor, causal: bool = False,
-                       softmax_scale: Optional[float] = None, *, out=None, lse=None,
-                       workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                       softmax_scale: Optional[float] = None, *, out=None, lse=None, workspace=None,
+                       indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """o [batch, s_q, h_q, dv] bf16 and lse [batch, h_q, s_q] fp32 for one layer.
 
     q bf16 [batch, s_q, h_q, 576]; kvcache bf16 [pages, 64, h_kv, 576] or uint8
     FP8 records [pages, 64, h_kv, 656]; block_table int32 [batch, max_blocks];
     cache_seqlens int32 [batch]; tile_metadata / num_splits from mla_get_metadata
     for these lengths. causal: query token s of s_q reads keys t <= L - s_q + s.
-    softmax_scale defaults to 1/sqrt(576)."""
+    softmax_scale defaults to 1/sqrt(576). indices (optional, int32 [batch, s_q, topk]):
+    token-level sparse decode -- query token s of sequence b attends only to the listed cached
+    positions of b (-1: padding); its metadata comes from mla_get_metadata_sparse."""
     dec = MlaDecoder(q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal, softmax_scale,
-                     out=out, lse=lse, workspace=workspace)
+                     out=out, lse=lse, workspace=workspace, indices=indices)
     return dec.run()

@@ -24,8 +24,8 @@ META_INTS = 8
 
 EXPORTED_SYMBOLS = (
     "mla_last_error", "mla_version", "mla_decode_args_size", "mla_device_cu_count", "mla_num_parts",
-    "mla_get_metadata", "mla_get_metadata_device", "mla_workspace_bytes", "mla_decode_kvcache",
-    "mla_decode_kvcache_noalloc",
+    "mla_get_metadata", "mla_get_metadata_device", "mla_get_metadata_sparse", "mla_workspace_bytes",
+    "mla_workspace_bytes_sparse", "mla_decode_kvcache", "mla_decode_kvcache_noalloc",
 )
 SCRATCH_BYTES = 128 << 20      # MLA_SCRATCH_BYTES
 
@@ -59,6 +59,9 @@ class MlaDecodeArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("max_splits", ctypes.c_int),
         ("events", ctypes.c_void_p * 3),
+        ("indices", ctypes.c_void_p),
+        ("idx_stride", ctypes.c_int64 * 2),
+        ("topk", ctypes.c_int),
     ]
 
 
@@ -92,6 +95,10 @@ def load() -> ctypes.CDLL:
     lib.mla_get_metadata_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    lib.mla_get_metadata_sparse.restype = ctypes.c_int
+    lib.mla_get_metadata_sparse.argtypes = [ctypes.c_int] * 8 + [i32p, i32p, ctypes.POINTER(ctypes.c_int)]
+    lib.mla_workspace_bytes_sparse.restype = ctypes.c_size_t
+    lib.mla_workspace_bytes_sparse.argtypes = [ctypes.c_int] * 5
     lib.mla_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.mla_decode_kvcache.restype = ctypes.c_int

@@ -183,6 +183,21 @@ struct Range {
   bool stale;             // the metadata was built for other page counts: outputs become NaN
 };
 
+// Length of (virtual) sequence b: its cache length, or topk for sparse decode.
+__device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
+  return p.topk > 0 ? p.topk : ld_meta(p.seqlens + b);
+}
+
+// Index of (sequence b, head, query token s_idx) in lse [batch, h_q, s_q]; for
+// sparse decode b is the virtual sequence b_real * sq_real + s.
+__device__ __forceinline__ int64_t lse_index(const DecodeParams& p, int b, int head, int s_idx) {
+  if (p.topk > 0) {
+    const int br = b / p.sq_real, s = b - br * p.sq_real;
+    return (static_cast<int64_t>(br) * p.h_q + head) * p.sq_real + s;
+  }
+  return (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
+}
+
 // Row `part` of the tile metadata. Returns false for an empty range. Sets
 // r.stale when the range's checksum of page counts (field 5) or the batch
 // (field 6) differs from what this call's lengths give (plan.h, chk_step).
@@ -195,7 +210,7 @@ __device__ __forceinline__ bool read_range(const DecodeParams& p, int part, Rang
   r.split0 = ld_meta(meta + 4);
   if (r.begin_b < 0 || r.begin_b >= p.batch || r.end_b < r.begin_b) return false;
   uint32_t chk = kChkSeed;
-  for (int b = r.begin_b; b <= r.end_b; ++b) chk = chk_step(chk, seq_npages(ld_meta(p.seqlens + b)));
+  for (int b = r.begin_b; b <= r.end_b; ++b) chk = chk_step(chk, seq_npages(seq_len(p, b)));
   r.stale = static_cast<int32_t>(chk) != ld_meta(meta + 5) || ld_meta(meta + 6) != p.batch ||
             ld_meta(meta + 2) != r.end_b;
   return true;
@@ -207,9 +222,16 @@ __device__ __forceinline__ bool read_range(const DecodeParams& p, int part, Rang
 __device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r, int b, int& L, int& pg0, int& pg1,
                                           bool& len_ok) {
   const int max_len = p.max_blocks * kPage;
-  int len = ld_meta(p.seqlens + b);
-  len_ok = len >= 0 && len <= max_len;
-  len = len < 0 ? 0 : (len > max_len ? max_len : len);
+  int len;
+  if (p.topk > 0) {                       // sparse: topk entries; the real length is checked
+    const int real = ld_meta(p.seqlens + b / p.sq_real);
+    len_ok = real >= 0 && real <= max_len;
+    len = p.topk;
+  } else {
+    len = ld_meta(p.seqlens + b);
+    len_ok = len >= 0 && len <= max_len;
+    len = len < 0 ? 0 : (len > max_len ? max_len : len);
+  }
   L = len;
   const int np = (len + kPage - 1) / kPage;
   pg0 = (b == r.begin_b) ? max(r.begin_page, 0) : 0;

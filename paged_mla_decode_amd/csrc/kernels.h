@@ -37,6 +37,17 @@ struct DecodeParams {
   int max_slots;
   int max_splits;             // hint: largest piece count of any sequence (0 = unknown)
   int grid_wgs;               // real workgroups of the split kernel (the grid is padded to a multiple of 8)
+  // Token-level sparse decode (topk > 0): every (sequence, query token) pair is a virtual
+  // sequence vb = b * sq_real + s of topk index entries, so batch = batch_real * sq_real,
+  // s_q = 1, rows = group = h_q / h_kv, and q_sb is the query-token stride. indices
+  // [batch_real, sq_real, topk] name cached positions of sequence b (-1: none); seqlens holds
+  // the real lengths [batch_real].
+  const int32_t* indices;
+  int64_t idx_sb, idx_ss;     // element strides of indices: sequence, query token
+  int topk;                   // 0: dense decode
+  int sq_real;
+  int real_causal;            // sparse: the causal flag (applied to the listed positions)
+  int64_t pool_bytes;         // sparse: bytes from a KV head's base to the end of the pool (< 2^31)
 };
 
 // The row-tile split kernel (mla_kernels_x.hip): 128-row tiles, 8 waves of
@@ -45,6 +56,8 @@ struct DecodeParams {
 // ev_start / ev_stop (may be null) take the kernel's start and end timestamps.
 hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wave, int grid, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_split_x_sparse(const DecodeParams& p, int kv_format, int grid, hipStream_t stream,
+                                 hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]);

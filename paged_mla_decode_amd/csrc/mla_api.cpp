@@ -59,21 +59,28 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Partial O: fp32 for tiles of up to 64 rows; fp16 plus one fp32 scale per 64 dims for
-// 128-row tiles (rows > 64).
-size_t partial_o_bytes(int slots, int rows, int h_kv) {
-  const size_t elem = rows > 64 ? sizeof(uint16_t) : sizeof(float);
-  return align256(static_cast<size_t>(slots) * h_kv * rows * mla::kDv * elem);
-}
-
-size_t partial_scale_bytes(int slots, int rows, int h_kv) {
-  if (rows <= 64) return 0;
-  return align256(static_cast<size_t>(slots) * h_kv * rows * (mla::kDv / 64) * sizeof(float));
-}
-
 size_t partial_lse_bytes(int slots, int rows, int h_kv) {
   return align256(static_cast<size_t>(slots) * h_kv * rows * sizeof(float));
 }
+
+// Partial O: fp32 for tiles of up to 64 rows; fp16 plus one fp32 scale per 64 dims for
+// 128-row tiles (wide: rows > 64, or sparse decode, which always runs 128-row tiles).
+size_t partial_o_bytes(int slots, int rows, int h_kv, bool wide) {
+  const size_t elem = wide ? sizeof(uint16_t) : sizeof(float);
+  return align256(static_cast<size_t>(slots) * h_kv * rows * mla::kDv * elem);
+}
+
+size_t partial_scale_bytes(int slots, int rows, int h_kv, bool wide) {
+  if (!wide) return 0;
+  return align256(static_cast<size_t>(slots) * h_kv * rows * (mla::kDv / 64) * sizeof(float));
+}
+
+size_t workspace_bytes(int batch, int num_parts, int rows, int h_kv, bool wide) {
+  const int slots = batch + num_parts;
+  return partial_o_bytes(slots, rows, h_kv, wide) + partial_scale_bytes(slots, rows, h_kv, wide) +
+         partial_lse_bytes(slots, rows, h_kv);
+}
+
 
 // Validation, argument packing and launch for both decode entry points.
 // use_scratch: the workspace is the library's static scratch (the caller's
@@ -136,9 +143,29 @@ mla_status decode_impl(const mla_decode_args* a, void* hip_stream, bool use_scra
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: o must be 8-byte and lse 4-byte aligned");
 
   const int group = a->h_q / a->h_kv;
-  const int rows = a->s_q * group;
-  const mla::Plan plan = mla::make_plan(rows, a->kv_format);
-  const size_t need = mla_workspace_bytes(a->batch, a->num_parts, rows, a->h_kv);
+  // sparse decode: every (sequence, query token) pair is a virtual sequence of topk entries
+  const bool sparse = a->indices != nullptr;
+  const int vbatch = sparse ? a->batch * a->s_q : a->batch;
+  const int rows = sparse ? group : a->s_q * group;
+  const mla::Plan plan = sparse ? mla::make_plan_sparse(group) : mla::make_plan(rows, a->kv_format);
+  int64_t pool_bytes = 0;
+  if (sparse) {
+    if (a->topk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: topk must be >= 1 with indices");
+    if (a->idx_stride[0] < 0 || a->idx_stride[1] < 0)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: idx_stride must be non-negative");
+    if (static_cast<int64_t>(a->batch) * a->s_q > (1 << 24) ||
+        (static_cast<int64_t>(a->batch - 1) * a->idx_stride[0] + (a->s_q - 1) * a->idx_stride[1] + a->topk) >=
+            (int64_t{1} << 31))
+      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: indices must span less than 2^31 entries");
+    if (a->s_q > 1 && a->q_stride[0] != a->s_q * a->q_stride[1])
+      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: sparse decode needs q's sequence stride to be s_q times its "
+                  "token stride");
+    pool_bytes = static_cast<int64_t>(a->num_pages) * kvb[0];
+    if (pool_bytes > (int64_t{1} << 31) - (int64_t{1} << 16))
+      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: sparse decode needs the KV pool to span less than 2^31 "
+                  "bytes (%lld)", static_cast<long long>(pool_bytes));
+  }
+  const size_t need = workspace_bytes(vbatch, a->num_parts, rows, a->h_kv, plan.wide);
   void* workspace = a->workspace;
   if (use_scratch) {
     if (need > mla::kScratchBytes)
@@ -179,23 +206,33 @@ mla_status decode_impl(const mla_decode_args* a, void* hip_stream, bool use_scra
   p.meta = a->tile_metadata;
   p.num_parts = a->num_parts;
   p.num_splits = a->num_splits;
-  p.batch = a->batch;
-  p.s_q = a->s_q;
+  p.batch = vbatch;
+  p.s_q = sparse ? 1 : a->s_q;
   p.h_q = a->h_q;
   p.h_kv = a->h_kv;
   p.group = group;
   p.rows = rows;
-  p.causal = a->causal ? 1 : 0;
+  p.causal = (a->causal && !sparse) ? 1 : 0;
+  if (sparse) {
+    p.q_sb = a->q_stride[1];                // virtual sequence b * s_q + s starts at q[b, s]
+    p.indices = a->indices;
+    p.idx_sb = a->idx_stride[0];
+    p.idx_ss = a->idx_stride[1];
+    p.topk = a->topk;
+    p.sq_real = a->s_q;
+    p.real_causal = a->causal ? 1 : 0;
+    p.pool_bytes = pool_bytes;
+  }
   p.scale_log2 = static_cast<float>(static_cast<double>(a->softmax_scale) * 1.4426950408889634074);
   p.o = static_cast<uint16_t*>(a->o);
   p.lse = a->lse;
-  const int slots = a->batch + a->num_parts;
+  const int slots = vbatch + a->num_parts;
   char* const ws = static_cast<char*>(workspace);
   p.part_o32 = plan.wide ? nullptr : reinterpret_cast<float*>(ws);
   p.part_o16 = plan.wide ? reinterpret_cast<uint16_t*>(ws) : nullptr;
-  p.part_scale = plan.wide ? reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv)) : nullptr;
-  p.part_lse = reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv) +
-                                        partial_scale_bytes(slots, rows, a->h_kv));
+  p.part_scale = plan.wide ? reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv, true)) : nullptr;
+  p.part_lse = reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv, plan.wide) +
+                                        partial_scale_bytes(slots, rows, a->h_kv, plan.wide));
   p.max_slots = slots;
   p.max_splits = a->max_splits > 0 ? a->max_splits : 0;
   p.grid_wgs = static_cast<int>(wgs);
@@ -297,9 +334,39 @@ mla_status mla_get_metadata_device(const int32_t* cache_seqlens, int batch, int 
 
 size_t mla_workspace_bytes(int batch, int num_parts, int heads_per_kv, int h_kv) {
   if (batch < 1 || num_parts < 1 || heads_per_kv < 1 || h_kv < 1) return 0;
-  const int slots = batch + num_parts;
-  return partial_o_bytes(slots, heads_per_kv, h_kv) + partial_scale_bytes(slots, heads_per_kv, h_kv) +
-         partial_lse_bytes(slots, heads_per_kv, h_kv);
+  return workspace_bytes(batch, num_parts, heads_per_kv, h_kv, heads_per_kv > 64);
+}
+
+size_t mla_workspace_bytes_sparse(int batch, int s_q, int num_parts, int h_q, int h_kv) {
+  if (batch < 1 || s_q < 1 || num_parts < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv) return 0;
+  return workspace_bytes(batch * s_q, num_parts, h_q / h_kv, h_kv, true);
+}
+
+mla_status mla_get_metadata_sparse(int batch, int s_q, int topk, int h_q, int h_kv, int kv_format, int num_cus,
+                                   int num_parts, int32_t* tile_metadata_host, int32_t* num_splits_host,
+                                   int* num_parts_out) {
+  if (!tile_metadata_host || !num_splits_host)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_sparse: null pointer");
+  if (batch < 1 || s_q < 1 || topk < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_sparse: need batch, s_q, topk, h_q, h_kv >= 1 and "
+                "h_q a multiple of h_kv");
+  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_sparse: unknown kv_format %d", kv_format);
+  if (num_parts < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_get_metadata_sparse: num_parts must be >= 0");
+  if (static_cast<int64_t>(batch) * s_q > (1 << 24))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_get_metadata_sparse: batch * s_q above 2^24");
+  const mla::Plan plan = mla::make_plan_sparse(h_q / h_kv);
+  int parts = num_parts;
+  if (parts == 0) {
+    const int cus = resolve_cus(num_cus);
+    if (cus <= 0) return fail(MLA_ERR_HIP, "mla_get_metadata_sparse: cannot query the CU count (pass num_cus > 0)");
+    parts = mla::default_parts(plan, h_kv, cus);
+  }
+  const std::vector<int32_t> lengths(static_cast<size_t>(batch) * s_q, topk);
+  mla::schedule(lengths.data(), batch * s_q, parts, plan.split_cost, plan.min_pages, tile_metadata_host,
+                num_splits_host);
+  if (num_parts_out) *num_parts_out = parts;
+  return MLA_OK;
 }
 
 mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {

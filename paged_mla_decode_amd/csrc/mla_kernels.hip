@@ -679,7 +679,7 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
           w[1] = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
           *reinterpret_cast<u32x2*>(orow + 16 * d) = w;
         }
-        if (q4 == 0) p.lse[(static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx] = lse;
+        if (q4 == 0) p.lse[lse_index(p, b, head, s_idx)] = lse;
       } else {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
@@ -799,7 +799,7 @@ __global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams
   const int head = kvh * p.group + (row_ok ? row % p.group : 0);
   const int dim0 = quarter * kCombDims + 8 * l16;
   uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
-  float* lse_out = p.lse + (static_cast<int64_t>(b) * p.h_q + head) * p.s_q + s_idx;
+  float* lse_out = p.lse + lse_index(p, b, head, s_idx);
   // no piece (num_splits inconsistent with the ranges) or slots outside the workspace: NaN, never
   // a read of partials nobody wrote (uniform over the workgroup)
   if (n <= 0 || slot0 < 0 || slot0 + n > p.max_slots) {
@@ -942,7 +942,9 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   hipEvent_t ev1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
   hipEvent_t ev2 = events ? static_cast<hipEvent_t>(events[2]) : nullptr;
   hipError_t err;
-  if (plan.wide) {
+  if (p.topk > 0) {
+    err = launch_split_x_sparse(p, kv_format, grid, stream, ev0, ev1);
+  } else if (plan.wide) {
     err = launch_split_x(p, kv_format, plan.m_tile / 4, grid, stream, ev0, ev1);
   } else if (plan.rb == 1) {
     err = launch_split<1, 4>(p, kv_format, grid, stream, ev0, ev1);

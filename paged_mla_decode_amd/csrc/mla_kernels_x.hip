@@ -157,9 +157,12 @@ __device__ __forceinline__ void x1_issue(const uint8_t* src, int valid, uint8_t*
 
 // S phase and softmax of one unit for this wave's 16 rows; P^T, rescale factor
 // and flag into the buffers of parity `par`.
+// SPARSE: token 16 tt + 4 q4 + i of the unit is masked unless bit (16 tt + 4 q4 + i) of tokmask is set.
+template <bool SPARSE>
 __device__ __forceinline__ void x1_s(const uint8_t* __restrict__ page, uint8_t* __restrict__ work, const XLane& ln,
                                      int par, int L, int last_ok, int tok0, float scale_log2, int unit_id,
-                                     const bf16x8 (&qf)[X1Layout::kRegChunks], float& m_run, float& l_run) {
+                                     const bf16x8 (&qf)[X1Layout::kRegChunks], float& m_run, float& l_run,
+                                     uint32_t tokmask) {
   using X = X1Layout;
   const int wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   uint8_t* const lds = work - X::kP;
@@ -193,12 +196,20 @@ __device__ __forceinline__ void x1_s(const uint8_t* __restrict__ page, uint8_t* 
     }
   }
   const int lim = min(L - 1, last_ok) - tok0 - 4 * q4;
+  // the attend bits of this lane's 8 tokens (4 q4 + i, 16 + 4 q4 + i), taken here so that the
+  // shifts are not spread over the MFMA phase above
+  uint32_t m8 = 0xFFu;
+  if constexpr (SPARSE) {
+    m8 = ((tokmask >> (4 * q4)) & 0xFu) | (((tokmask >> (16 + 4 * q4)) & 0xFu) << 4);
+    asm volatile("" : "+v"(m8));
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = (16 * tt + i <= lim) ? s[tt][i] * scale_log2 : kNegInf;
+      const bool allowed = (16 * tt + i <= lim) && (!SPARSE || ((m8 >> (4 * tt + i)) & 1u));
+      const float v = allowed ? s[tt][i] * scale_log2 : kNegInf;
       s[tt][i] = v;
       mx = fmaxf(mx, v);
     }
@@ -322,7 +333,8 @@ struct F8Layout {
   static constexpr int kAlpha = kP + 2 * kPBytes;             // [2][128] fp32
   static constexpr int kFlag = kAlpha + 2 * kRows * 4;        // [2] flag words (64 B reserved)
   static constexpr int kQlo = kFlag + 64;                     // lo codes of Q: [128 rows][512 B]
-  static constexpr int kTotal = kQlo + kRows * 512;
+  static constexpr int kQrope = kQlo + kRows * 512;           // RoPE dims of Q (bf16): [128 rows][128 B]
+  static constexpr int kTotal = kQrope + kRows * 128;
 };
 static_assert(F8Layout::kTotal <= 163840, "LDS budget");
 
@@ -363,9 +375,12 @@ __device__ __forceinline__ void f8_issue(const uint8_t* src, int valid, uint8_t*
 // Q of one sequence for this lane's row, in the operand forms of the S phase.
 struct F8Q {
   i32x8 hi[4];          // hi codes of latent group g (MFMA 16x16x128 B operand)
-  bf16x8 rope[2];       // RoPE dims 512 + 32 c + 8 q4 .. + 7 (MFMA 16x16x32 B operand)
   int scale_hi, scale_lo;   // E8M0 scale operands of the hi and lo MFMAs
 };
+
+// Byte offset of RoPE chunk c (8 dims: 512 + 32 (c / 4) + 8 (c % 4) ..) of tile row R in the
+// Q RoPE region: 8 chunks per row, XOR-swizzled by R % 8.
+__device__ __forceinline__ int qrope_off(int R, int c) { return R * 128 + 16 * (c ^ (R & 7)); }
 
 // Split this lane's Q values (row srow, 0 when !row_ok) into hi / lo codes; the
 // lo codes go to LDS (row R of the tile), the rest to q.
@@ -382,8 +397,10 @@ __device__ __forceinline__ void f8_qsetup(const uint16_t* qrow, bool row_ok, int
         raw[4 * g + 2 * h + k] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 128 * g + 64 * h + 16 * q4 + 8 * k)
                                         : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    q.rope[c] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 512 + 32 * c + 8 * q4) : bf16x8{};
+  for (int c = 0; c < 2; ++c) {
+    const u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 512 + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds + F8Layout::kQrope + qrope_off(R, 4 * c + q4)) = v;
+  }
   auto lo16 = [](uint32_t w) { return __uint_as_float(w << 16); };
   auto hi16 = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
   float mx = 0.f;
@@ -426,9 +443,10 @@ __device__ __forceinline__ void f8_qsetup(const uint16_t* qrow, bool row_ok, int
 // S phase and softmax of one FP8 unit for this wave's 16 rows (as x1_s); also
 // returns, for the PV phase, the scales of the lane's 8 tokens (k-slot order of
 // P^T) in the wave's value group.
+template <bool SPARSE>
 __device__ __forceinline__ void f8_s(const uint8_t* __restrict__ page, uint8_t* __restrict__ work, const XLane& ln,
                                      int par, int L, int last_ok, int tok0, float scale_log2, int unit_id,
-                                     const F8Q& q, float& m_run, float& l_run, float (&pv_scale)[8]) {
+                                     const F8Q& q, float& m_run, float& l_run, uint32_t tokmask) {
   using X = F8Layout;
   const int wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   uint8_t* const lds = work - X::kP;
@@ -455,7 +473,8 @@ __device__ __forceinline__ void f8_s(const uint8_t* __restrict__ page, uint8_t* 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16x8 kr = *reinterpret_cast<const bf16x8*>(page + X::kRope + ln.k_off[c] + 2048 * tt);
-      s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, q.rope[c], s[tt], 0, 0, 0);
+      const bf16x8 qr = *reinterpret_cast<const bf16x8*>(lds + X::kQrope + qrope_off(R, 4 * c + q4));
+      s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, qr, s[tt], 0, 0, 0);
     }
   }
   // latent groups: hi and lo MFMAs into one partial per token tile, then the
@@ -482,22 +501,22 @@ __device__ __forceinline__ void f8_s(const uint8_t* __restrict__ page, uint8_t* 
       for (int i = 0; i < 4; ++i) s[tt][i] += sg[i] * part[tt][i];
     }
   }
-  // the PV phase's token scales: group wave / 2 of tokens 4 q4 + i (tile 0) and 16 + 4 q4 + i (tile 1)
-  const int vg = wave >> 1;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const f32x4 sg = scales4(vg, tt);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pv_scale[4 * tt + i] = sg[i];
-  }
 
   const int lim = min(L - 1, last_ok) - tok0 - 4 * q4;
+  // the attend bits of this lane's 8 tokens (4 q4 + i, 16 + 4 q4 + i), taken here so that the
+  // shifts are not spread over the MFMA phase above
+  uint32_t m8 = 0xFFu;
+  if constexpr (SPARSE) {
+    m8 = ((tokmask >> (4 * q4)) & 0xFu) | (((tokmask >> (16 + 4 * q4)) & 0xFu) << 4);
+    asm volatile("" : "+v"(m8));
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = (16 * tt + i <= lim) ? s[tt][i] * scale_log2 : kNegInf;
+      const bool allowed = (16 * tt + i <= lim) && (!SPARSE || ((m8 >> (4 * tt + i)) & 1u));
+      const float v = allowed ? s[tt][i] * scale_log2 : kNegInf;
       s[tt][i] = v;
       mx = fmaxf(mx, v);
     }
@@ -529,10 +548,18 @@ __device__ __forceinline__ void f8_s(const uint8_t* __restrict__ page, uint8_t* 
 // PV phase of one FP8 unit: O^T[dims 64 w + 16 dd + 4 q4 + i][rows 16 rr + r16] += V^T P^T,
 // V^T from the codes (tr8 read, exact conversion, times the token's scale, bf16).
 __device__ __forceinline__ void f8_pv(const uint8_t* __restrict__ page, uint8_t* __restrict__ work, const XLane& ln,
-                                      int par, int unit_id, const float (&pv_scale)[8], f32x4 (&acc)[4][8]) {
+                                      int par, int unit_id, f32x4 (&acc)[4][8]) {
   using X = F8Layout;
   const int wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   uint8_t* const lds = work - X::kP;
+  // scales of the lane's 8 P^T tokens (4 q4 + i, 16 + 4 q4 + i) in the wave's value group w / 2
+  float pv_scale[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const f32x4 sg = *reinterpret_cast<const f32x4*>(page + X::kScales + 4 * (kXHalf * (wave >> 1) + 16 * tt + 4 * q4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv_scale[4 * tt + i] = sg[i];
+  }
   {
     int fl;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
@@ -584,7 +611,106 @@ __device__ __forceinline__ void f8_pv(const uint8_t* __restrict__ page, uint8_t*
   }
 }
 
+
+// ----------------------------------------------------------------------------
+// Token-level sparse decode on the same pipeline. A unit is 32 consecutive
+// entries of a (sequence, query token) pair's index list; lane j < 32 of every
+// wave resolves entry j in three steps, one per pipeline iteration so that
+// each memory round trip has an iteration to land: (A) load the index,
+// (B) check it and load its block-table entry, (C) turn it into the byte
+// offset of the token's row within the KV head's pool (kNoToken when the entry
+// is padding, is dropped by the causal mask, or is invalid) and the unit's
+// attend mask (bit j: entry j is attended). An invalid entry -- outside
+// [-1, L_b), or a block-table entry outside the pool -- makes the pair's
+// outputs NaN. The unit's loads then gather the rows from the pool (the buffer
+// is the whole pool, so kNoToken reads zeros) into the same LDS layout as a
+// dense unit, and the softmax masks with the attend mask.
+// ----------------------------------------------------------------------------
+
+constexpr uint32_t kNoToken = 0x80000000u;        // past any pool the sparse path accepts (< 2^31 bytes)
+
+struct SparseTok {
+  int t = -1;                // the index (step A), then -1 unless attended (step B)
+  int page = -1;             // its block-table entry (step B)
+  bool bad = false;          // the unit holds an invalid entry (uniform)
+};
+
+// Step A: lane j < 32 loads entry j of unit u (none past topk or past the range).
+__device__ __forceinline__ int sparse_load_index(const DecodeParams& p, const Range& r, const XUnit& u, int lane) {
+  const int j = u.pi * kPage + u.hf * kXHalf + lane;
+  if (u.b > r.end_b || lane >= kXHalf || j >= p.topk) return -1;
+  const int br = u.b / p.sq_real, s = u.b - br * p.sq_real;
+  return p.indices[br * p.idx_sb + s * p.idx_ss + j];
+}
+
+// Step B: validate the (landed) index, drop it unless attended, load its block-table entry.
+__device__ __forceinline__ SparseTok sparse_load_page(const DecodeParams& p, const Range& r, const XUnit& u, int idx,
+                                                      int lane) {
+  SparseTok k;
+  if (u.b > r.end_b) return k;
+  const int br = u.b / p.sq_real, s = u.b - br * p.sq_real;
+  const int L = ld_meta(p.seqlens + br);
+  const int max_len = p.max_blocks * kPage;
+  const bool in_list = lane < kXHalf;
+  const bool valid = idx == -1 || (idx >= 0 && idx < L && idx < max_len);
+  const bool attend = in_list && idx >= 0 && valid && (!p.real_causal || idx <= L - p.sq_real + s);
+  k.bad = __builtin_amdgcn_ballot_w64(in_list && !valid) != 0;
+  k.t = attend ? idx : -1;
+  k.page = attend ? p.block_table[static_cast<int64_t>(br) * p.bt_stride + (idx >> 6)] : -1;
+  return k;
+}
+
+// Step C: the byte offset of the row of the (landed) page entry, the attend mask, validity.
+__device__ __forceinline__ uint32_t sparse_offset(const DecodeParams& p, SparseTok& k, uint32_t& mask) {
+  const bool page_ok = k.page >= 0 && k.page < p.num_pages;
+  const bool attend = k.t >= 0;
+  k.bad = k.bad || (__builtin_amdgcn_ballot_w64(attend && !page_ok) != 0);
+  mask = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(attend && page_ok));
+  return (attend && page_ok) ? static_cast<uint32_t>(static_cast<int64_t>(k.page) * p.kv_sp + (k.t & 63) * p.kv_st)
+                             : kNoToken;
+}
+
+// Gathered loads of one sparse unit into an LDS slot: the layout of a dense unit,
+// each token's row at its own offset (lane j of `off` holds token j's). bf16:
+// waves 0..3, token 8 w + l / 8, column blocks 0..8; FP8: all waves, load
+// k = w + 8 j of f8_issue (token 8 (w % 4) + l / 8; scales: token l % 32).
 template <int FMT>
+__device__ __forceinline__ void sparse_issue(const uint8_t* kv_head, int64_t pool_bytes, uint32_t off, uint8_t* dst,
+                                             int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kv_head), 0,
+                                                                        static_cast<int>(pool_bytes), kRawBufferWord3);
+  const uint32_t chunk = 16 * ((lane & 7) ^ (lane >> 3));
+  if constexpr (FMT == kFmtFp8) {
+    using X = F8Layout;
+    const uint32_t tok = static_cast<uint32_t>(__shfl(static_cast<int>(off), 8 * (wave & 3) + (lane >> 3), 64));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int k = wave + kWW * j;
+      if (k < 16) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, tok + chunk, 128 * (k >> 2),
+                                                 0, kPageLoadPolicy);
+      } else if (k < 20) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, tok + chunk, 528, 0,
+                                                 kPageLoadPolicy);
+      } else if (k < X::kLoads) {
+        const uint32_t stok = static_cast<uint32_t>(__shfl(static_cast<int>(off), lane & 31, 64));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + X::kScales + 256 * (k - 20)), 4,
+                                                 stok + 512 + 4 * (lane >> 5), 8 * (k - 20), 0, kPageLoadPolicy);
+      }
+    }
+  } else {
+    if (wave >= kLoadWaves) return;
+    const uint32_t tok = static_cast<uint32_t>(__shfl(static_cast<int>(off), 8 * wave + (lane >> 3), 64));
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int k = wave + kLoadWaves * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * k), 16, tok + chunk, 128 * j, 0,
+                                               kPageLoadPolicy);
+    }
+  }
+}
+
+template <int FMT, bool SPARSE>
 __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
   constexpr bool kFp8 = (FMT == kFmtFp8);
   using X = typename std::conditional<kFp8, F8Layout, X1Layout>::type;
@@ -663,6 +789,30 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
   // ---- prime the ring: units 0 and 1 into slots 0 and 1 ---------------------------------
   XUnit uq[2];
   bool okq[2];
+  // sparse: units 2 and 3 ahead, their resolution state, and the attend masks of units 0..2
+  XUnit uq2{}, uq3{};
+  SparseTok tk2;
+  int idx3 = -1;
+  uint32_t maskq[2] = {0u, 0u};
+  auto next_unit = [&](const XUnit& u) { return (u.b <= r.end_b) ? x_next(p, r, u) : u; };
+  if constexpr (SPARSE) {
+    uq[0] = x_seek(p, r, r.begin_b);
+    uq[1] = next_unit(uq[0]);
+    uq2 = next_unit(uq[1]);
+    uq3 = next_unit(uq2);
+    const int i0 = sparse_load_index(p, r, uq[0], ln.lane), i1 = sparse_load_index(p, r, uq[1], ln.lane);
+    wait_vm_all();
+    SparseTok k0 = sparse_load_page(p, r, uq[0], i0, ln.lane), k1 = sparse_load_page(p, r, uq[1], i1, ln.lane);
+    const int i2 = sparse_load_index(p, r, uq2, ln.lane);
+    wait_vm_all();
+    const uint32_t o0 = sparse_offset(p, k0, maskq[0]), o1 = sparse_offset(p, k1, maskq[1]);
+    okq[0] = !k0.bad;
+    okq[1] = !k1.bad;
+    if (uq[0].b <= r.end_b) sparse_issue<FMT>(kv_head, p.pool_bytes, o0, lds + X::kRing, wave, ln.lane);
+    if (uq[1].b <= r.end_b) sparse_issue<FMT>(kv_head, p.pool_bytes, o1, lds + X::kRing + X::kSlot, wave, ln.lane);
+    tk2 = sparse_load_page(p, r, uq2, i2, ln.lane);      // lands by the first wait of the unit loop
+    idx3 = sparse_load_index(p, r, uq3, ln.lane);
+  } else {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if (i == 0)
@@ -675,6 +825,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
       okq[i] = src != nullptr;
       if (okq[i]) issue(src, unit_valid(uq[i]), lds + X::kRing + i * X::kSlot);
     }
+  }
   }
   int slot = 0;
   int unit_id = 0;
@@ -750,31 +901,52 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
       const int par = unit_id & 1;
       uint8_t* const cur = lds + X::kRing + slot * X::kSlot;
       const int tok0 = u.pi * kPage + u.hf * kXHalf;
-      float pv_scale[8];
+      const uint32_t tokmask = SPARSE ? maskq[0] : ~0u;
       if constexpr (kFp8)
-        f8_s(cur, work, ln, par, L, last_ok, tok0, p.scale_log2, unit_id, q8, m_run, l_run, pv_scale);
+        f8_s<SPARSE>(cur, work, ln, par, L, last_ok, tok0, p.scale_log2, unit_id, q8, m_run, l_run, tokmask);
       else
-        x1_s(cur, work, ln, par, L, last_ok, tok0, p.scale_log2, unit_id, qf, m_run, l_run);
+        x1_s<SPARSE>(cur, work, ln, par, L, last_ok, tok0, p.scale_log2, unit_id, qf, m_run, l_run, tokmask);
       wait_vm_all();                          // this wave's loads of uq[1] landed
-      lds_barrier_keep_loads();               // P^T of u and uq[1] visible; every wave is past PV of u - 1
-      const XUnit un = (uq[1].b <= r.end_b) ? x_next(p, r, uq[1]) : uq[1];
+      XUnit un;
       bool ok_n = true;
+      uint32_t mask_n = 0u, off_n = kNoToken;
+      if constexpr (SPARSE) {
+        // unit 2 ahead: its block-table entries landed with the wait above
+        off_n = sparse_offset(p, tk2, mask_n);
+        ok_n = !tk2.bad;
+        un = uq2;
+      }
+      lds_barrier_keep_loads();               // P^T of u and uq[1] visible; every wave is past PV of u - 1
+      if constexpr (SPARSE) {
+        // the slot of u - 1: its last reader was PV of u - 1, before this barrier
+        if (un.b <= r.end_b)
+          sparse_issue<FMT>(kv_head, p.pool_bytes, off_n, lds + X::kRing + ((slot + 2) % 3) * X::kSlot, wave,
+                            ln.lane);
+        tk2 = sparse_load_page(p, r, uq3, idx3, ln.lane);   // step B of unit 3 ahead (its index landed)
+        uq2 = uq3;
+        uq3 = next_unit(uq3);
+        idx3 = sparse_load_index(p, r, uq3, ln.lane);        // step A of the new unit 3 ahead
+      } else {
+      un = (uq[1].b <= r.end_b) ? x_next(p, r, uq[1]) : uq[1];
       if (un.b <= r.end_b) {
         const uint8_t* src_n = unit_src(un);
         ok_n = src_n != nullptr;
         // the slot of u - 1: its last reader was PV of u - 1, before this barrier
         if (ok_n) issue(src_n, unit_valid(un), lds + X::kRing + ((slot + 2) % 3) * X::kSlot);
       }
+      }
       if constexpr (kFp8)
-        f8_pv(cur, work, ln, par, unit_id, pv_scale, acc);
+        f8_pv(cur, work, ln, par, unit_id, acc);
       else
         x1_pv(cur, work, ln, par, unit_id, acc);
       ++unit_id;
       slot = (slot + 1) % 3;
       uq[0] = uq[1];
       okq[0] = okq[1];
+      maskq[0] = maskq[1];
       uq[1] = un;
       okq[1] = ok_n;
+      maskq[1] = mask_n;
     }
 
     // ---- epilogue: l of every row through LDS; each wave writes its 64 dims ----
@@ -787,7 +959,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
         float lse = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
         if (bad) lse = __builtin_nanf("");
         if (nsplit == 1)
-          p.lse[(static_cast<int64_t>(b) * p.h_q + shead) * p.s_q + s_idx] = lse;
+          p.lse[lse_index(p, b, shead, s_idx)] = lse;
         else if (slot0 + split_idx < p.max_slots && split_idx < nsplit)
           p.part_lse[(static_cast<int64_t>(slot0 + split_idx) * p.h_kv + kvh) * p.rows + srow] = lse;
       }
@@ -862,9 +1034,19 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
   if (rows_per_wave != 32) return hipErrorInvalidValue;
   const dim3 g(grid), blk(kWThreads);
   if (kv_format == kFmtFp8)
-    hipExtLaunchKernelGGL(splitkv_x1_kernel<kFmtFp8>, g, blk, 0, stream, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL((splitkv_x1_kernel<kFmtFp8, false>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
   else
-    hipExtLaunchKernelGGL(splitkv_x1_kernel<kFmtBf16>, g, blk, 0, stream, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL((splitkv_x1_kernel<kFmtBf16, false>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_x_sparse(const DecodeParams& p, int kv_format, int grid, hipStream_t stream,
+                                 hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const dim3 g(grid), blk(kWThreads);
+  if (kv_format == kFmtFp8)
+    hipExtLaunchKernelGGL((splitkv_x1_kernel<kFmtFp8, true>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  else
+    hipExtLaunchKernelGGL((splitkv_x1_kernel<kFmtBf16, true>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ constexpr int kFp8Record = 656;
 constexpr int kMetaInts = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kFmtSparsePlan = 0;   // make_plan ignores the format
 
 struct Plan {
   int wide;        // 1: 128-row tiles (more than 64 rows)
@@ -57,6 +58,15 @@ inline Plan make_plan(int heads_per_kv, int kv_format) {
   // (compute_heavy, ragged; the other workloads move by 1 % or less).
   p.split_cost = p.wide ? 8 : 3;
   p.min_pages = 1;
+  return p;
+}
+
+// Token-level sparse decode: every (sequence, query token) pair is its own
+// virtual sequence of topk entries with h_q / h_kv rows, always on the
+// 128-row kernel (a smaller group leaves rows of the tile idle).
+inline Plan make_plan_sparse(int group) {
+  Plan p = make_plan(65, kFmtSparsePlan);
+  p.m_tiles = (group + p.m_tile - 1) / p.m_tile;
   return p;
 }
 

@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(const int32_t* 
                                                                  int32_t* __restrict__ meta,
                                                                  int32_t* __restrict__ num_splits) {
   __shared__ SchedShared sh;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
 
   // ---- page counts and the exclusive prefix sums of (split_cost + pages) -------------------
   int cost = 0;
