@@ -18,5 +18,6 @@ from .mla_oracle import (  # noqa: F401
     combine_partials,
     mla_decode,
     mla_decode_sparse,
+    mla_sparse_prefill,
     mla_decode_workload,
 )

@@ -298,6 +298,55 @@ def mla_decode_sparse(
     return O, LSE
 
 
+def mla_sparse_prefill(
+    q_bits: np.ndarray,
+    kv_bits: np.ndarray,
+    indices: np.ndarray,
+    softmax_scale: float,
+    *,
+    dv: int = D_V,
+    tokens: Optional[Iterable[int]] = None,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """Sparse prefill: query token s attends, for each KV head, to the keys that
+    indices[s, kvh, :] names (flash_mla_sparse_fwd(q [s_q, h_q, d_qk], kv [s_kv, h_kv, d_qk],
+    indices [s_q, h_kv, topk], sm_scale, d_v=512): section "稀疏预填充使用" of the wmrh.cn
+    FlashMLA深度解析 page). The page gives only the arguments. Readings taken here: kv rows are
+    bf16 and contiguous (no pages); an entry is a row of kv in [0, s_kv), -1 is padding, any
+    other value is an error (ValueError); listed entries count as listed; query head h reads KV
+    head h // (h_q / h_kv); V is the first dv dims of each row; no key: O = 0, LSE = -inf; the
+    call returns O [s_q, h_q, dv] and the natural-log LSE [s_q, h_q].
+    Returns float64 arrays; with `tokens`, only those query tokens, in that order
+    (O [len(tokens), h_q, dv], LSE [len(tokens), h_q])."""
+    q = np.asarray(q_bits)
+    kv = np.asarray(kv_bits)
+    if q.ndim != 3 or q.shape[-1] != D_QK or kv.ndim != 3 or kv.shape[-1] != D_QK:
+        raise ValueError("q must be [s_q, h_q, 576] and kv [s_kv, h_kv, 576]")
+    Sq, H, _ = q.shape
+    Skv, Hk, _ = kv.shape
+    if H % Hk:
+        raise ValueError("h_q must be a multiple of h_kv")
+    G = H // Hk
+    idx = np.asarray(indices)
+    if idx.ndim != 3 or idx.shape[:2] != (Sq, Hk):
+        raise ValueError("indices must be [s_q, h_kv, topk]")
+    todo = list(range(Sq)) if tokens is None else [int(t) for t in tokens]
+    O = np.full((len(todo), H, dv), np.nan)
+    LSE = np.full((len(todo), H), np.nan)
+    for i, s in enumerate(todo):
+        for kvh in range(Hk):
+            row = idx[s, kvh].astype(np.int64)
+            keep = row != -1                                                    # -1: padding
+            sel = row[keep]
+            if sel.size and (sel.min() < 0 or sel.max() >= Skv):
+                raise ValueError(f"indices[{s}, {kvh}] names a row outside [0, {Skv}) (or below -1)")
+            K = bf16_bits_to_f64(kv[sel, kvh, :])                               # [n, 576]
+            heads = slice(kvh * G, (kvh + 1) * G)
+            o, lse = attend(bf16_bits_to_f64(q[s, heads, :]), K, K[:, :dv], float(softmax_scale))
+            O[i, heads, :] = o
+            LSE[i, heads] = lse
+    return O, LSE
+
+
 def mla_decode_workload(w, batches: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """mla_decode (mla_decode_sparse when it carries indices) on an object with the fields of
     workloads.Workload."""

@@ -120,3 +120,27 @@ def brute_force_sparse_decode(q_bits, kv, kv_format, block_table, seqlens, indic
                     O[b][s][h] = [math.fsum(e[i] * keys[i][d] for i in range(len(keys))) / tot for d in range(dv)]
                     LSE[b][h][s] = math.log(tot)
     return O, LSE
+
+
+def brute_force_sparse_prefill(q_bits, kv_bits, indices, scale, *, dv=512):
+    """Sparse prefill by the definition: query token s, head h attends to the rows
+    indices[s][h // G] of kv (its KV head; -1 names nothing; repeats count again)."""
+    Sq, H = len(q_bits), len(q_bits[0])
+    Hk = len(kv_bits[0])
+    G = H // Hk
+    O = [[None] * H for _ in range(Sq)]
+    LSE = [[None] * H for _ in range(Sq)]
+    for s in range(Sq):
+        for h in range(H):
+            kvh = h // G
+            keys = [[bf16_bits_to_float(x) for x in kv_bits[int(t)][kvh]] for t in indices[s][kvh] if int(t) != -1]
+            if not keys:
+                O[s][h] = [0.0] * dv
+                LSE[s][h] = -math.inf
+                continue
+            q = [bf16_bits_to_float(x) for x in q_bits[s][h]]
+            e = [math.exp(scale * math.fsum(q[d] * k[d] for d in range(576))) for k in keys]
+            tot = math.fsum(e)
+            O[s][h] = [math.fsum(e[i] * keys[i][d] for i in range(len(keys))) / tot for d in range(dv)]
+            LSE[s][h] = math.log(tot)
+    return O, LSE

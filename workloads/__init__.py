@@ -12,6 +12,10 @@ from .gen import (  # noqa: F401
     make_sparse_workload,
     draw_indices,
     dense_as_sparse,
+    PrefillWorkload,
+    PREFILL_SPECS,
+    make_prefill_workload,
+    named_prefill,
     named_workload,
     poison_unused,
     permute_pages,

@@ -357,3 +357,72 @@ def dense_as_sparse(w: Workload) -> Workload:
     for b, Lb in enumerate(L):
         idx[b, :, :Lb] = torch.arange(Lb, dtype=torch.int32)
     return replace(w, indices=idx, name=w.name + "+as-sparse")
+
+
+@dataclass
+class PrefillWorkload:
+    """Sparse prefill inputs: q bf16 [s_q, h_q, 576], kv bf16 [s_kv, h_kv, 576] (contiguous rows),
+    indices int32 [s_q, h_kv, topk] (rows of kv; -1: padding)."""
+    name: str
+    q: torch.Tensor
+    kv: torch.Tensor
+    indices: torch.Tensor
+    softmax_scale: float
+    dv: int = D_V
+    seed: int = 0
+    meta: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def s_q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def h_q(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def s_kv(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def h_kv(self) -> int:
+        return int(self.kv.shape[1])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[2])
+
+    def as_numpy(self) -> Dict[str, np.ndarray]:
+        return dict(q_bits=self.q.view(torch.int16).numpy().view(np.uint16),
+                    kv_bits=self.kv.view(torch.int16).numpy().view(np.uint16),
+                    indices=self.indices.numpy())
+
+
+def make_prefill_workload(*, name: str, s_q: int, h_q: int, s_kv: int, topk: int, h_kv: int = 1, seed: int = 0,
+                          duplicates: float = 0.0, padding: float = 0.0,
+                          softmax_scale: Optional[float] = None) -> PrefillWorkload:
+    """Seeded sparse-prefill inputs: values from torch.Generator(seed) (q, then kv: N(0, 1) rounded to
+    bf16); each (s, kvh) lists topk distinct rows of kv drawn uniformly (numpy PCG64(seed)), in random
+    order (all rows and -1 padding when s_kv < topk); duplicates / padding as in draw_indices."""
+    gen = torch.Generator().manual_seed(seed)
+    q = _randn_bf16(gen, (s_q, h_q, D_QK))
+    kv = _randn_bf16(gen, (s_kv, h_kv, D_QK))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = draw_indices([s_kv] * s_q, h_kv, topk, False, rng, duplicates, padding)     # [s_q, h_kv, topk]
+    scale = 1.0 / math.sqrt(D_QK) if softmax_scale is None else float(softmax_scale)
+    return PrefillWorkload(name=name, q=q, kv=kv, indices=idx, softmax_scale=scale, seed=seed)
+
+
+PREFILL_SPECS: Dict[str, Dict[str, object]] = {
+    # every one of 4096 query tokens attends to 2048 of 8192 rows (h_q = 128 heads, one latent KV head)
+    "sparse_prefill": dict(s_q=4096, h_q=128, s_kv=8192, topk=2048, h_kv=1, seed=7,
+                           text="s_q=4096, h_q=128, s_kv=8192, h_kv=1, topk=2048, bf16"),
+}
+
+
+def named_prefill(name: str) -> PrefillWorkload:
+    spec = dict(PREFILL_SPECS[name])
+    text = spec.pop("text")
+    w = make_prefill_workload(name=name, **spec)
+    w.meta["text"] = text
+    return w
