@@ -36,11 +36,34 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 INFINITY_CACHE_BYTES = 256 << 20
 
 
+def is_prefill(w) -> bool:
+    return hasattr(w, "kv") and not hasattr(w, "kvcache")
+
+
+def load_workload(name: str):
+    """A decode workload (WORKLOAD_SPECS) or a sparse-prefill one (PREFILL_SPECS) by name."""
+    from workloads import PREFILL_SPECS, named_prefill, named_workload
+    return named_prefill(name) if name in PREFILL_SPECS else named_workload(name)
+
+
+def prefill_attended(w):
+    """Listed entries of each (query token, KV head) that name a row (not -1)."""
+    return int((w.indices >= 0).sum())
+
+
 def algorithmic_work(w):
     """Bytes the method must move and FLOPs it must do (no partials, no re-reads).
 
     bytes = sum_b h_kv*L_b*bpt + q + o + lse + block-table entries + lengths,
-    flops = 2*(576 + 512) * h_q * sum_b sum_s n_allowed(b, s)."""
+    flops = 2*(576 + 512) * h_q * sum_b sum_s n_allowed(b, s).
+    Sparse prefill: bytes = every kv row once + q + o + lse + indices (a listed row is
+    gathered again for every query token that lists it, from cache, not HBM), flops =
+    2*(576 + 512) * (h_q / h_kv) * listed rows over all (token, KV head)."""
+    if is_prefill(w):
+        n_att = prefill_attended(w)
+        kv = w.s_kv * w.h_kv * 1152
+        byts = kv + w.s_q * w.h_q * (576 * 2 + 512 * 2 + 4) + w.indices.numel() * 4
+        return byts, 2 * (576 + 512) * (w.h_q // w.h_kv) * n_att, kv
     L = [int(x) for x in w.cache_seqlens.tolist()]
     B, S, H, Hk = w.batch, w.s_q, w.h_q, w.h_kv
     bpt = 1152 if w.kv_format == "bf16" else 656
@@ -256,8 +279,7 @@ def _per_dispatch(rows, counter: str, match) -> list:
 def pmc_summary(args) -> str:
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel by what the same
     counters read for the calibration copy of known size."""
-    from workloads import named_workload
-    w = named_workload(args.workload)
+    w = load_workload(args.workload)
     split_name = split_kernel_name(w)
     is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
     is_copy = lambda n: "elementwise" in n and "Mul" in n
@@ -307,8 +329,7 @@ def mfma_summary(args) -> str:
     work the counters saw against the algorithmic FLOPs. rocprofv3 reports GRBM_GUI_ACTIVE summed
     over the 8 XCDs (each has its own); the per-dispatch medians are used (the first dispatch of a
     run is cold)."""
-    from workloads import named_workload
-    w = named_workload(args.workload)
+    w = load_workload(args.workload)
     split_name = split_kernel_name(w)
     is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
     rows = _pmc_rows(args.mfma_summary)
@@ -347,9 +368,9 @@ def mfma_summary(args) -> str:
 
 
 def split_kernel_name(w) -> str:
-    """Name of the split kernel a workload runs (128-row tiles above 64 rows per KV head:
-    the one-barrier kernel for bf16 pages, the two-barrier one for FP8)."""
-    if w.heads_per_kv > 64:
+    """Name of the split kernel a workload runs: the 128-row one-barrier kernel above 64 rows
+    per KV head and for every sparse workload (decode and prefill), else the 64-row kernel."""
+    if is_prefill(w) or getattr(w, "indices", None) is not None or w.heads_per_kv > 64:
         return "splitkv_x1_kernel"
     return "splitkv_kernel"
 
@@ -371,6 +392,142 @@ def percentiles(xs, ps):
     """Nearest-rank percentiles of a list of floats."""
     ys = sorted(xs)
     return [ys[min(len(ys) - 1, max(0, math.ceil(p / 100 * len(ys)) - 1))] for p in ps]
+
+
+def _prefill_oracle_sample(w, target_s: float):
+    """Oracle prefill of one query token at a time (strided through the tokens) until target_s of
+    oracle time is spent; returns (tokens done, seconds, algorithmic FLOPs of them)."""
+    import oracle
+    a = w.as_numpy()
+    done, t_total, n = [], 0.0, 0
+    stride = 997                                # coprime with the token counts used: visits every token
+    while t_total < target_s and n < w.s_q:
+        s = (n * stride) % w.s_q
+        t0 = time.perf_counter()
+        oracle.mla_sparse_prefill(a["q_bits"], a["kv_bits"], a["indices"], w.softmax_scale, dv=w.dv, tokens=[s])
+        t_total += time.perf_counter() - t0
+        done.append(s)
+        n += 1
+    n_att = int((a["indices"][done] >= 0).sum())
+    return done, t_total, 2 * (576 + 512) * (w.h_q // w.h_kv) * n_att
+
+
+def prefill_cpu_baseline(w, target_s: float = 15.0, one_core_s: float = 3.0):
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
+        done, t_total, fl = _prefill_oracle_sample(w, target_s)
+    res = {"value": round(fl / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{len(done)} query tokens of {w.name} (all {w.h_q} heads, {w.topk} listed rows each), "
+                     f"{t_total:.2f} s, numpy float64",
+           "cpu_model": cpu_model()}
+    with threadpool_limits(limits=1):
+        d1, t1, f1 = _prefill_oracle_sample(w, one_core_s)
+    res["one_core"] = {w.name: {"value": round(f1 / t1 / 1e12, 6), "unit": "TFLOP/s",
+                                "sample": f"{len(d1)} query tokens, {t1:.2f} s"}}
+    return res
+
+
+def bench_prefill(args, dev):
+    """One step = the host scheduler's metadata for the sizes (uploaded) + one sparse prefill
+    call (split kernel + combine) over the whole batch of query tokens."""
+    import torch
+    import paged_mla_decode_amd as mla
+    from workloads import PREFILL_SPECS, named_prefill
+    w = named_prefill(args.workload)
+    byts, flops, _ = algorithmic_work(w)
+    print(f"[bench] {w.name}: {PREFILL_SPECS[w.name]['text']}", file=sys.stderr, flush=True)
+    q, kv, idx = w.q.to(dev), w.kv.to(dev), w.indices.to(dev)
+    parts = mla.mla_num_parts(w.s_q, w.h_q // w.h_kv, w.h_kv, "bf16")
+    flat_dev = torch.empty((parts * 8 + w.s_q + 1,), dtype=torch.int32, device=dev)
+    meta_dev, splits_dev = mla.split_metadata(flat_dev, w.s_q)
+
+    def host_metadata():
+        return mla.mla_get_metadata_sparse(w.s_q, 1, w.topk, w.h_q, w.h_kv, num_parts=parts, host=True)
+
+    _, s_host = host_metadata()
+    pre = mla.MlaSparsePrefill(q, kv, idx, w.softmax_scale, w.dv, tile_metadata=meta_dev, num_splits=splits_dev,
+                               max_splits=mla.max_splits_of(s_host))
+    stream = torch.cuda.current_stream(dev)
+    hip = HipEvents()
+    stage = [torch.empty((parts * 8 + w.s_q + 1,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    stage_done = [None, None]
+
+    def step(i, ev=None):
+        k = i & 1
+        if stage_done[k] is not None:
+            hip.synchronize(stage_done[k])
+        m_h, _ = host_metadata()
+        stage[k].copy_(mla.packed_metadata(m_h))
+        flat_dev.copy_(stage[k], non_blocking=True)
+        if stage_done[k] is None:
+            stage_done[k] = hip.create(timing=False)
+        hip.record(stage_done[k], stream)
+        pre.set_events(ev if ev is not None else (None, None, None))
+        pre.run(stream)
+
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(hip.create(), hip.create(), hip.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    split_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    comb_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+    for x in stage_done:
+        if x is not None:
+            hip.destroy(x)
+    split_avg = sum(split_ms) / len(split_ms)
+    comb_avg = sum(comb_ms) / len(comb_ms)
+    tflops = flops / (ms * 1e-3) / 1e12
+    roof = roofline(byts, flops, split_avg)
+    roof["traffic"] = stored_traffic(split_kernel_name(w), w.name)
+    roof_call = roofline(byts, flops, split_avg + comb_avg)
+    roof_call.pop("traffic")
+    result = {
+        "metric": "sparse MLA prefill achieved TFLOPS (+% of roofline), 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "s_q": w.s_q, "s_kv": w.s_kv, "h_q": w.h_q, "h_kv": w.h_kv, "topk": w.topk,
+                   "d_qk": 576, "d_v": 512, "num_parts": parts},
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "split_kernel_ms": round(split_avg, 5),
+        "split_kernel_ms_p10_p50_p90": [round(x, 5) for x in percentiles(split_ms, (10, 50, 90))],
+        "combine_kernel_ms": round(comb_avg, 5),
+        "algorithmic_bytes": byts,
+        "algorithmic_flops": flops,
+        "roofline": roof,
+        "roofline_split_combine": roof_call,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -409,10 +566,15 @@ def main():
 
     import torch
     import paged_mla_decode_amd as mla
-    from workloads import WORKLOAD_SPECS, named_workload
+    from workloads import PREFILL_SPECS, WORKLOAD_SPECS, named_workload
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in PREFILL_SPECS:
+        if args.metadata == "device":
+            raise SystemExit("--metadata device: the sparse metadata depends only on the sizes (host)")
+        bench_prefill(args, dev)
+        return
     w = named_workload(args.workload)
     byts, flops, kv_bytes = algorithmic_work(w)
     pool_bytes = w.kvcache.numel() * w.kvcache.element_size()

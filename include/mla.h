@@ -285,6 +285,63 @@ mla_status mla_decode_kvcache(const mla_decode_args* args, void* hip_stream);
  */
 mla_status mla_decode_kvcache_noalloc(const mla_decode_args* args, void* hip_stream);
 
+/*
+ * Sparse prefill (flash_mla_sparse_fwd(q, kv, indices, sm_scale, d_v=512) on
+ * the wmrh.cn FlashMLA深度解析 page, "稀疏预填充使用"): query token s, head h
+ * attends to the rows indices[s, h / (h_q / h_kv), 0..topk) of kv's KV head
+ * h / (h_q / h_kv); o = softmax(softmax_scale * q K^T) V with V the first dv
+ * dims of the listed rows, lse = ln sum exp(softmax_scale * q K^T). -1 is
+ * padding; a row listed twice counts twice; an entry outside [-1, s_kv)
+ * gives NaN o and lse for that (token, KV head); a token with no listed row
+ * gives o = 0, lse = -inf. No causal mask (the list decides).
+ * Every query token is scheduled as a sequence of topk entries: tile_metadata
+ * and num_splits are device copies of mla_get_metadata_sparse(s_q, 1, topk,
+ * h_q, h_kv, MLA_KV_BF16, ...) (one result serves every call with the same
+ * s_q, topk, h_q and h_kv), the workspace holds at least
+ * mla_workspace_bytes_sparse(s_q, 1, num_parts, h_q, h_kv) bytes.
+ */
+typedef struct mla_sparse_prefill_args {
+  /* q: bf16 [s_q, h_q, 576]; strides in elements for (token, head); the 576
+     dims contiguous; base and strides 16-byte aligned. */
+  const void* q;
+  int64_t q_stride[2];
+  /* kv: bf16 [s_kv, h_kv, 576] (latent dims 0..511 are also V); strides in
+     elements for (row, head); rows contiguous; base and strides 16-byte
+     aligned; the rows of one head span less than 2^31 bytes. */
+  const void* kv;
+  int64_t kv_stride[2];
+  /* indices: int32 [s_q, h_kv, topk], device; strides in elements for
+     (token, KV head); the last dim contiguous. */
+  const int32_t* indices;
+  int64_t idx_stride[2];
+  int s_q, s_kv, h_q, h_kv, topk;
+  int d_qk;                   /* must be 576 */
+  int dv;                     /* must be 512 */
+  float softmax_scale;
+
+  const int32_t* tile_metadata;   /* [num_parts][MLA_META_INTS], device */
+  int num_parts;
+  const int32_t* num_splits;      /* [s_q + 1], device */
+
+  void* o;                    /* out: bf16 [s_q, h_q, dv], contiguous */
+  float* lse;                 /* out: fp32 [s_q, h_q], contiguous; natural log */
+  void* workspace;            /* 256-byte aligned */
+  size_t workspace_bytes;
+  int max_splits;             /* as in mla_decode_args */
+  void* events[3];            /* as in mla_decode_args */
+} mla_sparse_prefill_args;
+
+/* sizeof(mla_sparse_prefill_args), for bindings that check their layout. */
+size_t mla_sparse_prefill_args_size(void);
+
+/*
+ * Launches the sparse prefill (the split kernel over the listed rows, then the
+ * combine kernel) on `hip_stream`. Asynchronous. Argument errors return a
+ * status before anything is launched; errors in the index values are reported
+ * in the outputs as above, never by a fault.
+ */
+mla_status mla_sparse_prefill_fwd(const mla_sparse_prefill_args* args, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

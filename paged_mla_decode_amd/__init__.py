@@ -20,10 +20,11 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import D_QK, D_V, FP8_RECORD_BYTES, META_INTS, PAGE_TOKENS, MlaDecodeArgs, MlaError
+from ._lib import D_QK, D_V, FP8_RECORD_BYTES, META_INTS, PAGE_TOKENS, MlaDecodeArgs, MlaError, MlaSparsePrefillArgs
 
 __all__ = [
-    "mla_get_metadata", "mla_get_metadata_device", "mla_get_metadata_sparse", "mla_decode_kvcache", "mla_workspace_bytes", "mla_num_parts", "MlaDecoder",
+    "mla_get_metadata", "mla_get_metadata_device", "mla_get_metadata_sparse", "mla_decode_kvcache",
+    "mla_workspace_bytes", "mla_num_parts", "MlaDecoder", "MlaSparsePrefill", "flash_mla_sparse_fwd",
     "MlaError", "kv_format_of", "library_path",
 ]
 
@@ -354,3 +355,100 @@ def mla_decode_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torc
     dec = MlaDecoder(q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal, softmax_scale,
                      out=out, lse=lse, workspace=workspace, indices=indices)
     return dec.run()
+
+
+class MlaSparsePrefill:
+    """A sparse prefill call (mla_sparse_prefill_fwd) with its argument block marshalled once.
+
+    q bf16 [s_q, h_q, 576]; kv bf16 [s_kv, h_kv, 576]; indices int32 [s_q, h_kv, topk] (rows
+    of kv, -1: padding). tile_metadata / num_splits default to mla_get_metadata_sparse(s_q, 1,
+    topk, h_q, h_kv) on q's device. `run()` launches on the current (or given) stream and
+    returns (o [s_q, h_q, dv] bf16, lse [s_q, h_q] fp32, natural log)."""
+
+    def __init__(self, q, kv, indices, sm_scale=None, d_v=D_V, *, tile_metadata=None, num_splits=None, out=None,
+                 lse=None, workspace=None, events=None, max_splits=None, num_parts: int = 0):
+        dev = q.device
+        if dev.type != "cuda":
+            raise ValueError("q must be a CUDA (HIP) tensor")
+        _check_tensor("q", q, torch.bfloat16, 3, dev)
+        _check_tensor("kv", kv, torch.bfloat16, 3, dev)
+        _check_tensor("indices", indices, torch.int32, 3, dev)
+        if q.stride(-1) != 1 or kv.stride(-1) != 1 or indices.stride(-1) != 1:
+            raise ValueError("q, kv and indices need a contiguous last dimension")
+        Sq, H, D = q.shape
+        Skv, Hk = int(kv.shape[0]), int(kv.shape[1])
+        if tuple(indices.shape[:2]) != (Sq, Hk) or indices.shape[2] < 1:
+            raise ValueError("indices must be int32 [s_q, h_kv, topk]")
+        topk = int(indices.shape[2])
+        if tile_metadata is None or num_splits is None:
+            tile_metadata, num_splits = mla_get_metadata_sparse(Sq, 1, topk, H, Hk, num_parts=num_parts, device=dev)
+        _check_tensor("tile_metadata", tile_metadata, torch.int32, 2, dev)
+        _check_tensor("num_splits", num_splits, torch.int32, 1, dev)
+        if not (tile_metadata.is_contiguous() and num_splits.is_contiguous()) or tile_metadata.shape[1] != META_INTS:
+            raise ValueError(f"tile_metadata must be contiguous [num_parts, {META_INTS}] and num_splits contiguous")
+        if num_splits.shape[0] != Sq + 1:
+            raise ValueError("num_splits must be [s_q + 1]")
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(D)
+        parts = int(tile_metadata.shape[0])
+        if out is None:
+            out = torch.empty((Sq, H, int(d_v)), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((Sq, H), dtype=torch.float32, device=dev)
+        _check_tensor("out", out, torch.bfloat16, 3, dev)
+        _check_tensor("lse", lse, torch.float32, 2, dev)
+        if not (out.is_contiguous() and lse.is_contiguous()):
+            raise ValueError("out and lse must be contiguous")
+        if tuple(out.shape) != (Sq, H, int(d_v)) or tuple(lse.shape) != (Sq, H):
+            raise ValueError("out must be [s_q, h_q, d_v] and lse [s_q, h_q]")
+        lib = _lib.load()
+        need = int(lib.mla_workspace_bytes_sparse(Sq, 1, parts, H, Hk)) if H % max(Hk, 1) == 0 else 0
+        if workspace is None:
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+        self.tensors = (q, kv, indices, tile_metadata, num_splits, out, lse, workspace)
+        self.out, self.lse, self.workspace = out, lse, workspace
+        a = MlaSparsePrefillArgs()
+        a.q = q.data_ptr()
+        a.q_stride[:] = [q.stride(0), q.stride(1)]
+        a.kv = kv.data_ptr()
+        a.kv_stride[:] = [kv.stride(0), kv.stride(1)]
+        a.indices = indices.data_ptr()
+        a.idx_stride[:] = [indices.stride(0), indices.stride(1)]
+        a.s_q, a.s_kv, a.h_q, a.h_kv, a.topk = int(Sq), Skv, int(H), Hk, topk
+        a.d_qk, a.dv = int(D), int(d_v)
+        a.softmax_scale = float(sm_scale)
+        a.tile_metadata = tile_metadata.data_ptr()
+        a.num_parts = parts
+        a.num_splits = num_splits.data_ptr()
+        a.o = out.data_ptr()
+        a.lse = lse.data_ptr()
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+        if max_splits is None:
+            max_splits = getattr(num_splits, "_mla_max_splits", 0)
+        a.max_splits = int(max_splits)
+        self.args = a
+        if events is not None:
+            self.set_events(events)
+        self._args_ref = ctypes.byref(a)
+        self._lib = lib
+        self.device = dev
+
+    def set_events(self, events: Sequence) -> None:
+        """Timing hooks: three raw hipEvent_t handles (ints) or None."""
+        for i in range(3):
+            e = events[i] if i < len(events) else None
+            self.args.events[i] = None if e is None else int(e)
+
+    def run(self, stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        _lib.check(self._lib.mla_sparse_prefill_fwd(self._args_ref, ctypes.c_void_p(s.cuda_stream)))
+        return self.out, self.lse
+
+
+def flash_mla_sparse_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: Optional[float] = None,
+                         d_v: int = D_V, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse prefill: (o [s_q, h_q, d_v] bf16, lse [s_q, h_q] fp32). Query token s, head h
+    attends to the rows indices[s, h // (h_q // h_kv), :] of kv's KV head h // (h_q // h_kv)
+    (-1: padding). Keyword arguments go to MlaSparsePrefill (metadata, out, lse, workspace)."""
+    return MlaSparsePrefill(q, kv, indices, sm_scale, d_v, **kw).run()

@@ -26,6 +26,7 @@ EXPORTED_SYMBOLS = (
     "mla_last_error", "mla_version", "mla_decode_args_size", "mla_device_cu_count", "mla_num_parts",
     "mla_get_metadata", "mla_get_metadata_device", "mla_get_metadata_sparse", "mla_workspace_bytes",
     "mla_workspace_bytes_sparse", "mla_decode_kvcache", "mla_decode_kvcache_noalloc",
+    "mla_sparse_prefill_args_size", "mla_sparse_prefill_fwd",
 )
 SCRATCH_BYTES = 128 << 20      # MLA_SCRATCH_BYTES
 
@@ -62,6 +63,34 @@ class MlaDecodeArgs(ctypes.Structure):
         ("indices", ctypes.c_void_p),
         ("idx_stride", ctypes.c_int64 * 2),
         ("topk", ctypes.c_int),
+    ]
+
+
+class MlaSparsePrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 2),
+        ("kv", ctypes.c_void_p),
+        ("kv_stride", ctypes.c_int64 * 2),
+        ("indices", ctypes.c_void_p),
+        ("idx_stride", ctypes.c_int64 * 2),
+        ("s_q", ctypes.c_int),
+        ("s_kv", ctypes.c_int),
+        ("h_q", ctypes.c_int),
+        ("h_kv", ctypes.c_int),
+        ("topk", ctypes.c_int),
+        ("d_qk", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("softmax_scale", ctypes.c_float),
+        ("tile_metadata", ctypes.c_void_p),
+        ("num_parts", ctypes.c_int),
+        ("num_splits", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("max_splits", ctypes.c_int),
+        ("events", ctypes.c_void_p * 3),
     ]
 
 
@@ -105,6 +134,13 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_kvcache.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     lib.mla_decode_kvcache_noalloc.restype = ctypes.c_int
     lib.mla_decode_kvcache_noalloc.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
+    lib.mla_sparse_prefill_args_size.restype = ctypes.c_size_t
+    lib.mla_sparse_prefill_args_size.argtypes = []
+    lib.mla_sparse_prefill_fwd.restype = ctypes.c_int
+    lib.mla_sparse_prefill_fwd.argtypes = [ctypes.POINTER(MlaSparsePrefillArgs), ctypes.c_void_p]
+    if lib.mla_sparse_prefill_args_size() != ctypes.sizeof(MlaSparsePrefillArgs):
+        raise ImportError(f"mla_sparse_prefill_args layout mismatch: library {lib.mla_sparse_prefill_args_size()} "
+                          f"bytes, binding {ctypes.sizeof(MlaSparsePrefillArgs)} bytes")
     if lib.mla_decode_args_size() != ctypes.sizeof(MlaDecodeArgs):
         raise ImportError(f"mla_decode_args layout mismatch: library {lib.mla_decode_args_size()} bytes, "
                           f"binding {ctypes.sizeof(MlaDecodeArgs)} bytes")

@@ -188,6 +188,11 @@ __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
   return p.topk > 0 ? p.topk : ld_meta(p.seqlens + b);
 }
 
+// Real cache length of sequence b_real (sparse paths): kv_rows for sparse prefill.
+__device__ __forceinline__ int real_len(const DecodeParams& p, int b_real) {
+  return p.kv_rows > 0 ? p.kv_rows : ld_meta(p.seqlens + b_real);
+}
+
 // Index of (sequence b, head, query token s_idx) in lse [batch, h_q, s_q]; for
 // sparse decode b is the virtual sequence b_real * sq_real + s.
 __device__ __forceinline__ int64_t lse_index(const DecodeParams& p, int b, int head, int s_idx) {
@@ -224,7 +229,7 @@ __device__ __forceinline__ void seq_pages(const DecodeParams& p, const Range& r,
   const int max_len = p.max_blocks * kPage;
   int len;
   if (p.topk > 0) {                       // sparse: topk entries; the real length is checked
-    const int real = ld_meta(p.seqlens + b / p.sq_real);
+    const int real = real_len(p, b / p.sq_real);
     len_ok = real >= 0 && real <= max_len;
     len = p.topk;
   } else {

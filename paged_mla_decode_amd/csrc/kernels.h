@@ -44,10 +44,15 @@ struct DecodeParams {
   // the real lengths [batch_real].
   const int32_t* indices;
   int64_t idx_sb, idx_ss;     // element strides of indices: sequence, query token
+  int64_t idx_sh;             // ... and KV head (0: one list serves every KV head)
   int topk;                   // 0: dense decode
   int sq_real;
   int real_causal;            // sparse: the causal flag (applied to the listed positions)
   int64_t pool_bytes;         // sparse: bytes from a KV head's base to the end of the pool (< 2^31)
+  // Sparse prefill (kv_rows > 0): the keys are kv_rows contiguous rows, row t at byte t * kv_st
+  // (64-row pages, page i = rows 64 i .. 64 i + 63, kv_sp = 64 kv_st); no block table, no
+  // seqlens: every query token's length is kv_rows.
+  int kv_rows;
 };
 
 // The row-tile split kernel (mla_kernels_x.hip): 128-row tiles, 8 waves of

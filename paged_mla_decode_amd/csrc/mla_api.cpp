@@ -82,6 +82,36 @@ size_t workspace_bytes(int batch, int num_parts, int rows, int h_kv, bool wide) 
 }
 
 
+mla_status check_workspace(const char* fn, const void* workspace, size_t bytes, size_t need) {
+  if (!workspace || bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  return MLA_OK;
+}
+
+// The common tail of the entry points: the grid bound, the partials' places in the
+// workspace, and the launch of the split and combine kernels. p holds everything else.
+mla_status finish_and_launch(const char* fn, mla::DecodeParams& p, const mla::Plan& plan, int kv_format,
+                             void* workspace, int num_parts, int max_splits, void* const events[3],
+                             void* hip_stream) {
+  const long wgs = static_cast<long>(num_parts) * plan.m_tiles * p.h_kv;
+  if (wgs > (1L << 30)) return fail(MLA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  const int slots = p.batch + num_parts;
+  char* const ws = static_cast<char*>(workspace);
+  p.part_o32 = plan.wide ? nullptr : reinterpret_cast<float*>(ws);
+  p.part_o16 = plan.wide ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+  p.part_scale = plan.wide ? reinterpret_cast<float*>(ws + partial_o_bytes(slots, p.rows, p.h_kv, true)) : nullptr;
+  p.part_lse = reinterpret_cast<float*>(ws + partial_o_bytes(slots, p.rows, p.h_kv, plan.wide) +
+                                        partial_scale_bytes(slots, p.rows, p.h_kv, plan.wide));
+  p.max_slots = slots;
+  p.max_splits = max_splits > 0 ? max_splits : 0;
+  p.grid_wgs = static_cast<int>(wgs);
+  const hipError_t err = mla::launch_decode(p, plan, kv_format, static_cast<hipStream_t>(hip_stream), events);
+  if (err != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", fn, hipGetErrorString(err));
+  return MLA_OK;
+}
+
 // Validation, argument packing and launch for both decode entry points.
 // use_scratch: the workspace is the library's static scratch (the caller's
 // workspace fields are ignored); nothing is allocated either way.
@@ -167,18 +197,16 @@ mla_status decode_impl(const mla_decode_args* a, void* hip_stream, bool use_scra
   }
   const size_t need = workspace_bytes(vbatch, a->num_parts, rows, a->h_kv, plan.wide);
   void* workspace = a->workspace;
+  if (!use_scratch) {
+    const mla_status st = check_workspace("mla_decode_kvcache", workspace, a->workspace_bytes, need);
+    if (st != MLA_OK) return st;
+  }
   if (use_scratch) {
     if (need > mla::kScratchBytes)
       return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
                   "mla_decode_kvcache_noalloc: this call needs %zu bytes of workspace; the static scratch holds %zu "
                   "(fewer num_parts or a smaller batch, or mla_decode_kvcache with a caller workspace)",
                   need, mla::kScratchBytes);
-  } else {
-    if (!workspace || a->workspace_bytes < need)
-      return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "mla_decode_kvcache: workspace of %zu bytes, need %zu",
-                  a->workspace_bytes, need);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-      return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: workspace must be 256-byte aligned");
   }
   const long wgs = static_cast<long>(a->num_parts) * plan.m_tiles * a->h_kv;
   if (wgs > (1L << 30)) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: grid too large");
@@ -226,20 +254,111 @@ mla_status decode_impl(const mla_decode_args* a, void* hip_stream, bool use_scra
   p.scale_log2 = static_cast<float>(static_cast<double>(a->softmax_scale) * 1.4426950408889634074);
   p.o = static_cast<uint16_t*>(a->o);
   p.lse = a->lse;
-  const int slots = vbatch + a->num_parts;
-  char* const ws = static_cast<char*>(workspace);
-  p.part_o32 = plan.wide ? nullptr : reinterpret_cast<float*>(ws);
-  p.part_o16 = plan.wide ? reinterpret_cast<uint16_t*>(ws) : nullptr;
-  p.part_scale = plan.wide ? reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv, true)) : nullptr;
-  p.part_lse = reinterpret_cast<float*>(ws + partial_o_bytes(slots, rows, a->h_kv, plan.wide) +
-                                        partial_scale_bytes(slots, rows, a->h_kv, plan.wide));
-  p.max_slots = slots;
-  p.max_splits = a->max_splits > 0 ? a->max_splits : 0;
-  p.grid_wgs = static_cast<int>(wgs);
+  return finish_and_launch("mla_decode_kvcache", p, plan, a->kv_format, workspace, a->num_parts, a->max_splits,
+                           a->events, hip_stream);
+}
 
-  hipError_t err = mla::launch_decode(p, plan, a->kv_format, static_cast<hipStream_t>(hip_stream), a->events);
-  if (err != hipSuccess) return fail(MLA_ERR_HIP, "mla_decode_kvcache: %s", hipGetErrorString(err));
-  return MLA_OK;
+// Sparse prefill: every query token s is virtual sequence s (batch s_q, one query
+// token each) of topk entries over the contiguous kv rows; the sparse decode kernels run it.
+mla_status prefill_impl(const mla_sparse_prefill_args* a, void* hip_stream) {
+  const char* const fn = "mla_sparse_prefill_fwd";
+  if (!a) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: args is null", fn);
+  if (!a->q || !a->kv || !a->indices || !a->tile_metadata || !a->num_splits || !a->o || !a->lse)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: null pointer among q, kv, indices, tile_metadata, num_splits, o, lse", fn);
+  if (a->s_q < 1 || a->s_kv < 1 || a->h_q < 1 || a->h_kv < 1 || a->topk < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: s_q, s_kv, h_q, h_kv, topk must be >= 1", fn);
+  if (a->h_q % a->h_kv)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: h_q (%d) is not a multiple of h_kv (%d)", fn, a->h_q, a->h_kv);
+  if (a->d_qk != mla::kDqk) return fail(MLA_ERR_UNSUPPORTED, "%s: d_qk must be 576 (got %d)", fn, a->d_qk);
+  if (a->dv != mla::kDv) return fail(MLA_ERR_UNSUPPORTED, "%s: dv must be 512 (got %d)", fn, a->dv);
+  if (!(std::isfinite(a->softmax_scale))) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite", fn);
+  if (a->num_parts < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: num_parts must be >= 1", fn);
+  if (a->s_q > (1 << 24)) return fail(MLA_ERR_UNSUPPORTED, "%s: s_q above 2^24", fn);
+  if (static_cast<int64_t>(a->s_q) * a->h_q > (int64_t{1} << 31) / mla::kDv)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: output too large", fn);
+
+  // q: bf16 [s_q, h_q, 576], 576 contiguous dims, 16-byte aligned rows.
+  for (int k = 0; k < 2; ++k)
+    if (a->q_stride[k] < 0 || (a->q_stride[k] % 8) != 0)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "%s: q_stride[%d] = %lld must be a non-negative multiple of 8", fn, k,
+                  static_cast<long long>(a->q_stride[k]));
+  if (!aligned16(a->q)) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: q must be 16-byte aligned", fn);
+  if (a->q_stride[1] < mla::kDqk && a->h_q > 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: q head stride overlaps the 576 dims", fn);
+  if (((a->h_q - 1) * a->q_stride[1] + mla::kDqk) * 2 >= (int64_t{1} << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: the q rows of one token must span less than 2 GiB", fn);
+
+  // kv: bf16 [s_kv, h_kv, 576], rows contiguous and 16-byte aligned.
+  int64_t kvb[2];
+  for (int k = 0; k < 2; ++k) {
+    kvb[k] = a->kv_stride[k] * 2;
+    if (a->kv_stride[k] < 0 || (kvb[k] % 16) != 0)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "%s: kv_stride[%d] must be non-negative and a multiple of 16 bytes", fn, k);
+  }
+  const int64_t row_bytes = mla::kDqk * 2;
+  if (kvb[0] < row_bytes || (a->h_kv > 1 && kvb[1] < row_bytes))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a kv stride is smaller than one row (1152 bytes)", fn);
+  if (!aligned16(a->kv)) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: kv must be 16-byte aligned", fn);
+  const int64_t pool_bytes = static_cast<int64_t>(a->s_kv - 1) * kvb[0] + row_bytes;
+  if (kvb[0] * mla::kPage >= (int64_t{1} << 31) || pool_bytes > (int64_t{1} << 31) - (int64_t{1} << 16))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: the kv rows of a head must span less than 2^31 bytes (%lld)", fn,
+                static_cast<long long>(pool_bytes));
+
+  // indices: int32 [s_q, h_kv, topk], last dim contiguous.
+  if (a->idx_stride[0] < 0 || a->idx_stride[1] < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: idx_stride must be non-negative", fn);
+  if (static_cast<int64_t>(a->s_q - 1) * a->idx_stride[0] + static_cast<int64_t>(a->h_kv - 1) * a->idx_stride[1] +
+          a->topk >= (int64_t{1} << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: indices must span less than 2^31 entries", fn);
+  if ((reinterpret_cast<uintptr_t>(a->o) & 7u) || (reinterpret_cast<uintptr_t>(a->lse) & 3u))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: o must be 8-byte and lse 4-byte aligned", fn);
+
+  const int group = a->h_q / a->h_kv;
+  const mla::Plan plan = mla::make_plan_sparse(group);
+  const size_t need = workspace_bytes(a->s_q, a->num_parts, group, a->h_kv, true);
+  {
+    const mla_status st = check_workspace(fn, a->workspace, a->workspace_bytes, need);
+    if (st != MLA_OK) return st;
+  }
+
+  mla::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_sb = a->q_stride[0];                 // virtual sequence s is query token s
+  p.q_ss = a->q_stride[0];
+  p.q_sh = a->q_stride[1];
+  p.kv = static_cast<const uint8_t*>(a->kv);
+  p.kv_st = kvb[0];
+  p.kv_sp = kvb[0] * mla::kPage;
+  p.kv_sh = kvb[1];
+  p.num_pages = (a->s_kv + mla::kPage - 1) / mla::kPage;
+  p.block_table = nullptr;
+  p.bt_stride = 0;
+  p.max_blocks = p.num_pages;
+  p.seqlens = nullptr;
+  p.kv_rows = a->s_kv;
+  p.meta = a->tile_metadata;
+  p.num_parts = a->num_parts;
+  p.num_splits = a->num_splits;
+  p.batch = a->s_q;
+  p.s_q = 1;
+  p.h_q = a->h_q;
+  p.h_kv = a->h_kv;
+  p.group = group;
+  p.rows = group;
+  p.causal = 0;
+  p.indices = a->indices;
+  p.idx_sb = a->idx_stride[0];
+  p.idx_ss = 0;
+  p.idx_sh = a->idx_stride[1];
+  p.topk = a->topk;
+  p.sq_real = 1;
+  p.real_causal = 0;
+  p.pool_bytes = pool_bytes;
+  p.scale_log2 = static_cast<float>(static_cast<double>(a->softmax_scale) * 1.4426950408889634074);
+  p.o = static_cast<uint16_t*>(a->o);
+  p.lse = a->lse;
+  return finish_and_launch(fn, p, plan, MLA_KV_BF16, a->workspace, a->num_parts, a->max_splits, a->events,
+                           hip_stream);
 }
 
 }  // namespace
@@ -376,5 +495,11 @@ mla_status mla_decode_kvcache(const mla_decode_args* a, void* hip_stream) {
 mla_status mla_decode_kvcache_noalloc(const mla_decode_args* a, void* hip_stream) {
   return decode_impl(a, hip_stream, true);
 }
+
+mla_status mla_sparse_prefill_fwd(const mla_sparse_prefill_args* a, void* hip_stream) {
+  return prefill_impl(a, hip_stream);
+}
+
+size_t mla_sparse_prefill_args_size(void) { return sizeof(mla_sparse_prefill_args); }
 
 }  // extern "C"

@@ -636,11 +636,12 @@ struct SparseTok {
 };
 
 // Step A: lane j < 32 loads entry j of unit u (none past topk or past the range).
-__device__ __forceinline__ int sparse_load_index(const DecodeParams& p, const Range& r, const XUnit& u, int lane) {
+__device__ __forceinline__ int sparse_load_index(const DecodeParams& p, const Range& r, const XUnit& u, int kvh,
+                                                 int lane) {
   const int j = u.pi * kPage + u.hf * kXHalf + lane;
   if (u.b > r.end_b || lane >= kXHalf || j >= p.topk) return -1;
   const int br = u.b / p.sq_real, s = u.b - br * p.sq_real;
-  return p.indices[br * p.idx_sb + s * p.idx_ss + j];
+  return p.indices[br * p.idx_sb + s * p.idx_ss + kvh * p.idx_sh + j];
 }
 
 // Step B: validate the (landed) index, drop it unless attended, load its block-table entry.
@@ -649,14 +650,17 @@ __device__ __forceinline__ SparseTok sparse_load_page(const DecodeParams& p, con
   SparseTok k;
   if (u.b > r.end_b) return k;
   const int br = u.b / p.sq_real, s = u.b - br * p.sq_real;
-  const int L = ld_meta(p.seqlens + br);
+  const int L = real_len(p, br);
   const int max_len = p.max_blocks * kPage;
   const bool in_list = lane < kXHalf;
   const bool valid = idx == -1 || (idx >= 0 && idx < L && idx < max_len);
   const bool attend = in_list && idx >= 0 && valid && (!p.real_causal || idx <= L - p.sq_real + s);
   k.bad = __builtin_amdgcn_ballot_w64(in_list && !valid) != 0;
   k.t = attend ? idx : -1;
-  k.page = attend ? p.block_table[static_cast<int64_t>(br) * p.bt_stride + (idx >> 6)] : -1;
+  if (p.kv_rows > 0)                       // contiguous rows: page idx / 64 of the row array
+    k.page = attend ? (idx >> 6) : -1;
+  else
+    k.page = attend ? p.block_table[static_cast<int64_t>(br) * p.bt_stride + (idx >> 6)] : -1;
   return k;
 }
 
@@ -800,10 +804,10 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
     uq[1] = next_unit(uq[0]);
     uq2 = next_unit(uq[1]);
     uq3 = next_unit(uq2);
-    const int i0 = sparse_load_index(p, r, uq[0], ln.lane), i1 = sparse_load_index(p, r, uq[1], ln.lane);
+    const int i0 = sparse_load_index(p, r, uq[0], kvh, ln.lane), i1 = sparse_load_index(p, r, uq[1], kvh, ln.lane);
     wait_vm_all();
     SparseTok k0 = sparse_load_page(p, r, uq[0], i0, ln.lane), k1 = sparse_load_page(p, r, uq[1], i1, ln.lane);
-    const int i2 = sparse_load_index(p, r, uq2, ln.lane);
+    const int i2 = sparse_load_index(p, r, uq2, kvh, ln.lane);
     wait_vm_all();
     const uint32_t o0 = sparse_offset(p, k0, maskq[0]), o1 = sparse_offset(p, k1, maskq[1]);
     okq[0] = !k0.bad;
@@ -811,7 +815,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
     if (uq[0].b <= r.end_b) sparse_issue<FMT>(kv_head, p.pool_bytes, o0, lds + X::kRing, wave, ln.lane);
     if (uq[1].b <= r.end_b) sparse_issue<FMT>(kv_head, p.pool_bytes, o1, lds + X::kRing + X::kSlot, wave, ln.lane);
     tk2 = sparse_load_page(p, r, uq2, i2, ln.lane);      // lands by the first wait of the unit loop
-    idx3 = sparse_load_index(p, r, uq3, ln.lane);
+    idx3 = sparse_load_index(p, r, uq3, kvh, ln.lane);
   } else {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -925,7 +929,7 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
         tk2 = sparse_load_page(p, r, uq3, idx3, ln.lane);   // step B of unit 3 ahead (its index landed)
         uq2 = uq3;
         uq3 = next_unit(uq3);
-        idx3 = sparse_load_index(p, r, uq3, ln.lane);        // step A of the new unit 3 ahead
+        idx3 = sparse_load_index(p, r, uq3, kvh, ln.lane);        // step A of the new unit 3 ahead
       } else {
       un = (uq[1].b <= r.end_b) ? x_next(p, r, uq[1]) : uq[1];
       if (un.b <= r.end_b) {

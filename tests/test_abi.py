@@ -230,3 +230,65 @@ def test_device_scheduler_checks_before_launch():
     assert lib.mla_get_metadata_device(*args(8, 1025)) == _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_get_metadata_device(fake, 4, 16, 1, 9, 256, 4, fake, fake, None, None) == \
         _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_args_struct_layout_matches():
+    assert _lib.load().mla_sparse_prefill_args_size() == ctypes.sizeof(_lib.MlaSparsePrefillArgs)
+
+
+def _valid_prefill_args():
+    a = _lib.MlaSparsePrefillArgs()
+    fake = 1 << 20          # never dereferenced: every case below fails validation first
+    a.q = fake
+    a.q_stride[:] = [128 * 576, 576]
+    a.kv = fake
+    a.kv_stride[:] = [576, 576]
+    a.indices = fake
+    a.idx_stride[:] = [64, 64]
+    a.s_q, a.s_kv, a.h_q, a.h_kv, a.topk = 4, 300, 128, 1, 64
+    a.d_qk, a.dv = 576, 512
+    a.softmax_scale = 1 / 24
+    a.tile_metadata = fake
+    a.num_parts = 4
+    a.num_splits = fake
+    a.o = fake
+    a.lse = fake
+    a.workspace = fake
+    a.workspace_bytes = _lib.load().mla_workspace_bytes_sparse(4, 1, 4, 128, 1)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_qk", 512, _lib.MLA_ERR_UNSUPPORTED),
+    ("dv", 576, _lib.MLA_ERR_UNSUPPORTED),
+    ("h_kv", 3, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("s_q", 0, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("s_kv", 0, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("topk", 0, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("s_kv", 1 << 21, _lib.MLA_ERR_UNSUPPORTED),               # rows past 2^31 bytes
+    ("num_parts", 0, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("workspace_bytes", 16, _lib.MLA_ERR_WORKSPACE_TOO_SMALL),
+    ("workspace", None, _lib.MLA_ERR_WORKSPACE_TOO_SMALL),
+    ("workspace", (1 << 20) + 16, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("indices", None, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("q", (1 << 20) + 2, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("kv", (1 << 20) + 8, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("lse", None, _lib.MLA_ERR_INVALID_ARGUMENT),
+    ("softmax_scale", float("inf"), _lib.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_prefill_rejects_bad_arguments(field, value, status):
+    lib = _lib.load()
+    a = _valid_prefill_args()
+    setattr(a, field, value)
+    assert lib.mla_sparse_prefill_fwd(ctypes.byref(a), None) == status
+    assert b"mla_sparse_prefill_fwd" in lib.mla_last_error()
+
+
+@pytest.mark.parametrize("which,k,value", [("q_stride", 1, 100), ("kv_stride", 0, 4), ("kv_stride", 0, 512),
+                                           ("idx_stride", 1, -1)])
+def test_prefill_rejects_bad_strides(which, k, value):
+    lib = _lib.load()
+    a = _valid_prefill_args()
+    getattr(a, which)[k] = value
+    assert lib.mla_sparse_prefill_fwd(ctypes.byref(a), None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_sparse_prefill_fwd(None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
