@@ -136,6 +136,21 @@ def gather_sequence(kvcache: np.ndarray, kv_format: str, block_table_row: np.nda
     return decode_kv_rows(rows, kv_format)
 
 
+def gather_values(vcache: np.ndarray, block_table_row: np.ndarray, L: int) -> np.ndarray:
+    """Values of one sequence from a separate V cache, in token order: float64 [L, h_kv, dv].
+
+    The optional vcache_ argument of mha_fwd_kvcache_mla (num_blocks x page_block_size x
+    num_heads_k x head_size_v: mmssai.com, section "代码解读：flash_api.cpp 核心逻辑"). Reading:
+    bf16 rows, addressed like the keys (token t at page block_table_row[t // 64], slot t % 64).
+    """
+    L = int(L)
+    t = np.arange(L)
+    pages = np.asarray(block_table_row)[t // PAGE].astype(np.int64)
+    if L and (pages.min() < 0 or pages.max() >= vcache.shape[0]):
+        raise ValueError("block_table entry outside the V cache")
+    return bf16_bits_to_f64(np.asarray(vcache)[pages, t % PAGE])
+
+
 def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of query rows Q [n, d] over keys K [t, d], values V [t, dv].
 
@@ -185,6 +200,7 @@ def mla_decode(
     causal: bool = False,
     softmax_scale: Optional[float] = None,
     batches: Optional[Iterable[int]] = None,
+    vcache: Optional[np.ndarray] = None,
 ) -> Tuple[np.ndarray, np.ndarray]:
     """Reference MLA decode.
 
@@ -192,6 +208,8 @@ def mla_decode(
     kvcache       uint16 [P, 64, Hk, 576] (bf16 bits) or uint8 [P, 64, Hk, 656] (FP8 records)
     block_table   int    [B, NB]
     cache_seqlens int    [B]
+    vcache        optional uint16 [P, 64, Hk, dv] (bf16 bits): V rows from here (gather_values)
+                  instead of the first dv dims of the keys
     Returns O float64 [B, S, H, dv] and LSE float64 [B, H, S]. With `batches`,
     only those sequences are computed and the others are NaN.
     """
@@ -212,12 +230,19 @@ def mla_decode(
     O = np.full((B, S, H, dv), np.nan)
     LSE = np.full((B, H, S), np.nan)
     todo = range(B) if batches is None else [int(b) for b in batches]
+    if vcache is not None:
+        vc = np.asarray(vcache)
+        if vc.ndim != 4 or vc.shape[1] != PAGE or vc.shape[2] != Hk or vc.shape[3] != dv:
+            raise ValueError("vcache must be [pages, 64, h_kv, dv]")
     for b in todo:
         L = int(seqlens[b])
         K = gather_sequence(kv, kv_format, bt[b], L)                        # [L, Hk, 576]
+        Vsep = None if vcache is None else gather_values(vc, bt[b], L)      # [L, Hk, dv]
         for kvh in range(Hk):
             Kh = K[:, kvh, :]
             Vh = Kh[:, :dv]
+            if Vsep is not None:
+                Vh = Vsep[:, kvh, :]
             for s in range(S):
                 last = (L - S + s) if causal else (L - 1)
                 n_allowed = max(0, min(L, last + 1))
@@ -356,4 +381,5 @@ def mla_decode_workload(w, batches: Optional[Iterable[int]] = None) -> Tuple[np.
                                  w.indices.numpy(), dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale,
                                  batches=batches)
     return mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
-                      dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=batches)
+                      dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=batches,
+                      vcache=a.get("vcache"))

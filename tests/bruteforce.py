@@ -34,9 +34,12 @@ def fp8_record_to_floats(rec: bytes) -> list:
     return latent + rope
 
 
-def brute_force_decode(q_bits, kv, kv_format, block_table, seqlens, *, dv=512, causal=False, scale=None):
+def brute_force_decode(q_bits, kv, kv_format, block_table, seqlens, *, dv=512, causal=False, scale=None,
+                       vcache=None):
     """q_bits: nested lists / array [B][S][H][576] of bf16 bit patterns.
     kv: array [P][64][Hk][576] bf16 bits, or [P][64][Hk][656] uint8 records.
+    vcache (optional): array [P][64][Hk][dv] bf16 bits; V of token t is its row there
+    (same page and slot as its key) instead of the key's first dv dims.
     Returns (O [B][S][H][dv] lists, LSE [B][H][S] lists)."""
     B, S, H = len(q_bits), len(q_bits[0]), len(q_bits[0][0])
     Hk = len(kv[0][0])
@@ -56,14 +59,19 @@ def brute_force_decode(q_bits, kv, kv_format, block_table, seqlens, *, dv=512, c
         L = int(seqlens[b])
         for kvh in range(Hk):
             keys = []                      # token order, walking the block table page by page
+            vals = []
             for i, page in enumerate(block_table[b]):
                 for slot in range(64):
                     t = i * 64 + slot
                     if t >= L:
                         break
                     keys.append(row(int(page), slot, kvh))
+                    if vcache is not None:
+                        vals.append([bf16_bits_to_float(x) for x in vcache[int(page)][slot][kvh]])
                 if (i + 1) * 64 >= L:
                     break
+            if vcache is None:
+                vals = [k[:dv] for k in keys]
             for s in range(S):
                 for g in range(G):
                     h = kvh * G + g
@@ -76,7 +84,7 @@ def brute_force_decode(q_bits, kv, kv_format, block_table, seqlens, *, dv=512, c
                     z = [scale * math.fsum(q[d] * keys[t][d] for d in range(576)) for t in allowed]
                     e = [math.exp(v) for v in z]
                     tot = math.fsum(e)
-                    O[b][s][h] = [math.fsum(e[i] * keys[t][d] for i, t in enumerate(allowed)) / tot
+                    O[b][s][h] = [math.fsum(e[i] * vals[t][d] for i, t in enumerate(allowed)) / tot
                                   for d in range(dv)]
                     LSE[b][h][s] = math.log(tot)
     return O, LSE

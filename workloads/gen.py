@@ -57,6 +57,7 @@ class Workload:
     seed: int = 0
     meta: Dict[str, object] = field(default_factory=dict)
     indices: Optional[torch.Tensor] = None   # int32 [B, S, topk] for token-level sparse decode (-1: padding)
+    vcache: Optional[torch.Tensor] = None    # bf16 [P, 64, Hk, dv]: V rows apart from the keys
 
     @property
     def topk(self) -> int:
@@ -91,12 +92,15 @@ class Workload:
         """Raw views for numpy consumers: bf16 tensors as their uint16 bit patterns."""
         kv = self.kvcache
         kv_np = kv.view(torch.int16).numpy().view(np.uint16) if kv.dtype == torch.bfloat16 else kv.numpy()
-        return dict(
+        d = dict(
             q_bits=self.q.view(torch.int16).numpy().view(np.uint16),
             kvcache=kv_np,
             block_table=self.block_table.numpy(),
             cache_seqlens=self.cache_seqlens.numpy(),
         )
+        if self.vcache is not None:
+            d["vcache"] = self.vcache.view(torch.int16).numpy().view(np.uint16)
+        return d
 
 
 def _randn_bf16(gen: torch.Generator, shape, chunk_elems: int = 1 << 26) -> torch.Tensor:
@@ -157,12 +161,14 @@ def make_workload(
     max_blocks: Optional[int] = None,
     softmax_scale: Optional[float] = None,
     rng: Optional[np.random.Generator] = None,
+    vcache: bool = False,
 ) -> Workload:
     """Build one workload from explicit lengths.
 
     `pool_pages` (default: the pages the lengths need) sizes the physical
     pool; extra pages stay unreferenced. `max_blocks` widens the block table
-    beyond the longest sequence.
+    beyond the longest sequence. `vcache`: also draw a separate bf16 V cache
+    [pool, 64, h_kv, 512] (after q and the keys, from the same generator).
     """
     if kv_format not in ("bf16", "fp8"):
         raise ValueError(f"kv_format must be 'bf16' or 'fp8', got {kv_format!r}")
@@ -195,11 +201,12 @@ def make_workload(
         kv = _randn_bf16(gen, (pool, PAGE, h_kv, D_QK))
     else:
         kv = _fp8_pool(gen, pool, h_kv)
+    vc = _randn_bf16(gen, (pool, PAGE, h_kv, D_V)) if vcache else None
     scale = 1.0 / math.sqrt(D_QK) if softmax_scale is None else float(softmax_scale)
     return Workload(
         name=name, q=q, kvcache=kv, kv_format=kv_format,
         block_table=torch.from_numpy(bt), cache_seqlens=torch.from_numpy(L.astype(np.int32)),
-        causal=bool(causal), softmax_scale=scale, seed=seed,
+        causal=bool(causal), softmax_scale=scale, seed=seed, vcache=vc,
     )
 
 
@@ -262,6 +269,10 @@ WORKLOAD_SPECS: Dict[str, Dict[str, object]] = {
                 text="batch=64, s_q=1, h_q=128, all L=8192, FP8 656 B/token"),
     # token-level sparse decode over an FP8 cache: every query token attends to 2048 of its
     # sequence's 16384 cached tokens
+    # a separate bf16 V cache beside the keys (the optional V cache of the decode call)
+    "vcache": dict(batch=128, s_q=1, h_q=16, causal=False, kv_format="bf16", seed=8,
+                   lengths=("uniform", 1024, 8192), vcache=True,
+                   text="batch=128, s_q=1, h_q=16, L~U[1024,8192], separate bf16 V cache [pages, 64, 1, 512]"),
     "sparse_fp8": dict(batch=64, s_q=1, h_q=128, causal=False, kv_format="fp8", seed=6,
                        lengths=("fixed", [16384] * 64), topk=2048,
                        text="batch=64, s_q=1, h_q=128, all L=16384, topk=2048 of them per query token, "
@@ -293,7 +304,7 @@ def named_workload(name: str, **overrides) -> Workload:
     w = make_workload(name=name, batch=int(spec["batch"]), s_q=int(spec["s_q"]), h_q=int(spec["h_q"]),
                       h_kv=1, seqlens=L.tolist(), kv_format=str(spec["kv_format"]),
                       causal=bool(spec["causal"]), seed=int(spec["seed"]),
-                      pool_pages=spec.get("pool_pages"), rng=rng)
+                      pool_pages=spec.get("pool_pages"), rng=rng, vcache=bool(spec.get("vcache", False)))
     if spec.get("topk"):
         irng = np.random.Generator(np.random.PCG64(int(spec["seed"]) + 7919))
         w.indices = draw_indices(w.cache_seqlens.tolist(), w.s_q, int(spec["topk"]), w.causal, irng)
@@ -322,6 +333,11 @@ def poison_unused(w: Workload) -> Workload:
     kv2 = torch.empty((P + 1,) + tuple(kv.shape[1:]), dtype=kv.dtype)
     kv2[:P] = kv
     kv2[P] = nan_row
+    vc2 = None
+    if w.vcache is not None:
+        vc2 = torch.empty((P + 1,) + tuple(w.vcache.shape[1:]), dtype=w.vcache.dtype)
+        vc2[:P] = w.vcache
+        vc2[P] = float("nan")
     bt = w.block_table.clone()
     L = w.cache_seqlens.tolist()
     for b, Lb in enumerate(L):
@@ -330,7 +346,9 @@ def poison_unused(w: Workload) -> Workload:
         if Lb % PAGE:
             last = int(bt[b, n - 1])
             kv2[last, Lb % PAGE:] = nan_row
-    return replace(w, kvcache=kv2, block_table=bt, name=w.name + "+poison")
+            if vc2 is not None:
+                vc2[last, Lb % PAGE:] = float("nan")
+    return replace(w, kvcache=kv2, block_table=bt, vcache=vc2, name=w.name + "+poison")
 
 
 def permute_pages(w: Workload, seed: int) -> Workload:
@@ -340,12 +358,16 @@ def permute_pages(w: Workload, seed: int) -> Workload:
     perm = torch.from_numpy(rng.permutation(P).astype(np.int64))   # new position of old page i
     kv2 = torch.empty_like(w.kvcache)
     kv2[perm] = w.kvcache
+    vc2 = None
+    if w.vcache is not None:
+        vc2 = torch.empty_like(w.vcache)
+        vc2[perm] = w.vcache
     bt = w.block_table.clone()
     L = w.cache_seqlens.tolist()
     for b, Lb in enumerate(L):
         n = (Lb + PAGE - 1) // PAGE
         bt[b, :n] = perm[w.block_table[b, :n].long()].to(torch.int32)
-    return replace(w, kvcache=kv2, block_table=bt, name=w.name + "+permuted")
+    return replace(w, kvcache=kv2, block_table=bt, vcache=vc2, name=w.name + "+permuted")
 
 
 def dense_as_sparse(w: Workload) -> Workload:
