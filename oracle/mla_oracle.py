@@ -145,10 +145,10 @@ def gather_values(vcache: np.ndarray, block_table_row: np.ndarray, L: int) -> np
     """
     L = int(L)
     t = np.arange(L)
-    pages = np.asarray(block_table_row)[t // PAGE].astype(np.int64)
-    if L and (pages.min() < 0 or pages.max() >= vcache.shape[0]):
+    page_of = np.asarray(block_table_row).astype(np.int64)[t // PAGE]
+    if L and (page_of.min() < 0 or page_of.max() >= vcache.shape[0]):
         raise ValueError("block_table entry outside the V cache")
-    return bf16_bits_to_f64(np.asarray(vcache)[pages, t % PAGE])
+    return bf16_bits_to_f64(np.asarray(vcache)[page_of, t % PAGE])
 
 
 def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:

@@ -110,10 +110,10 @@ VC_MUTANTS = {
     "ignore_vcache": ("            if Vsep is not None:\n                Vh = Vsep[:, kvh, :]",
                       "            if False:\n                Vh = Vsep[:, kvh, :]"),
     "v_head0": ("Vh = Vsep[:, kvh, :]", "Vh = Vsep[:, 0, :]"),
-    "v_slot": ("return bf16_bits_to_f64(np.asarray(vcache)[pages, t % PAGE])",
-               "return bf16_bits_to_f64(np.asarray(vcache)[pages, (t + 1) % PAGE])"),
-    "v_page": ("    pages = np.asarray(block_table_row)[t // PAGE].astype(np.int64)\n    if L and (pages.min() < 0 or pages.max() >= vcache.shape[0]):",
-               "    pages = np.asarray(block_table_row)[t // PAGE].astype(np.int64)[::-1]\n    if L and (pages.min() < 0 or pages.max() >= vcache.shape[0]):"),
+    "v_slot": ("return bf16_bits_to_f64(np.asarray(vcache)[page_of, t % PAGE])",
+               "return bf16_bits_to_f64(np.asarray(vcache)[page_of, (t + 1) % PAGE])"),
+    "v_page": ("page_of = np.asarray(block_table_row).astype(np.int64)[t // PAGE]",
+               "page_of = np.asarray(block_table_row).astype(np.int64)[t // PAGE][::-1]"),
 }
 
 
