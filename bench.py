@@ -79,6 +79,8 @@ def algorithmic_work(w):
         byts = (n_att * Hk * bpt + B * S * H * (576 * 2 + 512 * 2 + 4) + n_att * 4 + idx.size * 4 + B * 4)
         return byts, 2 * (576 + 512) * H * n_att, n_att * Hk * bpt
     kv = sum(Hk * l * bpt for l in L)
+    if getattr(w, "vcache", None) is not None:
+        kv += sum(Hk * l * w.dv * 2 for l in L)       # the separate V rows
     q = B * S * H * 576 * 2
     o = B * S * H * 512 * 2
     lse = B * S * H * 4
@@ -177,7 +179,8 @@ def _oracle_sample(w, target_s: float):
                                      idx, dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
         else:
             oracle.mla_decode(a["q_bits"], a["kvcache"], w.kv_format, a["block_table"], a["cache_seqlens"],
-                              dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b])
+                              dv=w.dv, causal=w.causal, softmax_scale=w.softmax_scale, batches=[b],
+                              vcache=a.get("vcache"))
         t_total += time.perf_counter() - t0
         done.append(b)
         n += 1
@@ -192,6 +195,8 @@ def _oracle_sample(w, target_s: float):
             w.h_q * (576 * 2 + 512 * 2 + 4) + 4 * w.topk) + 4 * len(done)
         return done, t_total, byts, sum(toks)
     L = [int(a["cache_seqlens"][b]) for b in done]
+    if "vcache" in a:
+        bpt += w.dv * 2
     byts = sum(w.h_kv * l * bpt for l in L) + len(done) * w.s_q * w.h_q * (576 * 2 + 512 * 2 + 4) \
         + sum((l + 63) // 64 for l in L) * 4 + 4 * len(done)
     return done, t_total, byts, sum(L)
@@ -368,8 +373,11 @@ def mfma_summary(args) -> str:
 
 
 def split_kernel_name(w) -> str:
-    """Name of the split kernel a workload runs: the 128-row one-barrier kernel above 64 rows
-    per KV head and for every sparse workload (decode and prefill), else the 64-row kernel."""
+    """Name of the split kernel a workload runs: the separate-V-cache kernel when there is a V
+    cache, the 128-row one-barrier kernel above 64 rows per KV head and for every sparse
+    workload (decode and prefill), else the 64-row kernel."""
+    if getattr(w, "vcache", None) is not None:
+        return "splitkv_vc_kernel"
     if is_prefill(w) or getattr(w, "indices", None) is not None or w.heads_per_kv > 64:
         return "splitkv_x1_kernel"
     return "splitkv_kernel"
@@ -578,6 +586,8 @@ def main():
     w = named_workload(args.workload)
     byts, flops, kv_bytes = algorithmic_work(w)
     pool_bytes = w.kvcache.numel() * w.kvcache.element_size()
+    if w.vcache is not None:
+        pool_bytes += w.vcache.numel() * w.vcache.element_size()
     copies = args.copies or max(1, math.ceil(2 * INFINITY_CACHE_BYTES / max(pool_bytes, 1)))
     print(f"[bench] {w.name}: {WORKLOAD_SPECS[w.name]['text']}; pool {pool_bytes / 1e6:.1f} MB x {copies} copies",
           file=sys.stderr, flush=True)
@@ -587,6 +597,7 @@ def main():
     L_dev = w.cache_seqlens.to(dev)
     L_host = w.cache_seqlens.clone().pin_memory()
     kvs = [w.kvcache.to(dev) for _ in range(copies)]
+    vcs = [w.vcache.to(dev) if w.vcache is not None else None for _ in range(copies)]
     M = w.heads_per_kv
     sparse = getattr(w, "indices", None) is not None
     nseq = w.batch * w.s_q if sparse else w.batch
@@ -616,8 +627,8 @@ def main():
     _, s_host = host_metadata()
     max_splits = mla.max_splits_of(s_host)
     decoders = [mla.MlaDecoder(q, kv, bt, L_dev, w.dv, meta_dev, splits_dev, w.causal, w.softmax_scale,
-                               out=out, lse=lse, workspace=ws, max_splits=max_splits, indices=idx_dev)
-                for kv in kvs]
+                               out=out, lse=lse, workspace=ws, max_splits=max_splits, indices=idx_dev, vcache=vc)
+                for kv, vc in zip(kvs, vcs)]
     stream = torch.cuda.current_stream(dev)
     hip = HipEvents()
 
@@ -722,7 +733,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
                    "d_qk": 576, "d_v": 512, "page": 64, "kv_format": w.kv_format, "causal": w.causal,
                    "total_kv_tokens": int(w.cache_seqlens.sum()), "num_parts": parts, "kv_copies": copies,
-                   **({"topk": w.topk} if sparse else {})},
+                   **({"topk": w.topk} if sparse else {}), **({"vcache": True} if w.vcache is not None else {})},
         "tflops": round(tflops, 2),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),

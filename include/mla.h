@@ -244,6 +244,19 @@ typedef struct mla_decode_args {
   const int32_t* indices;
   int64_t idx_stride[2];
   int topk;
+
+  /* Optional separate V cache (the vcache_ argument of mha_fwd_kvcache_mla,
+     num_blocks x page_block_size x num_heads_k x head_size_v: mmssai.com,
+     "代码解读：flash_api.cpp 核心逻辑"). NULL: V is the first dv dims of each
+     cached key row. Otherwise bf16 [num_pages, 64, h_kv, dv]: the value of
+     cached token t is its row here, at the same page and slot as its key (the
+     same block_table); strides in elements for (page, token, head), each row
+     contiguous, base and strides 16-byte aligned, a 64-token page spanning less
+     than 2 GiB. Needs kv_format MLA_KV_BF16 and dense decode (indices NULL);
+     the workspace size is unchanged. Runs on 64-row tiles (ceil(s_q * h_q /
+     h_kv / 64) workgroups per range and KV head). */
+  const void* vcache;
+  int64_t vc_stride[3];
 } mla_decode_args;
 
 /*

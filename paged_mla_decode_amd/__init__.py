@@ -235,7 +235,7 @@ class MlaDecoder:
 
     def __init__(self, q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal=False,
                  softmax_scale=None, *, out=None, lse=None, workspace=None, events=None, max_splits=None,
-                 no_alloc=False, indices=None):
+                 no_alloc=False, indices=None, vcache=None):
         dev = q.device
         if dev.type != "cuda":
             raise ValueError("q must be a CUDA (HIP) tensor")
@@ -264,6 +264,11 @@ class MlaDecoder:
             _check_tensor("indices", indices, torch.int32, 3, dev)
             if tuple(indices.shape[:2]) != (B, S) or indices.shape[2] < 1 or indices.stride(-1) != 1:
                 raise ValueError("indices must be int32 [batch, s_q, topk] with a contiguous last dimension")
+        if vcache is not None:
+            _check_tensor("vcache", vcache, torch.bfloat16, 4, dev)
+            if (tuple(vcache.shape) != (int(kvcache.shape[0]), PAGE_TOKENS, Hk, int(dv))
+                    or vcache.stride(-1) != 1):
+                raise ValueError("vcache must be bf16 [num_pages, 64, h_kv, dv] with a contiguous last dimension")
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(D)
         rows = S * H // max(Hk, 1)
@@ -287,7 +292,7 @@ class MlaDecoder:
         if workspace is None and not no_alloc:
             workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
         self.tensors = (q, kvcache, block_table, cache_seqlens, tile_metadata, num_splits, out, lse, workspace,
-                        indices)
+                        indices, vcache)
         self.out, self.lse, self.workspace = out, lse, workspace
         a = MlaDecodeArgs()
         a.q = q.data_ptr()
@@ -318,6 +323,9 @@ class MlaDecoder:
             a.indices = indices.data_ptr()
             a.idx_stride[:] = [indices.stride(0), indices.stride(1)]
             a.topk = int(indices.shape[2])
+        if vcache is not None:
+            a.vcache = vcache.data_ptr()
+            a.vc_stride[:] = [vcache.stride(0), vcache.stride(1), vcache.stride(2)]
         self.args = a
         if events is not None:
             self.set_events(events)
@@ -342,7 +350,8 @@ class MlaDecoder:
 def mla_decode_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
                        dv: int, tile_metadata: torch.Tensor, num_splits: torch.Tensor, causal: bool = False,
                        softmax_scale: Optional[float] = None, *, out=None, lse=None, workspace=None,
-                       indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                       indices: Optional[torch.Tensor] = None,
+                       vcache: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """o [batch, s_q, h_q, dv] bf16 and lse [batch, h_q, s_q] fp32 for one layer.
 
     q bf16 [batch, s_q, h_q, 576]; kvcache bf16 [pages, 64, h_kv, 576] or uint8
@@ -351,9 +360,11 @@ def mla_decode_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torc
     for these lengths. causal: query token s of s_q reads keys t <= L - s_q + s.
     softmax_scale defaults to 1/sqrt(576). indices (optional, int32 [batch, s_q, topk]):
     token-level sparse decode -- query token s of sequence b attends only to the listed cached
-    positions of b (-1: padding); its metadata comes from mla_get_metadata_sparse."""
+    positions of b (-1: padding); its metadata comes from mla_get_metadata_sparse. vcache
+    (optional, bf16 [pages, 64, h_kv, dv]): V rows from here, at the keys' pages and slots,
+    instead of the first dv dims of the keys (bf16 keys, dense decode)."""
     dec = MlaDecoder(q, kvcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal, softmax_scale,
-                     out=out, lse=lse, workspace=workspace, indices=indices)
+                     out=out, lse=lse, workspace=workspace, indices=indices, vcache=vcache)
     return dec.run()
 
 

@@ -63,6 +63,8 @@ class MlaDecodeArgs(ctypes.Structure):
         ("indices", ctypes.c_void_p),
         ("idx_stride", ctypes.c_int64 * 2),
         ("topk", ctypes.c_int),
+        ("vcache", ctypes.c_void_p),
+        ("vc_stride", ctypes.c_int64 * 3),
     ]
 
 

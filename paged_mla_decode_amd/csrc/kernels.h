@@ -53,6 +53,10 @@ struct DecodeParams {
   // (64-row pages, page i = rows 64 i .. 64 i + 63, kv_sp = 64 kv_st); no block table, no
   // seqlens: every query token's length is kv_rows.
   int kv_rows;
+  // A separate V cache (non-null: bf16 rows of kDv dims, byte strides page / token / head;
+  // same block table as the keys); bf16 keys, dense decode only.
+  const uint8_t* vcache;
+  int64_t vc_sp, vc_st, vc_sh;
 };
 
 // The row-tile split kernel (mla_kernels_x.hip): 128-row tiles, 8 waves of
@@ -63,6 +67,10 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
                           hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_split_x_sparse(const DecodeParams& p, int kv_format, int grid, hipStream_t stream,
                                  hipEvent_t ev_start, hipEvent_t ev_stop);
+// The separate-V-cache split kernel (mla_kernels_x.hip): 64-row tiles, 4 waves;
+// fp16 block-scaled partials when p.part_o16 is set (more than 64 rows), else fp32.
+hipError_t launch_split_vc(const DecodeParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop);
 
 hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format, hipStream_t stream,
                          void* const events[3]);

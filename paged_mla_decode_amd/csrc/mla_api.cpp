@@ -177,7 +177,30 @@ mla_status decode_impl(const mla_decode_args* a, void* hip_stream, bool use_scra
   const bool sparse = a->indices != nullptr;
   const int vbatch = sparse ? a->batch * a->s_q : a->batch;
   const int rows = sparse ? group : a->s_q * group;
-  const mla::Plan plan = sparse ? mla::make_plan_sparse(group) : mla::make_plan(rows, a->kv_format);
+  mla::Plan plan = sparse ? mla::make_plan_sparse(group) : mla::make_plan(rows, a->kv_format);
+  int64_t vcb[3] = {0, 0, 0};
+  if (a->vcache) {
+    if (a->kv_format != MLA_KV_BF16)
+      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: a separate V cache needs bf16 keys (kv_format 0)");
+    if (sparse) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: a separate V cache with indices");
+    for (int k = 0; k < 3; ++k) {
+      vcb[k] = a->vc_stride[k] * 2;
+      if (a->vc_stride[k] < 0 || (vcb[k] % 16) != 0)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: vc_stride[%d] must be non-negative and a multiple "
+                    "of 16 bytes", k);
+    }
+    const int64_t vrow = mla::kDv * 2;
+    if (vcb[0] < vrow || vcb[1] < vrow || (a->h_kv > 1 && vcb[2] < vrow))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: a vcache stride is smaller than one V row (%lld bytes)",
+                  static_cast<long long>(vrow));
+    if (!aligned16(a->vcache))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: vcache must be 16-byte aligned");
+    if (vcb[1] * mla::kPage >= (int64_t{1} << 31))
+      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_kvcache: a 64-token V page must span less than 2 GiB");
+    // 64-row tiles whatever the row count; the partial format (plan.wide) stays the plain decode's
+    plan.m_tile = 64;
+    plan.m_tiles = (rows + 63) / 64;
+  }
   int64_t pool_bytes = 0;
   if (sparse) {
     if (a->topk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode_kvcache: topk must be >= 1 with indices");
@@ -250,6 +273,12 @@ mla_status decode_impl(const mla_decode_args* a, void* hip_stream, bool use_scra
     p.sq_real = a->s_q;
     p.real_causal = a->causal ? 1 : 0;
     p.pool_bytes = pool_bytes;
+  }
+  if (a->vcache) {
+    p.vcache = static_cast<const uint8_t*>(a->vcache);
+    p.vc_sp = vcb[0];
+    p.vc_st = vcb[1];
+    p.vc_sh = vcb[2];
   }
   p.scale_log2 = static_cast<float>(static_cast<double>(a->softmax_scale) * 1.4426950408889634074);
   p.o = static_cast<uint16_t*>(a->o);

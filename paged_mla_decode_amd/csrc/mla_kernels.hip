@@ -944,6 +944,8 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   hipError_t err;
   if (p.topk > 0) {
     err = launch_split_x_sparse(p, kv_format, grid, stream, ev0, ev1);
+  } else if (p.vcache != nullptr) {
+    err = launch_split_vc(p, grid, stream, ev0, ev1);
   } else if (plan.wide) {
     err = launch_split_x(p, kv_format, plan.m_tile / 4, grid, stream, ev0, ev1);
   } else if (plan.rb == 1) {

@@ -1031,6 +1031,296 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
   wait_vm_all();
 }
 
+// ----------------------------------------------------------------------------
+// A separate V cache (the optional vcache of the decode call: bf16 rows
+// [pages, 64, h_kv, 512] addressed through the same block table as the keys;
+// mmssai.com, "代码解读：flash_api.cpp 核心逻辑").
+//
+// 64-row tiles on 4 wavefronts: wave w owns rows 16 w .. 16 w + 15 and keeps
+// their whole O (512 dims, 128 accumulator registers) and all of Q in
+// registers, so P never leaves the wave and no exchange is needed. Units of 32
+// tokens stream into a two-slot ring; a slot holds the unit's keys (36 KB in
+// the xk_off layout) and its values (32 KB, the same layout over 64 chunks).
+// One barrier per unit: after it, the loads of the next unit go out into the
+// other slot (free: every wave has finished the unit before) and land while
+// this one is computed. More than 64 rows per KV head take several row tiles;
+// WIDE (more than 64 rows) writes the fp16 block-scaled partials of the
+// 128-row kernels, otherwise fp32 partials, so the workspace and the combine
+// are those of the plain decode.
+// ----------------------------------------------------------------------------
+
+constexpr int kVcWaves = 4;
+constexpr int kVcThreads = 64 * kVcWaves;
+constexpr int kVcRows = 16 * kVcWaves;                       // rows per workgroup
+constexpr int kVcKBytes = kXHalfBytes;                       // 36864: keys of a unit
+constexpr int kVcVBytes = kXHalf * kDv * 2;                  // 32768: values of a unit
+constexpr int kVcSlot = kVcKBytes + kVcVBytes;
+constexpr int kVcLds = 2 * kVcSlot;                          // 139264
+static_assert(kVcLds <= 163840, "LDS budget");
+
+// Direct loads of one unit into a slot: keys (k = wave + 4 j, j < 9: column
+// block j, tokens 8 wave .. + 7) and values (j < 8), each buffer ending after
+// the unit's `valid` tokens, so rows past them read zeros.
+__device__ __forceinline__ void vc_issue(const uint8_t* ksrc, const uint8_t* vsrc, int valid, uint8_t* dst, int wave,
+                                         uint32_t koff, uint32_t voff, int kst, int vst) {
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ksrc), 0, valid * kst, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vsrc), 0, valid * vst, kRawBufferWord3);
+#pragma unroll
+  for (int j = 0; j < 9; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(void, dst + 1024 * (wave + 4 * j)), 16, koff,
+                                             8 * wave * kst + 128 * j, 0, kPageLoadPolicy);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(void, dst + kVcKBytes + 1024 * (wave + 4 * j)), 16, voff,
+                                             8 * wave * vst + 128 * j, 0, kPageLoadPolicy);
+}
+
+// S, softmax and PV of one unit for this wave's 16 rows: keys at kpage, values at vpage.
+__device__ __forceinline__ void vc_unit(const uint8_t* __restrict__ kpage, const uint8_t* __restrict__ vpage,
+                                        const XLane& ln, const bf16x8 (&qf)[18], int L, int last_ok, int tok0,
+                                        float scale_log2, float& m_run, float& l_run, f32x4 (&acc)[32]) {
+  const int q4 = ln.q4;
+  auto kload = [&](int c, int tt) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(kpage + ln.k_off[c & 1] + 16 * tt * 128 + 4096 * (c >> 1));
+  };
+  f32x4 s[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    bf16x8 kbuf[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) kbuf[0][tt] = kload(0, tt);
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+      if (c + 1 < 18) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) kbuf[(c + 1) & 1][tt] = kload(c + 1, tt);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[c & 1][tt], qf[c], s[tt], 0, 0, 0);
+    }
+  }
+  // mask (sequence end, causal limit) and online softmax; lane (r16, q4) holds tokens
+  // 16 tt + 4 q4 + i of row r16
+  const int lim = min(L - 1, last_ok) - tok0 - 4 * q4;
+  float mx = kNegInf;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = (16 * tt + i <= lim) ? s[tt][i] * scale_log2 : kNegInf;
+      s[tt][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max4lanes(mx);
+  const bool grow = mx > m_run + kRescaleSlack;
+  const bool rescale = grow && m_run != kNegInf;
+  const float alpha = rescale ? fast_exp2(m_run - mx) : 1.f;
+  l_run *= alpha;
+  m_run = grow ? mx : m_run;
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[d] *= alpha;      // this lane's row only
+  }
+  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+  bf16x8 pv;
+  float psum = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(s[tt][i] - m_use);
+      psum += e;
+      pv[4 * tt + i] = static_cast<__bf16>(e);
+    }
+  l_run += psum;
+  // O^T[dims 16 d + 4 q4 + i][row r16] += V^T P^T: P^T (k-slots: tokens 4 q4 + j, then 16 + 4 q4 + j)
+  // is pv itself; V^T by transposed reads in the same token order
+  auto vload = [&](int d) -> bf16x8 {
+    const uint8_t* a0 = vpage + ln.v_off[d & 3] + 4096 * (d >> 2);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * 128));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  constexpr int kAhead = 4;
+  bf16x8 va[kAhead];
+#pragma unroll
+  for (int d = 0; d < kAhead; ++d) va[d] = vload(d);
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const bf16x8 a = va[d % kAhead];
+    if (d + kAhead < 32) va[d % kAhead] = vload(d + kAhead);
+    acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pv, acc[d], 0, 0, 0);
+  }
+}
+
+template <bool WIDE>
+__global__ void __launch_bounds__(kVcThreads) splitkv_vc_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kVcLds];
+  XLane ln;
+  ln.tid = threadIdx.x;
+  ln.lane = ln.tid & 63;
+  ln.wave = __builtin_amdgcn_readfirstlane(ln.tid >> 6);
+  ln.r16 = ln.lane & 15;
+  ln.q4 = ln.lane >> 4;
+  ln.k_off[0] = xk_off(ln.r16, ln.q4);
+  ln.k_off[1] = xk_off(ln.r16, 4 + ln.q4);
+  {
+    const int tok = 4 * ln.q4 + (ln.r16 >> 2);
+    const int hh = (ln.r16 & 3) >> 1, half8 = ln.r16 & 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ln.v_off[e] = xk_off(tok, 2 * e + hh) + 8 * half8;
+  }
+  const int wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
+
+  const int per_xcd = gridDim.x / 8;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= p.grid_wgs) return;
+  const int m_tiles = (p.rows + kVcRows - 1) / kVcRows;
+  const int mt = logical % m_tiles;
+  const int kvh = (logical / m_tiles) % p.h_kv;
+  const int part = logical / (m_tiles * p.h_kv);
+  Range r;
+  if (!read_range(p, part, r)) return;
+
+  const int srow = mt * kVcRows + 16 * wave + r16;
+  const bool srow_ok = srow < p.rows;
+  const int s_idx = srow_ok ? srow / p.group : 0;
+  const int shead = kvh * p.group + (srow_ok ? srow % p.group : 0);
+  const int kst = static_cast<int>(p.kv_st), vst = static_cast<int>(p.vc_st);
+  const uint32_t koff = x_load_off(ln.lane, kst), voff = x_load_off(ln.lane, vst);
+  const uint8_t* const k_head = p.kv + kvh * p.kv_sh;
+  const uint8_t* const v_head = p.vcache + kvh * p.vc_sh;
+
+  // loads of unit u into `dst`; false (nothing issued) for a block-table entry outside the pool
+  auto issue_unit = [&](const XUnit& u, uint8_t* dst) -> bool {
+    const int pg = ld_meta(p.block_table + static_cast<int64_t>(u.b) * p.bt_stride + u.pi);
+    if (pg < 0 || pg >= p.num_pages) return false;
+    const int valid = min(u.L - (u.pi * kPage + u.hf * kXHalf), kXHalf);
+    const uint8_t* ks = k_head + static_cast<int64_t>(pg) * p.kv_sp + static_cast<int64_t>(u.hf * kXHalf) * p.kv_st;
+    const uint8_t* vs = v_head + static_cast<int64_t>(pg) * p.vc_sp + static_cast<int64_t>(u.hf * kXHalf) * p.vc_st;
+    vc_issue(ks, vs, valid, dst, wave, koff, voff, kst, vst);
+    return true;
+  };
+
+  XUnit u = x_seek(p, r, r.begin_b);
+  bool ok = true;
+  int slot = 0;
+  if (u.b <= r.end_b) ok = issue_unit(u, lds);
+
+  for (int b = r.begin_b; b <= r.end_b; ++b) {
+    int L, pg0, pg1;
+    bool len_ok;
+    seq_pages(p, r, b, L, pg0, pg1, len_ok);
+    const int split_idx = (b == r.begin_b) ? r.split0 : 0;
+    const int slot0 = ld_meta(p.num_splits + b);
+    const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
+    const int last_ok = p.causal ? (L - p.s_q + s_idx) : (L - 1);
+
+    bf16x8 qf[18];
+    {
+      const uint16_t* qrow = p.q + b * p.q_sb + s_idx * p.q_ss + shead * p.q_sh;
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
+        const u32x4 v = srow_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+        qf[c] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 acc[32];
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool bad = r.stale || !len_ok;
+
+    // Invariant at the top: the loads of unit u into `slot` are issued (none if !ok).
+    while (u.b == b) {
+      const XUnit un = x_next(p, r, u);
+      wait_vm_all();                          // this wave's loads of u (and Q) landed
+      lds_barrier_keep_loads();               // every wave's loads of u landed; the other slot is free
+      bool ok_n = true;
+      if (un.b <= r.end_b) ok_n = issue_unit(un, lds + (slot ^ 1) * kVcSlot);
+      bad |= !ok;
+      const uint8_t* cur = lds + slot * kVcSlot;
+      vc_unit(cur, cur + kVcKBytes, ln, qf, L, last_ok, u.pi * kPage + u.hf * kXHalf, p.scale_log2, m_run, l_run,
+              acc);
+      slot ^= 1;
+      u = un;
+      ok = ok_n;
+    }
+
+    // ---- epilogue: this lane's row, dims 16 d + 4 q4 .. + 3 ----
+    const float l_tot = sum4lanes(l_run);
+    float lse = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+    if (bad) lse = __builtin_nanf("");
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int d = 0; d < 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[d][i] = bad ? nan : acc[d][i] * inv;
+    if (nsplit == 1) {
+      if (srow_ok) {
+        if (q4 == 0) p.lse[lse_index(p, b, shead, s_idx)] = lse;
+        uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + shead) * kDv + 4 * q4;
+#pragma unroll
+        for (int d = 0; d < 32; ++d) {
+          u32x2 w;
+          w[0] = static_cast<uint32_t>(f32_to_bf16(acc[d][0])) | (static_cast<uint32_t>(f32_to_bf16(acc[d][1])) << 16);
+          w[1] = static_cast<uint32_t>(f32_to_bf16(acc[d][2])) | (static_cast<uint32_t>(f32_to_bf16(acc[d][3])) << 16);
+          *reinterpret_cast<u32x2*>(orow + 16 * d) = w;
+        }
+      }
+    } else {
+      const int pslot = slot0 + split_idx;
+      const bool slot_ok = pslot >= 0 && pslot < p.max_slots && split_idx < nsplit;
+      const int64_t prow = (static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + srow;
+      if constexpr (WIDE) {
+        // fp16 with a power-of-two scale per 64-dim block (block g: d = 4 g .. 4 g + 3)
+#pragma unroll
+        for (int g = 0; g < kPartBlocks; ++g) {
+          float mx = 0.f;
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, finite_abs(acc[4 * g + dd][i]));
+          float scl, bi;
+          part_block_scale(max4lanes(mx), scl, bi);
+          u32x4 w[2];
+          int off[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4& x = acc[4 * g + 2 * h];
+            const f32x4& y = acc[4 * g + 2 * h + 1];
+            u32x2 a, c;
+            a[0] = pack_f16x2(x[0] * bi, x[1] * bi);
+            a[1] = pack_f16x2(x[2] * bi, x[3] * bi);
+            c[0] = pack_f16x2(y[0] * bi, y[1] * bi);
+            c[1] = pack_f16x2(y[2] * bi, y[3] * bi);
+            w[h] = span_f16x8(a, c, q4, &off[h]);
+          }
+          if (srow_ok && slot_ok) {
+            uint16_t* const po = p.part_o16 + prow * kDv + 64 * g;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(po + 32 * h + off[h]) = w[h];
+            if (q4 == 0) p.part_scale[prow * kPartBlocks + g] = scl;
+          }
+        }
+      } else {
+        if (srow_ok && slot_ok) {
+          float* const po = p.part_o32 + prow * kDv + 4 * q4;
+#pragma unroll
+          for (int d = 0; d < 32; ++d) *reinterpret_cast<f32x4*>(po + 16 * d) = acc[d];
+        }
+      }
+      if (srow_ok && slot_ok && q4 == 0) p.part_lse[prow] = lse;
+    }
+  }
+  wait_vm_all();
+}
+
 }  // namespace
 
 hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wave, int grid, hipStream_t stream,
@@ -1041,6 +1331,16 @@ hipError_t launch_split_x(const DecodeParams& p, int kv_format, int rows_per_wav
     hipExtLaunchKernelGGL((splitkv_x1_kernel<kFmtFp8, false>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
   else
     hipExtLaunchKernelGGL((splitkv_x1_kernel<kFmtBf16, false>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_vc(const DecodeParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop) {
+  const dim3 g(grid), blk(kVcThreads);
+  if (p.part_o16 != nullptr)
+    hipExtLaunchKernelGGL((splitkv_vc_kernel<true>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
+  else
+    hipExtLaunchKernelGGL((splitkv_vc_kernel<false>), g, blk, 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 

@@ -292,3 +292,22 @@ def test_prefill_rejects_bad_strides(which, k, value):
     getattr(a, which)[k] = value
     assert lib.mla_sparse_prefill_fwd(ctypes.byref(a), None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_sparse_prefill_fwd(None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("edit,status", [
+    (lambda a: (setattr(a, "kv_format", 1), a.kv_stride.__setitem__(slice(0, 3), [64 * 656, 656, 656])),
+     _lib.MLA_ERR_UNSUPPORTED),                                                 # FP8 keys
+    (lambda a: (setattr(a, "indices", 1 << 20), setattr(a, "topk", 4)), _lib.MLA_ERR_UNSUPPORTED),
+    (lambda a: a.vc_stride.__setitem__(1, 100), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.vc_stride.__setitem__(1, 256), _lib.MLA_ERR_INVALID_ARGUMENT),  # smaller than a V row
+    (lambda a: setattr(a, "vcache", (1 << 20) + 8), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.vc_stride.__setitem__(1, 1 << 24), _lib.MLA_ERR_UNSUPPORTED),   # 64-token page past 2 GiB
+])
+def test_decode_rejects_bad_vcache(edit, status):
+    lib = _lib.load()
+    a = _valid_args()
+    a.vcache = 1 << 20
+    a.vc_stride[:] = [64 * 512, 512, 512]
+    edit(a)
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == status
+    assert b"mla_decode_kvcache" in lib.mla_last_error()
