@@ -760,10 +760,24 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
       x1_issue(src, valid, dst, wave, ld_off, st);
   };
 
-  const int srow = mt * M_TILE + 16 * wave + r16;
-  const bool srow_ok = srow < p.rows;
-  const int s_idx = srow_ok ? srow / p.group : 0;
-  const int shead = kvh * p.group + (srow_ok ? srow % p.group : 0);
+  // This lane's S-phase row (row 16 wave + r16 of the tile) and its query token and head. They
+  // are needed before and after the unit loop, not in it: recomputed from an opaque copy of r16
+  // at each use so they are not held (and spilled) across the loop -- a spill reload waits for
+  // every memory operation in flight, and the epilogue had several, each a memory round trip.
+  struct RowIdx {
+    int srow, s_idx, shead;
+    bool ok;
+  };
+  auto row_idx = [&]() -> RowIdx {
+    int rr = r16;
+    asm volatile("" : "+v"(rr));
+    RowIdx x;
+    x.srow = mt * M_TILE + 16 * wave + rr;
+    x.ok = x.srow < p.rows;
+    x.s_idx = x.ok ? x.srow / p.group : 0;
+    x.shead = kvh * p.group + (x.ok ? x.srow % p.group : 0);
+    return x;
+  };
 
   const uint8_t* const kv_head = p.kv + kvh * p.kv_sh;
   uint32_t win_lo = 0, win_hi = 0;
@@ -842,21 +856,22 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
     const int split_idx = (b == r.begin_b) ? r.split0 : 0;
     const int slot0 = ld_meta(p.num_splits + b);
     const int nsplit = ld_meta(p.num_splits + b + 1) - slot0;
-    const int last_ok = p.causal ? (L - p.s_q + s_idx) : (L - 1);
+    const RowIdx ri = row_idx();
+    const int last_ok = p.causal ? (L - p.s_q + ri.s_idx) : (L - 1);
 
     bf16x8 qf[X1Layout::kRegChunks];
     F8Q q8;
     if constexpr (kFp8) {
       // hi codes and scales in registers, lo codes in this wave's rows of the LDS
-      const uint16_t* qrow = p.q + b * p.q_sb + s_idx * p.q_ss + shead * p.q_sh;
-      f8_qsetup(qrow, srow_ok, 16 * wave + r16, q4, lds, q8);
+      const uint16_t* qrow = p.q + b * p.q_sb + ri.s_idx * p.q_ss + ri.shead * p.q_sh;
+      f8_qsetup(qrow, ri.ok, 16 * wave + r16, q4, lds, q8);
     } else {
     {
-      const uint16_t* qrow = p.q + b * p.q_sb + s_idx * p.q_ss + shead * p.q_sh;
+      const uint16_t* qrow = p.q + b * p.q_sb + ri.s_idx * p.q_ss + ri.shead * p.q_sh;
 #pragma unroll
       for (int c = 0; c < 18; ++c) {
         if (X1Layout::qslot(c) >= 0) continue;
-        const u32x4 v = srow_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = ri.ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
         qf[X1Layout::qreg(c)] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -866,7 +881,9 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
       const int q_bytes = 2 * static_cast<int>((p.s_q - 1) * p.q_ss + (p.h_q - 1) * p.q_sh + kDqk);
       const __amdgpu_buffer_rsrc_t qrsrc =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qb), 0, q_bytes, kRawBufferWord3);
-      const int lrow = ln.lane >> 2, pslot = ln.lane & 3;
+      int lane_q = ln.lane;
+      asm volatile("" : "+v"(lane_q));          // offsets computed here, not held across the unit loop
+      const int lrow = lane_q >> 2, pslot = lane_q & 3;
 #pragma unroll
       for (int j = 0; j < (X1Layout::kQChunks * 8 + kWW - 1) / kWW; ++j) {
         const int k = wave + kWW * j;
@@ -958,14 +975,15 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
     float* lrow = reinterpret_cast<float*>(lds + X::kP);
     {
       const float l_tot = sum4lanes(l_run);
-      if (q4 == 0) lrow[16 * wave + r16] = l_tot;
-      if (q4 == 0 && srow_ok) {
+      const RowIdx re = row_idx();
+      if (q4 == 0) lrow[re.srow - mt * M_TILE] = l_tot;
+      if (q4 == 0 && re.ok) {
         float lse = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
         if (bad) lse = __builtin_nanf("");
         if (nsplit == 1)
-          p.lse[lse_index(p, b, shead, s_idx)] = lse;
+          p.lse[lse_index(p, b, re.shead, re.s_idx)] = lse;
         else if (slot0 + split_idx < p.max_slots && split_idx < nsplit)
-          p.part_lse[(static_cast<int64_t>(slot0 + split_idx) * p.h_kv + kvh) * p.rows + srow] = lse;
+          p.part_lse[(static_cast<int64_t>(slot0 + split_idx) * p.h_kv + kvh) * p.rows + re.srow] = lse;
       }
     }
     lds_barrier_keep_loads();
