@@ -323,7 +323,8 @@ def pmc_summary(args) -> str:
     return "\n".join(lines) + "\n"
 
 
-MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
 SIMDS = 256 * 4
 XCDS = 8
 
@@ -340,6 +341,8 @@ def mfma_summary(args) -> str:
     rows = _pmc_rows(args.mfma_summary)
     busy = _per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", is_split)
     mops = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16", is_split)
+    mops8 = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_F8", is_split) or [0.0]
+    mops64 = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_F6F4", is_split) or [0.0]
     gui = _per_dispatch(rows, "GRBM_GUI_ACTIVE", is_split)
     if not (busy and mops and gui):
         raise SystemExit("missing split-kernel dispatches or MFMA counters in the counter files")
@@ -353,6 +356,7 @@ def mfma_summary(args) -> str:
     dur_us = med(list(dur_ns.values())) / 1e3
     util = med(busy) / (active * SIMDS)
     mfma_flops = med(mops) * 512.0
+    f8_flops = (med(mops8) + med(mops64)) * 512.0
     lines = [
         f"# MFMA utilisation of {split_name} on workload {w.name} (rocprofv3 --pmc)",
         f"kernel: {split_name}",
@@ -365,11 +369,104 @@ def mfma_summary(args) -> str:
         f"mfma_util (busy / (active x {SIMDS})): {util:.4f}",
         f"dispatch_duration_us (counter-run timestamps): {dur_us:.1f}",
         f"implied_clock_ghz (active cycles / duration): {active / (dur_us * 1e3):.2f}",
-        f"bf16_mfma_flops_per_dispatch (MOPS x 512): {mfma_flops:.4e}",
+        f"bf16_mfma_flops_per_dispatch (MOPS_BF16 x 512): {mfma_flops:.4e}",
+        f"fp8_mfma_flops_per_dispatch ((MOPS_F8 + MOPS_F6F4) x 512): {f8_flops:.4e}",
         f"algorithmic_flops_per_step: {flops:.4e}",
-        f"mfma_flops_over_algorithmic: {mfma_flops / flops:.3f}",
+        f"mfma_flops_over_algorithmic: {(mfma_flops + f8_flops) / flops:.3f}",
+        f"attainable_bf16_tflops_at_this_clock (2.5 PF x clock / 2.4 GHz): "
+        f"{BF16_PEAK_TFLOPS * (active / (dur_us * 1e3)) / 2.4:.0f}",
     ]
     return "\n".join(lines) + "\n"
+
+
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_BUSY_CYCLES "
+                "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_INSTS_VALU")
+
+
+def counter_summary(args) -> str:
+    """Per-dispatch medians of every counter of one rocprofv3 --pmc run for the split kernel (LDS
+    and wait counters: LDS_COUNTERS), with the wait shares: SQ_WAIT_ANY, SQ_WAIT_INST_LDS and
+    SQ_WAVE_CYCLES count in the same units (wave-cycles), so their ratios are the share of wave
+    time spent waiting (on anything / on LDS instruction issue)."""
+    w = load_workload(args.workload)
+    split_name = split_kernel_name(w)
+    is_split = lambda n: (split_name + "(") in n or (split_name + "<") in n
+    rows = _pmc_rows(args.counter_summary)
+    names = sorted({r["Counter_Name"] for r in rows})
+    med = lambda xs: percentiles(xs, (50,))[0]
+    vals = {}
+    for n in names:
+        v = _per_dispatch(rows, n, is_split)
+        if v:
+            vals[n] = med(v)
+    if not vals:
+        raise SystemExit("no split-kernel dispatches in the counter files")
+    lines = [f"# counters of {split_name} on workload {w.name} (rocprofv3 --pmc), median per dispatch",
+             f"kernel: {split_name}", f"workload: {w.name}", f"source_sha256: {source_sha256()}",
+             f"split_dispatches: {len(_per_dispatch(rows, names[0], is_split))}"]
+    lines += [f"{n}: {vals[n]:.6g}" for n in sorted(vals)]
+    if "SQ_WAVE_CYCLES" in vals and vals["SQ_WAVE_CYCLES"] > 0:
+        if "SQ_WAIT_ANY" in vals:
+            lines.append(f"wait_any_over_wave_cycles: {vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.3f}")
+        if "SQ_WAIT_INST_LDS" in vals:
+            lines.append(f"wait_inst_lds_over_wave_cycles: {vals['SQ_WAIT_INST_LDS'] / vals['SQ_WAVE_CYCLES']:.3f}")
+    return "\n".join(lines) + "\n"
+
+
+def trace_summary(args) -> str:
+    """kernels_<workload>.txt: rocprofv3 --kernel-trace --stats of a bench run (its
+    *kernel_stats.csv, durations in ns), the split kernel's average beside the HIP-event figure
+    of the same run, and that run's bench line (the JSON file it printed)."""
+    import csv
+    import glob
+    d, jpath = args.trace_summary
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {d}")
+    with open(files[0]) as f:
+        text = f.read().strip()
+    with open(jpath) as f:
+        line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
+    res = json.loads(line)
+    w = load_workload(args.workload)
+    name = split_kernel_name(w)
+    split_avg = None
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if (name + "(") in r["Name"] or (name + "<") in r["Name"]:
+                split_avg = float(r["AverageNs"]) / 1e3
+                calls = int(r["Calls"])
+    # the timed steps are the last `steps` dispatches (the warmup ones run before the clock settles)
+    timed_avg = None
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        with open(traces[0]) as f:
+            rows = [r for r in csv.DictReader(f) if (name + "(") in r["Kernel_Name"] or (name + "<") in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-res["steps"]:]]
+        if durs:
+            timed_avg = sum(durs) / len(durs)
+    out = [f"# rocprofv3 kernel-trace statistics, workload {w.name} ({res['steps']} timed + {res['warmup']} warmup steps)",
+           "# command (from the repository root on the GPU host):",
+           f"#   cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 "
+           f"<repo>/bench.py --workload {w.name} --steps {res['steps']} --warmup {res['warmup']} --no-cpu-baseline > <json>",
+           f"#   python3 bench.py --trace-summary <dir> <json> --workload {w.name}",
+           "# columns as rocprofv3 writes them to its kernel_stats.csv (durations in ns)",
+           text, ""]
+    if split_avg is not None:
+        out.append(f"split kernel ({name}) average (rocprofv3 stats, all {calls} calls): {split_avg:.2f} us")
+    if timed_avg is not None:
+        out.append(f"split kernel average over the {res['steps']} timed calls (rocprofv3 kernel trace): {timed_avg:.2f} us")
+    out.append(f"split kernel average (bench.py HIP events, the same {res['steps']} timed calls): "
+               f"{res['split_kernel_ms'] * 1e3:.2f} us")
+    out.append(f"bench line of the profiled run: ms_per_step {res['ms_per_step']}, value {res['value']} {res['unit']}, "
+               f"roofline {json.dumps(res['roofline'])}")
+    if timed_avg is not None:
+        byts, flops, _ = algorithmic_work(w)
+        rf = roofline(byts, flops, timed_avg * 1e-3)
+        out.append(f"roofline from the rocprofv3 timed-call average: {rf['achieved']} {rf['unit']} = {rf['frac']:.4f} "
+                   f"of {rf['peak']} (bench line: {res['roofline']['frac']})")
+    return "\n".join(out) + "\n"
 
 
 def split_kernel_name(w) -> str:
@@ -557,15 +654,27 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench made with --calibrate-copy-mb, and print the traffic summary")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("DIR", "JSON"),
+                    help="no GPU run: summarise one rocprofv3 --kernel-trace --stats run of this bench (DIR) "
+                         "with the JSON line that run printed")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="no GPU run: per-dispatch medians of the counters of one rocprofv3 --pmc run of this "
+                         "bench (LDS_COUNTERS: LDS use and wait shares)")
     ap.add_argument("--mfma-summary", metavar="DIR",
-                    help="no GPU run: summarise one rocprofv3 --pmc run of this bench with the counters "
-                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+                    help="no GPU run: summarise one rocprofv3 --pmc run of this bench with the counters of "
+                         "MFMA_COUNTERS (busy cycles, bf16 / fp8 / fp6-fp4 MOPs, SQ busy, GUI active)")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(args), end="")
         return
     if args.mfma_summary:
         print(mfma_summary(args), end="")
+        return
+    if args.trace_summary:
+        print(trace_summary(args), end="")
+        return
+    if args.counter_summary:
+        print(counter_summary(args), end="")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
