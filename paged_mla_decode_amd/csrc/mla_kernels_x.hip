@@ -737,8 +737,6 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
   }
   const int tid = ln.tid, wave = ln.wave, r16 = ln.r16, q4 = ln.q4;
   const int st = static_cast<int>(p.kv_st);
-  const uint32_t ld_off = x_load_off(ln.lane, st);
-  const uint32_t scale_off = static_cast<uint32_t>((ln.lane & 31) * st + 512 + 4 * (ln.lane >> 5));
 
   const int per_xcd = gridDim.x / 8;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -752,12 +750,20 @@ __global__ void __launch_bounds__(kWThreads) splitkv_x1_kernel(DecodeParams p) {
   if (!read_range(p, part, r)) return;
 
   if (tid < 2) reinterpret_cast<int*>(lds + X::kFlag)[tid] = -1;
-  // issue the loads of one unit into a ring slot
+  // issue the loads of one unit into a ring slot. The per-lane source offsets are computed
+  // here from an opaque copy of the lane index, not held across the unit loop: held, they
+  // were spilled, and the reload before the scale loads waited for every load in flight
+  // (the unit's own code loads included), which made two waves late at every barrier.
   auto issue = [&](const uint8_t* src, int valid, uint8_t* dst) {
-    if constexpr (kFp8)
+    int lane = ln.lane;
+    asm volatile("" : "+v"(lane));
+    const uint32_t ld_off = x_load_off(lane, st);
+    if constexpr (kFp8) {
+      const uint32_t scale_off = static_cast<uint32_t>((lane & 31) * st + 512 + 4 * (lane >> 5));
       f8_issue(src, valid, dst, wave, ld_off, scale_off, st);
-    else if (wave < kLoadWaves)
+    } else if (wave < kLoadWaves) {
       x1_issue(src, valid, dst, wave, ld_off, st);
+    }
   };
 
   // This lane's S-phase row (row 16 wave + r16 of the tile) and its query token and head. They
