@@ -51,7 +51,11 @@ def test_committed_counter_summaries_parse():
                     "fetch_scale", "write_scale"):
             assert key in kv, f"{os.path.basename(f)} lacks {key}"
         ratio = int(kv["hbm_bytes_per_launch"]) / int(kv["algorithmic_bytes_per_step"])
-        assert 0.9 < ratio < 3.0, f"{os.path.basename(f)}: traffic / algorithmic bytes = {ratio:.3f}"
+        # sparse prefill: the algorithmic bytes count each listed kv row once, but every query token
+        # gathers its own topk rows (2048 of 8192 for each of 4096 tokens), and the 9.4 MB kv array
+        # does not stay in one XCD's 4 MB L2, so the L2-miss counters see up to s_q * topk rows
+        limit = 10.0 if kv["workload"] == "sparse_prefill" else 3.0
+        assert 0.9 < ratio < limit, f"{os.path.basename(f)}: traffic / algorithmic bytes = {ratio:.3f}"
         got = bench.stored_traffic(kv["kernel"], kv["workload"])
         assert got is None or got == int(kv["hbm_bytes_per_launch"])
 
