@@ -635,42 +635,53 @@ struct SparseTok {
   bool bad = false;          // the unit holds an invalid entry (uniform)
 };
 
-// Step A: lane j < 32 loads entry j of unit u (none past topk or past the range).
+// The three steps keep their loads unconditional and apply each lane's validity one step
+// later: a load under a lane condition is merged with its default value right after it is
+// issued, and the wait for that value (vmcnt(0)) also waits for every unit load in flight.
+
+// Step A: lane j < 32 loads entry j of unit u (lanes past the list, or past topk, read entry
+// 0 of the list; step B drops them). Nothing past the range.
 __device__ __forceinline__ int sparse_load_index(const DecodeParams& p, const Range& r, const XUnit& u, int kvh,
                                                  int lane) {
+  if (u.b > r.end_b) return -1;
   const int j = u.pi * kPage + u.hf * kXHalf + lane;
-  if (u.b > r.end_b || lane >= kXHalf || j >= p.topk) return -1;
-  const int br = u.b / p.sq_real, s = u.b - br * p.sq_real;
-  return p.indices[br * p.idx_sb + s * p.idx_ss + kvh * p.idx_sh + j];
+  const bool in_list = lane < kXHalf && j < p.topk;
+  const int b = __builtin_amdgcn_readfirstlane(u.b);
+  const int br = b / p.sq_real, s = b - br * p.sq_real;
+  return p.indices[br * p.idx_sb + s * p.idx_ss + kvh * p.idx_sh + (in_list ? j : 0)];
 }
 
-// Step B: validate the (landed) index, drop it unless attended, load its block-table entry.
-__device__ __forceinline__ SparseTok sparse_load_page(const DecodeParams& p, const Range& r, const XUnit& u, int idx,
+// Step B: validate the (landed) index, drop it unless attended, load its block-table entry
+// (lanes that do not attend read entry 0 of the row; step C drops them).
+__device__ __forceinline__ SparseTok sparse_load_page(const DecodeParams& p, const Range& r, const XUnit& u, int raw,
                                                       int lane) {
   SparseTok k;
   if (u.b > r.end_b) return k;
-  const int br = u.b / p.sq_real, s = u.b - br * p.sq_real;
+  const int b = __builtin_amdgcn_readfirstlane(u.b);
+  const int br = b / p.sq_real, s = b - br * p.sq_real;
   const int L = real_len(p, br);
   const int max_len = p.max_blocks * kPage;
-  const bool in_list = lane < kXHalf;
+  const int j = u.pi * kPage + u.hf * kXHalf + lane;
+  const bool in_list = lane < kXHalf && j < p.topk;
+  const int idx = in_list ? raw : -1;
   const bool valid = idx == -1 || (idx >= 0 && idx < L && idx < max_len);
   const bool attend = in_list && idx >= 0 && valid && (!p.real_causal || idx <= L - p.sq_real + s);
   k.bad = __builtin_amdgcn_ballot_w64(in_list && !valid) != 0;
   k.t = attend ? idx : -1;
-  if (p.kv_rows > 0)                       // contiguous rows: page idx / 64 of the row array
-    k.page = attend ? (idx >> 6) : -1;
-  else
-    k.page = attend ? p.block_table[static_cast<int64_t>(br) * p.bt_stride + (idx >> 6)] : -1;
+  if (p.kv_rows == 0 && p.max_blocks > 0)     // (contiguous rows: the page is taken in step C)
+    k.page = p.block_table[static_cast<int64_t>(br) * p.bt_stride + (attend ? (idx >> 6) : 0)];
   return k;
 }
 
 // Step C: the byte offset of the row of the (landed) page entry, the attend mask, validity.
 __device__ __forceinline__ uint32_t sparse_offset(const DecodeParams& p, SparseTok& k, uint32_t& mask) {
-  const bool page_ok = k.page >= 0 && k.page < p.num_pages;
   const bool attend = k.t >= 0;
+  // contiguous rows (kv_rows > 0): page t / 64 of the row array; else the block-table entry
+  const int page = attend ? (p.kv_rows > 0 ? (k.t >> 6) : k.page) : -1;
+  const bool page_ok = page >= 0 && page < p.num_pages;
   k.bad = k.bad || (__builtin_amdgcn_ballot_w64(attend && !page_ok) != 0);
   mask = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(attend && page_ok));
-  return (attend && page_ok) ? static_cast<uint32_t>(static_cast<int64_t>(k.page) * p.kv_sp + (k.t & 63) * p.kv_st)
+  return (attend && page_ok) ? static_cast<uint32_t>(static_cast<int64_t>(page) * p.kv_sp + (k.t & 63) * p.kv_st)
                              : kNoToken;
 }
 
@@ -683,6 +694,7 @@ __device__ __forceinline__ void sparse_issue(const uint8_t* kv_head, int64_t poo
                                              int wave, int lane) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kv_head), 0,
                                                                         static_cast<int>(pool_bytes), kRawBufferWord3);
+  asm volatile("" : "+v"(lane));             // lane-derived offsets computed here, not held (and spilled)
   const uint32_t chunk = 16 * ((lane & 7) ^ (lane >> 3));
   if constexpr (FMT == kFmtFp8) {
     using X = F8Layout;
