@@ -894,6 +894,132 @@ __global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams
 }
 
 
+// Sequences of at most 8 pieces: one workgroup per (sequence, 16 rows, KV head, QPL
+// 128-dim quarters); each lane merges its row's 8 dims in each of the QPL quarters, so
+// the loads of QPL quarters of PG pieces are in flight together (the merge is latency
+// bound: fewer, fuller waves). The running max and sum are shared by the quarters.
+template <bool F16, int QPL>
+__global__ void __launch_bounds__(kThreads) combine_q_kernel(DecodeParams p) {
+  constexpr int PG = QPL >= 4 ? 2 : 4;           // pieces whose loads are in flight together
+  constexpr int kGroups = kDv / (kCombDims * QPL);
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int row = blockIdx.y * 16 + tid / 16;
+  const int l16 = tid & 15;
+  const int kvh = blockIdx.z / kGroups;
+  const int q0 = (blockIdx.z % kGroups) * QPL;
+  const int slot0 = ld_meta(p.num_splits + b);
+  const int n = ld_meta(p.num_splits + b + 1) - slot0;
+  if (n == 1 || row >= p.rows) return;          // one piece: written by the split kernel
+  const int s_idx = row / p.group;
+  const int head = kvh * p.group + row % p.group;
+  const int dim0 = q0 * kCombDims + 8 * l16;
+  uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
+  float* lse_out = p.lse + lse_index(p, b, head, s_idx);
+  if (n <= 0 || slot0 < 0 || slot0 + n > p.max_slots) {
+#pragma unroll
+    for (int qq = 0; qq < QPL; ++qq)
+      *reinterpret_cast<u32x4*>(orow + qq * kCombDims) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    if (l16 == 0 && q0 == 0) *lse_out = __builtin_nanf("");
+    return;
+  }
+  const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;
+  const int64_t row0 = static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
+  const float* lse_in = p.part_lse + row0;
+  float m = kNegInf, l = 0.f;
+  f32x4 a0[QPL], a1[QPL];
+#pragma unroll
+  for (int qq = 0; qq < QPL; ++qq) a0[qq] = a1[qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < n; i0 += PG) {
+    float lse[PG];
+    f32x4 x0[PG][QPL], x1[PG][QPL];
+    if constexpr (F16) {
+      const uint16_t* o_in = p.part_o16 + row0 * kDv + dim0;
+      const float* sc_in = p.part_scale + row0 * kPartBlocks + (dim0 >> 6);
+      float sc[PG][QPL];
+      u32x4 h[PG][QPL];
+      // all loads first (converting right after each load would wait for it)
+#pragma unroll
+      for (int j = 0; j < PG; ++j) {
+        const int i = i0 + j;
+        lse[j] = (i < n) ? lse_in[i * stride] : kNegInf;
+#pragma unroll
+        for (int qq = 0; qq < QPL; ++qq) {
+          h[j][qq] = (i < n) ? *reinterpret_cast<const u32x4*>(o_in + i * stride * kDv + qq * kCombDims)
+                             : u32x4{0u, 0u, 0u, 0u};
+          sc[j][qq] = (i < n) ? sc_in[i * stride * kPartBlocks + qq * (kCombDims / 64)] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < PG; ++j)
+#pragma unroll
+        for (int qq = 0; qq < QPL; ++qq) {
+          const u32x4 w = h[j][qq];
+          x0[j][qq] = f32x4{f16_lo(w[0]), f16_hi(w[0]), f16_lo(w[1]), f16_hi(w[1])} * sc[j][qq];
+          x1[j][qq] = f32x4{f16_lo(w[2]), f16_hi(w[2]), f16_lo(w[3]), f16_hi(w[3])} * sc[j][qq];
+        }
+    } else {
+      const float* o_in = p.part_o32 + row0 * kDv + dim0;
+#pragma unroll
+      for (int j = 0; j < PG; ++j) {
+        const int i = i0 + j;
+        lse[j] = (i < n) ? lse_in[i * stride] : kNegInf;
+#pragma unroll
+        for (int qq = 0; qq < QPL; ++qq) {
+          x0[j][qq] = (i < n) ? *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + qq * kCombDims)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+          x1[j][qq] = (i < n) ? *reinterpret_cast<const f32x4*>(o_in + i * stride * kDv + qq * kCombDims + 4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    // the online merge of merge_group, with the max and sum shared by the quarters
+    const int nv = min(n - i0, PG);
+    float mc = kNegInf;
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < PG; ++j)
+      if (j < nv) {
+        mc = fmaxf(mc, lse[j]);
+        nan |= lse[j] != lse[j];
+      }
+    if (nan) l = __builtin_nanf("");
+    const float mn = fmaxf(m, mc);
+    if (mn == kNegInf) continue;                  // nothing allowed so far
+    const float scl = (m == kNegInf) ? 0.f : __expf(m - mn);
+    l *= scl;
+#pragma unroll
+    for (int qq = 0; qq < QPL; ++qq) {
+      a0[qq] *= scl;
+      a1[qq] *= scl;
+    }
+#pragma unroll
+    for (int j = 0; j < PG; ++j)
+      if (j < nv) {
+        const float w = __expf(lse[j] - mn);
+        l += w;
+        if (w != 0.f) {                           // an empty piece has w = 0 and O = 0
+#pragma unroll
+          for (int qq = 0; qq < QPL; ++qq) {
+            a0[qq] += w * x0[j][qq];
+            a1[qq] += w * x1[j][qq];
+          }
+        }
+      }
+    m = mn;
+  }
+  const float inv = merge_inv(l);
+#pragma unroll
+  for (int qq = 0; qq < QPL; ++qq)
+    *reinterpret_cast<u32x4*>(orow + qq * kCombDims) = pack_bf16x8(a0[qq] * inv, a1[qq] * inv);
+  if (l16 == 0 && q0 == 0) {
+    MergeState st;
+    st.m = m;
+    st.l = l;
+    *lse_out = merge_lse(st);
+  }
+}
+
 template <int RB, int TG>
 hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
                         hipEvent_t ev_stop) {
@@ -960,10 +1086,14 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
     // sequences cut into many pieces (the host metadata's largest piece count): 4 piece groups
     const bool many = p.max_splits > 2 * kCombGroup;
+    // fp16 partials of at most 8 pieces: two quarters per lane (mtp's combine 20.6 -> 16.8 us,
+    // compute_heavy's 10.4 -> 9.6; four quarters per lane time the same, the fp32 partials of
+    // the narrow tiles gain nothing)
+    const dim3 cgrid_q2(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / (2 * kCombDims)));
     if (plan.wide && many)
       hipLaunchKernelGGL((combine_rows_kernel<true, 4>), cgrid, dim3(4 * kThreads), 0, stream, p);
     else if (plan.wide)
-      hipLaunchKernelGGL((combine_rows_kernel<true, 1>), cgrid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((combine_q_kernel<true, 2>), cgrid_q2, dim3(kThreads), 0, stream, p);
     else if (many)
       hipLaunchKernelGGL((combine_rows_kernel<false, 4>), cgrid, dim3(4 * kThreads), 0, stream, p);
     else
