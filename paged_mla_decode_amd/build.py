@@ -18,11 +18,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libmla.so")
 SOURCES = ["mla_api.cpp", "scheduler.cpp", "scheduler_device.hip", "mla_kernels.hip", "mla_kernels_x.hip"]
-# Per-file flags. The 128-row kernel keeps 256 fp32 accumulators per lane next
-# to its Q operands; selecting the VGPR form of MFMA lets the register
-# allocator place accumulators in either register file, which removes the
-# spills the all-AGPR form causes there.
-FILE_FLAGS = {"mla_kernels_x.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file flags. The kernels keep their fp32 accumulators next to their MFMA
+# operands (the 128-row kernel 128 per lane beside its Q operands); selecting
+# the VGPR form of MFMA lets the register allocator place accumulators in
+# either register file, which removes the spills the all-AGPR form causes (the
+# FP8 variants of the 64-row kernel: 46 and 18 spilled registers without it).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+FILE_FLAGS = {"mla_kernels_x.hip": _VGPR_FORM, "mla_kernels.hip": _VGPR_FORM}
 ARCH = "gfx950"
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
