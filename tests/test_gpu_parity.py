@@ -140,6 +140,23 @@ def test_full_size_workloads(name):
         compare(w, O, LSE, O_ref, LSE_ref, batches=[long_b], label="full ragged, the 32768-token sequence")
 
 
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (16, 2), (32, 1), (64, 1)])
+def test_fp8_narrow_tiles_many_pieces(h_q, s_q):
+    """FP8 records with up to 64 query rows per KV head (the 64-row kernels' FP8 variants, e.g.
+    16 heads per GPU) at a size where every sequence spans many pages and, in the default launch
+    configuration, several pieces (one with more than 16), so the fp32 partials and the
+    many-piece combine run; every sequence against the oracle, and a bitwise rerun."""
+    rng = np.random.default_rng(71 + h_q + s_q)
+    lens = [int(x) for x in rng.integers(600, 3000, size=23)] + [12000]
+    w = make_workload(name=f"fp8_narrow_h{h_q}_s{s_q}", batch=24, s_q=s_q, h_q=h_q, seqlens=lens,
+                      causal=s_q > 1, kv_format="fp8", seed=72 + h_q)
+    O, LSE = run_gpu(w)
+    O2, LSE2 = run_gpu(w)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2), "run-to-run results differ"
+    O_ref, LSE_ref = oracle.mla_decode_workload(w)
+    compare(w, O, LSE, O_ref, LSE_ref, label=f"fp8 h_q={h_q} s_q={s_q}, 24 sequences")
+
+
 def test_full_compute_heavy_causal_flag_is_noop():
     w = full("compute_heavy")
     O1, L1 = run_gpu(w, causal=False)
