@@ -32,6 +32,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <mutex>
 #include <unordered_map>
@@ -770,50 +772,39 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const f32x4& a0, const f32x4& a1) {
 
 constexpr int kCombDims = 128;                  // dims per workgroup
 constexpr int kCombGroup = 4;                   // pieces whose loads are in flight together
+constexpr int kFewPieces = 2 * kCombGroup;      // one round of loads per lane (two groups of 4)
 
-// One workgroup per (sequence, 16 rows, KV head, 128-dim quarter); 16 lanes
-// per row, 8 dims per lane, the pieces in groups of kCombGroup with all their
-// loads in flight at once. (A two-pass kernel with 16 pieces per workgroup in
-// parallel, for sequences cut into many pieces, was slower on the ragged
-// workload: 24 us against 19 us.)
-// G piece groups of kThreads threads each: group g merges pieces 4 g .. 4 g + 3,
-// 4 (g + G) .., and group 0 merges the G states through LDS at the end (G > 1
-// for sequences cut into many pieces: fewer rounds of dependent loads).
-template <bool F16, int G>
-__global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams p) {
-  const int tid = threadIdx.x % kThreads;
-  const int grp = threadIdx.x / kThreads;
-  const int b = blockIdx.x;
-  const int row = blockIdx.y * 16 + tid / 16;
+// One workgroup's share of a sequence cut into 2..n_max pieces: 16 rows of one KV head, one
+// 128-dim quarter; 16 lanes per row, 8 dims per lane, the pieces in groups of kCombGroup with
+// all their loads in flight at once. Sequences of one piece (written by the split kernel) and
+// of more than n_max pieces (left to other workgroups) are skipped.
+template <bool F16>
+__device__ __forceinline__ void combine_rows_task(const DecodeParams& p, int b, int rt, int z, int n_max) {
+  const int tid = threadIdx.x;
+  const int row = rt * 16 + tid / 16;
   const int l16 = tid & 15;
-  const int kvh = blockIdx.z / (kDv / kCombDims);
-  const int quarter = blockIdx.z % (kDv / kCombDims);
+  const int kvh = z / (kDv / kCombDims);
+  const int quarter = z % (kDv / kCombDims);
   const int slot0 = ld_meta(p.num_splits + b);
   const int n = ld_meta(p.num_splits + b + 1) - slot0;
-  if (n == 1) return;                            // the whole workgroup: one piece is written by the split kernel
-  if constexpr (G == 1) {
-    if (row >= p.rows) return;
-  }
-  const bool row_ok = row < p.rows;              // G > 1: every thread reaches the barrier below
-  const int s_idx = row_ok ? row / p.group : 0;
-  const int head = kvh * p.group + (row_ok ? row % p.group : 0);
+  if (n == 1 || n > n_max || row >= p.rows) return;
+  const int s_idx = row / p.group;
+  const int head = kvh * p.group + row % p.group;
   const int dim0 = quarter * kCombDims + 8 * l16;
   uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
   float* lse_out = p.lse + lse_index(p, b, head, s_idx);
   // no piece (num_splits inconsistent with the ranges) or slots outside the workspace: NaN, never
-  // a read of partials nobody wrote (uniform over the workgroup)
+  // a read of partials nobody wrote
   if (n <= 0 || slot0 < 0 || slot0 + n > p.max_slots) {
-    if (row_ok && grp == 0) {
-      *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-      if (l16 == 0 && quarter == 0) *lse_out = __builtin_nanf("");
-    }
+    *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    if (l16 == 0 && quarter == 0) *lse_out = __builtin_nanf("");
     return;
   }
   const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;
   const float* lse_in = p.part_lse + static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   const int64_t row0 = static_cast<int64_t>(slot0) * stride + static_cast<int64_t>(kvh) * p.rows + row;
   MergeState st;
-  for (int i0 = grp * kCombGroup; row_ok && i0 < n; i0 += G * kCombGroup) {
+  for (int i0 = 0; i0 < n; i0 += kCombGroup) {
     float lse[kCombGroup];
     f32x4 x0[kCombGroup], x1[kCombGroup];
     if constexpr (F16) {
@@ -858,39 +849,15 @@ __global__ void __launch_bounds__(kThreads * G) combine_rows_kernel(DecodeParams
     }
     merge_group<kCombGroup>(st, lse, x0, x1, min(n - i0, kCombGroup));
   }
-  if constexpr (G > 1) {
-    __shared__ float xs[G - 1][10][kThreads];
-    if (grp > 0) {
-      float* x = &xs[grp - 1][0][tid];
-      x[0] = st.m;
-      x[kThreads] = st.l;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[(2 + i) * kThreads] = st.a0[i];
-        x[(6 + i) * kThreads] = st.a1[i];
-      }
-    }
-    __syncthreads();
-    if (grp > 0 || !row_ok) return;
-#pragma unroll
-    for (int g = 0; g < G - 1; ++g) {
-      const float* x = &xs[g][0][tid];
-      const float m2 = x[0], l2 = x[kThreads];
-      const float mn = fmaxf(st.m, m2);
-      const float s1 = (st.m == kNegInf) ? 0.f : __expf(st.m - mn);
-      const float s2 = (m2 == kNegInf) ? 0.f : __expf(m2 - mn);
-      st.l = st.l * s1 + l2 * s2;                 // NaN in either stays NaN
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st.a0[i] = st.a0[i] * s1 + x[(2 + i) * kThreads] * s2;
-        st.a1[i] = st.a1[i] * s1 + x[(6 + i) * kThreads] * s2;
-      }
-      st.m = mn;
-    }
-  }
   const float inv = merge_inv(st.l);
   *reinterpret_cast<u32x4*>(orow) = pack_bf16x8(st.a0 * inv, st.a1 * inv);
   if (l16 == 0 && quarter == 0) *lse_out = merge_lse(st);
+}
+
+// One workgroup per (sequence, 16 rows, KV head, 128-dim quarter).
+template <bool F16>
+__global__ void __launch_bounds__(kThreads) combine_rows_kernel(DecodeParams p) {
+  combine_rows_task<F16>(p, blockIdx.x, blockIdx.y, blockIdx.z, INT_MAX);
 }
 
 
@@ -1020,6 +987,199 @@ __global__ void __launch_bounds__(kThreads) combine_q_kernel(DecodeParams p) {
   }
 }
 
+// Merge a second state (m2, l2, b0, b1) into st: the online-softmax merge of two partial
+// results; two states that allowed nothing stay empty, NaN in either stays NaN.
+__device__ __forceinline__ void merge_states(MergeState& st, float m2, float l2, const f32x4& b0, const f32x4& b1) {
+  const float mn = fmaxf(st.m, m2);
+  const float s1 = (st.m == kNegInf) ? 0.f : __expf(st.m - mn);
+  const float s2 = (m2 == kNegInf) ? 0.f : __expf(m2 - mn);
+  st.l = st.l * s1 + l2 * s2;
+  st.a0 = st.a0 * s1 + b0 * s2;
+  st.a1 = st.a1 * s1 + b1 * s2;
+  st.m = mn;
+}
+
+// Metadata in which some sequence is cut into more than kFewPieces pieces. The last
+// batch x row tiles x KV heads x 4 workgroups are combine_rows_task's (sequences of up to
+// kFewPieces pieces); the first ones, the helpers (dispatched first: theirs is the longest
+// chain of loads), find the sequences of more pieces themselves (their count is not known
+// on the host) and share their tasks: (listed sequence, 2 rows, KV head, 32-dim slice).
+// Small tasks spread a long sequence's partials over many workgroups (a workgroup's time
+// grows with the cache lines it requests, and one row's 32 fp32 dims are one line). In a
+// task 32 piece groups of 8 lanes (4 lanes of 8 dims per row) take every 32nd piece, 2
+// pieces each with their loads in flight together (64 pieces per round of loads); the 8
+// groups of a wave merge by lane exchange, the 4 waves through LDS.
+constexpr int kListRows = 2;
+constexpr int kListDims = 32;
+constexpr int kListLanes = kListRows * (kListDims / 8);
+constexpr int kListGroups = kThreads / kListLanes;
+constexpr int kListInFlight = 2;
+constexpr int kListWgs = 256;                  // helpers (at most)
+
+template <bool F16>
+__global__ void __launch_bounds__(kThreads) combine_many_kernel(DecodeParams p) {
+  const int rt_n = (p.rows + 15) / 16;
+  const int zq = p.h_kv * (kDv / kCombDims);
+  const int nb = p.batch * rt_n * zq;
+  const int helpers = static_cast<int>(gridDim.x) - nb;
+  if (static_cast<int>(blockIdx.x) >= helpers) {
+    const int w = blockIdx.x - helpers;
+    const int r = w / p.batch;
+    combine_rows_task<F16>(p, w - r * p.batch, r % rt_n, r / rt_n, kFewPieces);
+    return;
+  }
+  __shared__ int list_b[kThreads], list_slot[kThreads], list_n[kThreads];
+  __shared__ int wave_cnt[kThreads / 64];
+  __shared__ float xs[kThreads / 64 - 1][10][kListLanes];
+  const int tid = threadIdx.x;
+  const int grp = tid / kListLanes;
+  const int lane = tid % kListLanes;
+  const int slices = kDv / kListDims;
+  const int per_seq = (p.rows + kListRows - 1) / kListRows * p.h_kv * slices;   // tasks of one listed sequence
+  const int64_t stride = static_cast<int64_t>(p.h_kv) * p.rows;
+  int base = 0;                                  // first task of the current chunk
+  int t = blockIdx.x;                            // this helper's next task
+  for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
+    // the chunk's sequences of more than kFewPieces pieces, in order
+    const int b = c0 + tid;
+    int slot0 = 0, n = 1;
+    if (b < p.batch) {
+      slot0 = p.num_splits[b];
+      n = p.num_splits[b + 1] - slot0;
+    }
+    const bool listed = n > kFewPieces;
+    const uint64_t ball = __ballot(listed);
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) wave_cnt[w] = __popcll(ball);
+    __syncthreads();
+    int off = 0, cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+      off += (i < w) ? wave_cnt[i] : 0;
+      cnt += wave_cnt[i];
+    }
+    if (listed) {
+      const int pos = off + __popcll(ball & ((1ull << (tid & 63)) - 1ull));
+      list_b[pos] = b;
+      list_slot[pos] = slot0;
+      list_n[pos] = n;
+    }
+    __syncthreads();
+    const int end = base + cnt * per_seq;
+    for (; t < end; t += helpers) {              // uniform over the workgroup
+      const int tl = t - base;
+      const int li = tl / per_seq;
+      int r = tl - li * per_seq;
+      const int slice = r % slices;
+      r /= slices;
+      const int kvh = r % p.h_kv;
+      const int rt = r / p.h_kv;
+      const int sb = list_b[li];
+      const int s0 = list_slot[li];
+      const int sn = list_n[li];
+      const int row = rt * kListRows + lane / (kListDims / 8);
+      const bool row_ok = row < p.rows;
+      const int rowc = row_ok ? row : p.rows - 1;  // loads of rows past the end stay inside the workspace
+      const int s_idx = rowc / p.group;
+      const int head = kvh * p.group + rowc % p.group;
+      const int dim0 = slice * kListDims + 8 * (lane % (kListDims / 8));
+      uint16_t* orow = p.o + ((static_cast<int64_t>(sb) * p.s_q + s_idx) * p.h_q + head) * kDv + dim0;
+      float* lse_out = p.lse + lse_index(p, sb, head, s_idx);
+      const bool lse_lane = lane % (kListDims / 8) == 0 && slice == 0;
+      if (s0 < 0 || s0 + sn > p.max_slots) {     // slots outside the workspace: NaN
+        if (row_ok && grp == 0) {
+          *reinterpret_cast<u32x4*>(orow) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+          if (lse_lane) *lse_out = __builtin_nanf("");
+        }
+        continue;
+      }
+      const int64_t row0 = static_cast<int64_t>(s0) * stride + static_cast<int64_t>(kvh) * p.rows + rowc;
+      MergeState st;
+      for (int i0 = grp; i0 < sn; i0 += kListGroups * kListInFlight) {
+        float lse[kListInFlight];
+        f32x4 x0[kListInFlight], x1[kListInFlight];
+        // every load issued before any is used: indices past the last piece repeat it
+        if constexpr (F16) {
+          u32x4 h[kListInFlight];
+          float sc[kListInFlight];
+#pragma unroll
+          for (int j = 0; j < kListInFlight; ++j) {
+            const int64_t ri = row0 + min(i0 + kListGroups * j, sn - 1) * stride;
+            lse[j] = p.part_lse[ri];
+            h[j] = *reinterpret_cast<const u32x4*>(p.part_o16 + ri * kDv + dim0);
+            sc[j] = p.part_scale[ri * kPartBlocks + (dim0 >> 6)];
+          }
+          // the values are taken here, after the last load was issued: otherwise the compiler
+          // moves the O loads behind the LSE test of the merge (two rounds of loads)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int j = 0; j < kListInFlight; ++j) asm volatile("" : "+v"(lse[j]), "+v"(h[j]), "+v"(sc[j]));
+#pragma unroll
+          for (int j = 0; j < kListInFlight; ++j) {
+            x0[j] = f32x4{f16_lo(h[j][0]), f16_hi(h[j][0]), f16_lo(h[j][1]), f16_hi(h[j][1])} * sc[j];
+            x1[j] = f32x4{f16_lo(h[j][2]), f16_hi(h[j][2]), f16_lo(h[j][3]), f16_hi(h[j][3])} * sc[j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < kListInFlight; ++j) {
+            const int64_t ri = row0 + min(i0 + kListGroups * j, sn - 1) * stride;
+            lse[j] = p.part_lse[ri];
+            x0[j] = *reinterpret_cast<const f32x4*>(p.part_o32 + ri * kDv + dim0);
+            x1[j] = *reinterpret_cast<const f32x4*>(p.part_o32 + ri * kDv + dim0 + 4);
+          }
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int j = 0; j < kListInFlight; ++j) asm volatile("" : "+v"(lse[j]), "+v"(x0[j]), "+v"(x1[j]));
+        }
+        merge_group<kListInFlight>(st, lse, x0, x1, min(kListInFlight, (sn - i0 + kListGroups - 1) / kListGroups));
+      }
+      // the wave's groups (lanes kListLanes apart), then the 4 waves
+#pragma unroll
+      for (int sh = kListLanes; sh < 64; sh *= 2) {
+        f32x4 b0, b1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b0[i] = __shfl_xor(st.a0[i], sh);
+          b1[i] = __shfl_xor(st.a1[i], sh);
+        }
+        merge_states(st, __shfl_xor(st.m, sh), __shfl_xor(st.l, sh), b0, b1);
+      }
+      if (w > 0 && (tid & 63) < kListLanes) {
+        float* x = &xs[w - 1][0][lane];
+        x[0] = st.m;
+        x[kListLanes] = st.l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[(2 + i) * kListLanes] = st.a0[i];
+          x[(6 + i) * kListLanes] = st.a1[i];
+        }
+      }
+      __syncthreads();
+      if (tid < kListLanes) {
+#pragma unroll
+        for (int g = 0; g < kThreads / 64 - 1; ++g) {
+          const float* x = &xs[g][0][lane];
+          f32x4 b0, b1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            b0[i] = x[(2 + i) * kListLanes];
+            b1[i] = x[(6 + i) * kListLanes];
+          }
+          merge_states(st, x[0], x[kListLanes], b0, b1);
+        }
+        if (row_ok) {
+          const float inv = merge_inv(st.l);
+          *reinterpret_cast<u32x4*>(orow) = pack_bf16x8(st.a0 * inv, st.a1 * inv);
+          if (lse_lane) *lse_out = merge_lse(st);
+        }
+      }
+      __syncthreads();                           // xs is written again by the next task
+    }
+    base = end;
+    __syncthreads();                             // the lists are written again by the next chunk
+  }
+}
+
 template <int RB, int TG>
 hipError_t launch_split(const DecodeParams& p, int kv_format, int grid, hipStream_t stream, hipEvent_t ev_start,
                         hipEvent_t ev_stop) {
@@ -1084,20 +1244,26 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   if (err != hipSuccess) return err;
   {
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
-    // sequences cut into many pieces (the host metadata's largest piece count): 4 piece groups
-    const bool many = p.max_splits > 2 * kCombGroup;
+    // some sequence cut into more than kFewPieces pieces (the host metadata's largest piece
+    // count): helper workgroups for those. At most (ranges - 1) / kFewPieces sequences have
+    // that many pieces (each piece past a sequence's first starts a range).
+    const bool many = p.max_splits > kFewPieces;
+    const int64_t per_quarters = static_cast<int64_t>(p.batch) * ((p.rows + 15) / 16) * p.h_kv * (kDv / kCombDims);
+    const int64_t helper_tasks = static_cast<int64_t>(std::max(1, (p.grid_wgs - 1) / kFewPieces)) *
+                                 ((p.rows + kListRows - 1) / kListRows) * p.h_kv * (kDv / kListDims);
+    const dim3 mgrid(static_cast<unsigned>(per_quarters + std::min<int64_t>(helper_tasks, kListWgs)));
     // fp16 partials of at most 8 pieces: two quarters per lane (mtp's combine 20.6 -> 16.8 us,
     // compute_heavy's 10.4 -> 9.6; four quarters per lane time the same, the fp32 partials of
     // the narrow tiles gain nothing)
     const dim3 cgrid_q2(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / (2 * kCombDims)));
     if (plan.wide && many)
-      hipLaunchKernelGGL((combine_rows_kernel<true, 4>), cgrid, dim3(4 * kThreads), 0, stream, p);
+      hipLaunchKernelGGL((combine_many_kernel<true>), mgrid, dim3(kThreads), 0, stream, p);
     else if (plan.wide)
       hipLaunchKernelGGL((combine_q_kernel<true, 2>), cgrid_q2, dim3(kThreads), 0, stream, p);
     else if (many)
-      hipLaunchKernelGGL((combine_rows_kernel<false, 4>), cgrid, dim3(4 * kThreads), 0, stream, p);
+      hipLaunchKernelGGL((combine_many_kernel<false>), mgrid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((combine_rows_kernel<false, 1>), cgrid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((combine_rows_kernel<false>), cgrid, dim3(kThreads), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -157,6 +157,64 @@ def test_fp8_narrow_tiles_many_pieces(h_q, s_q):
     compare(w, O, LSE, O_ref, LSE_ref, label=f"fp8 h_q={h_q} s_q={s_q}, 24 sequences")
 
 
+MANY = [
+    # name, batch, s_q, h_q, h_kv, lengths, causal, fmt, num_parts, pieces of the longest sequence (at least)
+    ("many_rows5", 3, 1, 5, 1, [5000, 300, 2500], False, "bf16", 256, 65),
+    ("many_hkv2", 2, 1, 32, 2, [4500, 900], False, "bf16", 200, 65),
+    ("many_rows128_causal", 3, 2, 64, 1, [5000, 64, 2000], True, "bf16", 300, 65),
+    ("many_fp8_rows16", 2, 1, 16, 1, [6000, 100], False, "fp8", 256, 65),
+    ("many_fp8_rows128", 2, 1, 128, 1, [4100, 700], False, "fp8", 256, 65),
+]
+
+
+def _pieces(w, num_parts):
+    import paged_mla_decode_amd as mla
+    _, splits = mla.mla_get_metadata_host(w.cache_seqlens, w.heads_per_kv, w.h_kv, kv_format=w.kv_format,
+                                          num_parts=num_parts)
+    return np.diff(splits.numpy())
+
+
+@pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
+def test_sequences_of_many_pieces(case):
+    """Sequences cut into more than 8 pieces (merged by the combine's helper workgroups), here
+    more than 64 (two rounds of loads), with row counts that do not fill the helpers' row
+    pairs, two KV heads, fp32 and fp16 partials."""
+    name, B, S, H, Hk, L, causal, fmt, parts, least = case
+    w = make_workload(name=name, batch=B, s_q=S, h_q=H, h_kv=Hk, seqlens=L, causal=causal, kv_format=fmt,
+                      seed=80 + len(name), pool_pages=sum((x + 63) // 64 for x in L) + 5)
+    n = _pieces(w, parts)
+    print(f"[case] {name} num_parts={parts} pieces={n.tolist()}", flush=True)
+    assert n.max() >= least
+    O, LSE = run_gpu(w, num_parts=parts)
+    O2, LSE2 = run_gpu(w, num_parts=parts)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2), "run-to-run results differ"
+    O_ref, LSE_ref = oracle.mla_decode_workload(w)
+    compare(w, O, LSE, O_ref, LSE_ref, label=f"{name}/parts={parts}")
+
+
+def test_more_than_256_sequences_of_many_pieces():
+    """300 sequences of 9-11 pieces each: the combine's helpers list them in two chunks."""
+    rng = np.random.default_rng(81)
+    lens = [int(x) for x in rng.integers(560, 700, size=300)]
+    w = make_workload(name="many_chunks", batch=300, s_q=1, h_q=16, seqlens=lens, seed=82)
+    n = _pieces(w, 4000)
+    print(f"[case] many_chunks: {int((n > 8).sum())} sequences of more than 8 pieces", flush=True)
+    assert (n > 8).sum() > 256
+    O, LSE = run_gpu(w, num_parts=4000)
+    O_ref, LSE_ref = oracle.mla_decode_workload(w)
+    compare(w, O, LSE, O_ref, LSE_ref, label="300 sequences of 9-11 pieces")
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_invalid_page_in_a_sequence_of_many_pieces(h_q):
+    w = make_workload(name="badpage_many", batch=3, s_q=1, h_q=h_q, seqlens=[100, 3000, 50], seed=83)
+    w_ok = make_workload(name="badpage_many", batch=3, s_q=1, h_q=h_q, seqlens=[100, 3000, 50], seed=83)
+    assert _pieces(w, 256)[1] > 8
+    w.block_table[1, 20] = 10_000
+    O, LSE = run_gpu(w, num_parts=256)
+    _compare_except(w_ok, O, LSE, [1], f"a bad page in a sequence of many pieces (h_q={h_q})")
+
+
 def test_full_compute_heavy_causal_flag_is_noop():
     w = full("compute_heavy")
     O1, L1 = run_gpu(w, causal=False)
