@@ -36,6 +36,7 @@
 #include <climits>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 #include <unordered_map>
 
 #include "device_common.h"
@@ -401,6 +402,31 @@ __device__ __forceinline__ void merge_add(const float* red, int sl, int r16, int
   }
 }
 
+// The token-group merge of four waves that hold the same 16 rows (each over its own tokens), as
+// two exchanges through LDS in which all four waves take part: waves w and w ^ 2 swap halves of
+// the 512 dims (wave w keeps half w >> 1), then waves w and w ^ 1 swap quarters of the kept half
+// (wave w keeps quarter w, acc[8w .. 8w + 8), and writes it). Step-1 blocks are 16 rows x 256
+// fp32 (16 KB, one per sending wave), step-2 blocks 16 rows x 128 fp32 (8 KB); 16-byte chunk c of
+// a row sits at chunk c ^ r16 (no bank conflicts between the 16 rows).
+template <int D0, int N>
+__device__ __forceinline__ void red_put(uint32_t base, int r16, int q4, const f32x4 (&acc)[32]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) lds_store16(base + 16 * ((4 * j + q4) ^ r16), acc[D0 + j]);
+}
+template <int D0, int N>
+__device__ __forceinline__ void red_add(uint32_t base, int r16, int q4, f32x4 (&acc)[32]) {
+#pragma unroll
+  for (int g = 0; g < N; g += 8) {
+    uint32_t a[8];
+    bf16x8 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = base + 16 * ((4 * (g + k) + q4) ^ r16);
+    lds_read16_block<8>(a, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[D0 + g + k] += __builtin_bit_cast(f32x4, v[k]);
+  }
+}
+
 template <int RB, int TG, int FMT>
 __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
   static_assert(RB * TG == kWaves, "4 waves per workgroup");
@@ -645,33 +671,55 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
       m_fin = M;
       // Sum the TG accumulators of each row block through LDS, in the slot not
       // receiving a page (bf16) or the converted page (fp8).
-      float* red = reinterpret_cast<float*>(kFp8 ? conv : ring + (slot ^ 1) * kSlotBytes);
+      uint8_t* red = kFp8 ? conv : ring + (slot ^ 1) * kSlotBytes;
       if constexpr (TG == 4) {                 // RB == 1: waves 0..3 hold the same rows
-        if (wave >= 2) merge_put(red, wave - 2, r16, q4, acc);
+        const uint32_t s1 = lds_addr(red) + r16 * 1024, s2 = lds_addr(red) + r16 * 512;
+        if (wave < 2)
+          red_put<16, 16>(s1 + wave * 16384, r16, q4, acc);
+        else
+          red_put<0, 16>(s1 + wave * 16384, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (wave < 2) merge_add(red, wave, r16, q4, acc);
+        if (wave < 2)
+          red_add<0, 16>(s1 + (wave ^ 2) * 16384, r16, q4, acc);
+        else
+          red_add<16, 16>(s1 + (wave ^ 2) * 16384, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (wave == 1) merge_put(red, 0, r16, q4, acc);
+        switch (wave) {
+          case 0: red_put<8, 8>(s2, r16, q4, acc); break;
+          case 1: red_put<0, 8>(s2 + 8192, r16, q4, acc); break;
+          case 2: red_put<24, 8>(s2 + 2 * 8192, r16, q4, acc); break;
+          default: red_put<16, 8>(s2 + 3 * 8192, r16, q4, acc); break;
+        }
         lds_barrier_keep_loads();
-        if (wave == 0) merge_add(red, 0, r16, q4, acc);
+        switch (wave) {
+          case 0: red_add<0, 8>(s2 + 8192, r16, q4, acc); break;
+          case 1: red_add<8, 8>(s2, r16, q4, acc); break;
+          case 2: red_add<16, 8>(s2 + 3 * 8192, r16, q4, acc); break;
+          default: red_add<24, 8>(s2 + 2 * 8192, r16, q4, acc); break;
+        }
       } else {                                  // TG == 2, RB == 2
-        if (tg == 1) merge_put(red, rb, r16, q4, acc);
+        float* redf = reinterpret_cast<float*>(red);
+        if (tg == 1) merge_put(redf, rb, r16, q4, acc);
         lds_barrier_keep_loads();
-        if (tg == 0) merge_add(red, rb, r16, q4, acc);
+        if (tg == 0) merge_add(redf, rb, r16, q4, acc);
       }
       lds_barrier_keep_loads();                            // scratch free again before the next page lands
     }
 
-    if (tg == 0 && row_ok) {
+    // the rows' dims [16 D0, 16 (D0 + N)) (acc[D0 .. D0 + N)): 4 waves write a quarter each
+    // after the four-way merge, else the waves of token group 0 write all of them
+    auto store = [&](auto d0_c, auto n_c) {
+      constexpr int D0 = decltype(d0_c)::value, N = decltype(n_c)::value;
       const bool ok = !bad;
       const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
       float lse = (l_row > 0.f) ? (m_fin + __log2f(l_row)) * kLn2 : kNegInf;
       if (!ok) lse = __builtin_nanf("");
+      const bool lse_lane = q4 == 0 && (TG < 4 || wave == 0);
       if (nsplit == 1) {
         uint16_t* orow = p.o + ((static_cast<int64_t>(b) * p.s_q + s_idx) * p.h_q + head) * kDv + 4 * q4;
         const float nan = __builtin_nanf("");
 #pragma unroll
-        for (int d = 0; d < 32; ++d) {
+        for (int d = D0; d < D0 + N; ++d) {
           u32x2 w;
           const float x0 = ok ? acc[d][0] * inv : nan;
           const float x1 = ok ? acc[d][1] * inv : nan;
@@ -681,20 +729,32 @@ __global__ void __launch_bounds__(kThreads) splitkv_kernel(DecodeParams p) {
           w[1] = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
           *reinterpret_cast<u32x2*>(orow + 16 * d) = w;
         }
-        if (q4 == 0) p.lse[lse_index(p, b, head, s_idx)] = lse;
+        if (lse_lane) p.lse[lse_index(p, b, head, s_idx)] = lse;
       } else {
         const int pslot = slot0 + split_idx;
         if (pslot >= 0 && pslot < p.max_slots && split_idx < nsplit) {
           float* prow = p.part_o32 + ((static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row) * kDv + 4 * q4;
           const float nan = __builtin_nanf("");
 #pragma unroll
-          for (int d = 0; d < 32; ++d) {
+          for (int d = D0; d < D0 + N; ++d) {
             f32x4 v = acc[d] * inv;
             if (!ok) v = f32x4{nan, nan, nan, nan};
             *reinterpret_cast<f32x4*>(prow + 16 * d) = v;
           }
-          if (q4 == 0) p.part_lse[(static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row] = lse;
+          if (lse_lane) p.part_lse[(static_cast<int64_t>(pslot) * p.h_kv + kvh) * p.rows + row] = lse;
         }
+      }
+    };
+    if (row_ok) {
+      if constexpr (TG == 4) {
+        switch (wave) {
+          case 0: store(std::integral_constant<int, 0>{}, std::integral_constant<int, 8>{}); break;
+          case 1: store(std::integral_constant<int, 8>{}, std::integral_constant<int, 8>{}); break;
+          case 2: store(std::integral_constant<int, 16>{}, std::integral_constant<int, 8>{}); break;
+          default: store(std::integral_constant<int, 24>{}, std::integral_constant<int, 8>{}); break;
+        }
+      } else if (tg == 0) {
+        store(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{});
       }
     }
   }
