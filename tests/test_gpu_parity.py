@@ -164,6 +164,11 @@ MANY = [
     ("many_rows128_causal", 3, 2, 64, 1, [5000, 64, 2000], True, "bf16", 300, 65),
     ("many_fp8_rows16", 2, 1, 16, 1, [6000, 100], False, "fp8", 256, 65),
     ("many_fp8_rows128", 2, 1, 128, 1, [4100, 700], False, "fp8", 256, 65),
+    # a partial 128-row tile (fp16 partials) whose last row pair holds one row
+    ("many_rows75", 2, 1, 75, 1, [5000, 700], False, "bf16", 256, 65),
+    ("many_fp8_rows75_causal", 2, 3, 25, 1, [4300, 900], True, "fp8", 256, 65),
+    ("many_hkv2_rows128", 2, 1, 256, 2, [4500, 300], False, "bf16", 256, 65),
+    ("many_fp8_hkv2_rows64", 2, 1, 128, 2, [4200, 500], False, "fp8", 256, 65),
 ]
 
 
