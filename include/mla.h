@@ -217,12 +217,13 @@ typedef struct mla_decode_args {
 
   /* Optional hint: 0 = unknown, else the largest number of pieces of any
      sequence (max_b num_splits[b+1] - num_splits[b]). It selects the combine
-     kernel's shape: when some sequence has more than 8 pieces, extra
-     workgroups find those sequences on the device and merge them in small
-     slices, 64 pieces per round of loads. That changes the order in which
-     such a sequence's pieces are merged, so results for different hints agree
-     to rounding, not bit for bit; any hint gives correct results, and the same
-     hint always gives the same bits. */
+     kernel's shape: when some sequence has more than 8 pieces (for tiles of at
+     most 64 rows also when the hint is 0), extra workgroups find those
+     sequences on the device and merge them in small slices, 64 pieces per
+     round of loads. That changes the order in which such a sequence's pieces
+     are merged, so results for different hints agree to rounding, not bit for
+     bit; any hint gives correct results, and the same hint always gives the
+     same bits. */
   int max_splits;
 
   /* Optional timing hooks (hipEvent_t or NULL): events[0] and events[1] take

@@ -1305,9 +1305,11 @@ hipError_t launch_decode(const DecodeParams& p, const Plan& plan, int kv_format,
   {
     const dim3 cgrid(p.batch, (p.rows + 15) / 16, p.h_kv * (kDv / kCombDims));
     // some sequence cut into more than kFewPieces pieces (the host metadata's largest piece
-    // count): helper workgroups for those. At most (ranges - 1) / kFewPieces sequences have
-    // that many pieces (each piece past a sequence's first starts a range).
-    const bool many = p.max_splits > kFewPieces;
+    // count), or that count unknown (metadata built on the device) with fp32 partials: helper
+    // workgroups for those sequences (with none, they only read num_splits). At most
+    // (ranges - 1) / kFewPieces sequences have that many pieces (each piece past a sequence's
+    // first starts a range).
+    const bool many = p.max_splits > kFewPieces || (p.max_splits == 0 && !plan.wide);
     const int64_t per_quarters = static_cast<int64_t>(p.batch) * ((p.rows + 15) / 16) * p.h_kv * (kDv / kCombDims);
     const int64_t helper_tasks = static_cast<int64_t>(std::max(1, (p.grid_wgs - 1) / kFewPieces)) *
                                  ((p.rows + kListRows - 1) / kListRows) * p.h_kv * (kDv / kListDims);

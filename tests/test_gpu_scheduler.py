@@ -90,3 +90,31 @@ def test_device_metadata_for_lengths_past_its_limit_is_empty():
     torch.cuda.synchronize()
     md, sd = md.cpu(), sd.cpu()
     assert torch.all(md[:, 0] == -1) and torch.all(md[:, 6] == 3) and torch.all(sd == 0)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_unknown_piece_count_hint(fmt):
+    """max_splits = 0 (the piece count is not known on the host, as with device-built metadata):
+    tiles of at most 64 rows take the combine with helper workgroups, so a sequence of many
+    pieces is merged in one round of loads; sequences of at most 8 pieces give the same bits as
+    with the hint, and every sequence matches the oracle."""
+    import oracle
+    import paged_mla_decode_amd as mla
+    w = make_workload(name="hint0", batch=5, s_q=1, h_q=16, seqlens=[6000, 300, 40, 900, 2500], kv_format=fmt,
+                      seed=91)
+    q, kv, bt, L = w.q.to(DEV), w.kvcache.to(DEV), w.block_table.to(DEV), w.cache_seqlens.to(DEV)
+    mh, sh = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, 1, kv_format=fmt, num_parts=256)
+    n = np.diff(sh.cpu().numpy())
+    assert n.max() > 8 and (n <= 8).any(), n
+    hint = int(getattr(sh, "_mla_max_splits", 0))
+    o1, l1 = mla.MlaDecoder(q, kv, bt, L, 512, mh, sh, w.causal, max_splits=hint).run()
+    o0, l0 = mla.MlaDecoder(q, kv, bt, L, 512, mh, sh, w.causal, max_splits=0).run()
+    torch.cuda.synchronize()
+    few = [b for b in range(w.batch) if n[b] <= 8]
+    assert torch.equal(o0[few], o1[few]) and torch.equal(l0[few], l1[few])
+    O_ref, L_ref = oracle.mla_decode_workload(w)
+    O = o0.float().cpu().numpy().astype(np.float64)
+    LS = l0.cpu().numpy().astype(np.float64)
+    tol = 1e-2 if fmt == "bf16" else 3e-2
+    assert np.all(np.isfinite(O)) and float(np.max(np.abs(O - O_ref))) <= tol
+    assert float(np.max(np.abs(LS - L_ref))) <= 1e-3
