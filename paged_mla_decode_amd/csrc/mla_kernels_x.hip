@@ -465,40 +465,56 @@ __device__ __forceinline__ void f8_s(const uint8_t* __restrict__ page, uint8_t* 
     return i32x8{static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3]),
                  static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]), static_cast<int>(b[3])};
   };
-  // RoPE part (bf16 MFMA): K dims 512 + 32 c + 8 q4 .. = RoPE chunk 4 c + q4
+  // RoPE part (bf16 MFMA): K dims 512 + 32 c + 8 q4 .. = RoPE chunk 4 c + q4.
+  // Its operands and those of the first latent step are read up front; the
+  // latent part then runs in 8 steps (group g, token tile tt), each step's
+  // MFMAs covering the reads of the next step's K codes (and, before a group's
+  // first step, of the group's lo codes of Q), so that a wait for one step's
+  // operands leaves the next step's reads in flight.
+  bf16x8 qr[2], kr[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) qr[c] = *reinterpret_cast<const bf16x8*>(lds + X::kQrope + qrope_off(R, 4 * c + q4));
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) kr[tt][c] = *reinterpret_cast<const bf16x8*>(page + X::kRope + ln.k_off[c] + 2048 * tt);
+  i32x8 kc[2], ql[2];
+  kc[0] = kcodes(0, 0);
+  ql[0] = qlo_op(0);
   f32x4 s[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(page + X::kRope + ln.k_off[c] + 2048 * tt);
-      const bf16x8 qr = *reinterpret_cast<const bf16x8*>(lds + X::kQrope + qrope_off(R, 4 * c + q4));
-      s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, qr, s[tt], 0, 0, 0);
-    }
+    for (int c = 0; c < 2; ++c) s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[tt][c], qr[c], s[tt], 0, 0, 0);
   }
   // latent groups: hi and lo MFMAs into one partial per token tile, then the
-  // group's fp32 scales of tokens 16 tt + 4 q4 + i (scales are [group][token])
+  // group's fp32 scales of tokens 16 tt + 4 q4 + i (scales are [group][token];
+  // read at the group's second step, before that step's operand reads)
   auto scales4 = [&](int g, int tt) -> f32x4 {
     return *reinterpret_cast<const f32x4*>(page + X::kScales + 4 * (kXHalf * g + 16 * tt + 4 * q4));
   };
+  f32x4 part[2], sg[2];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const i32x8 ql = qlo_op(g);
-    f32x4 part[2];
+  for (int st = 0; st < 8; ++st) {
+    const int g = st >> 1, tt = st & 1;
+    if (tt == 1) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const i32x8 kc = kcodes(g, tt);
-      part[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, q.hi[g], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                                  kE8M0One, 0, q.scale_hi);
-      part[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, ql, part[tt], 0, 0, 0, kE8M0One, 0,
-                                                                  q.scale_lo);
+      for (int t2 = 0; t2 < 2; ++t2) sg[t2] = scales4(g, t2);
     }
+    if (st + 1 < 8) {
+      kc[(st + 1) & 1] = kcodes((st + 1) >> 1, (st + 1) & 1);
+      if (tt == 1) ql[(g + 1) & 1] = qlo_op(g + 1);
+    }
+    part[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc[st & 1], q.hi[g], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                0, kE8M0One, 0, q.scale_hi);
+    part[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc[st & 1], ql[g & 1], part[tt], 0, 0, 0, kE8M0One, 0,
+                                                                q.scale_lo);
+    if (tt == 1) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const f32x4 sg = scales4(g, tt);
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[tt][i] += sg[i] * part[tt][i];
+        for (int i = 0; i < 4; ++i) s[t2][i] += sg[t2][i] * part[t2][i];
     }
   }
 
@@ -583,16 +599,21 @@ __device__ __forceinline__ void f8_pv(const uint8_t* __restrict__ page, uint8_t*
   // P^T operand -- so byte j takes this lane's pv_scale[j].
   const int jj = r16 >> 1, hsel = r16 & 1;
   const int tok = (jj < 4) ? 4 * q4 + jj : 16 + 4 * q4 + (jj - 4);
-  bf16x8 va[4];
+  // all four transposing reads are issued before the first conversion waits
+  i32x2 w[4];
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd) {
     const int c = 4 * wave + dd;                    // 16-dim code chunk of dims 64 w + 16 dd
     const uint8_t* a0 = page + X::kCodes + xk_off(tok, c) + 8 * hsel;
-    const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, a0));
+    w[dd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, a0));
+  }
+  bf16x8 va[4];
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w[h2], false);
-      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w[h2], true);
+      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w[dd][h2], false);
+      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w[dd][h2], true);
       va[dd][4 * h2 + 0] = static_cast<__bf16>(f01[0] * pv_scale[4 * h2 + 0]);
       va[dd][4 * h2 + 1] = static_cast<__bf16>(f01[1] * pv_scale[4 * h2 + 1]);
       va[dd][4 * h2 + 2] = static_cast<__bf16>(f23[0] * pv_scale[4 * h2 + 2]);
