@@ -15,12 +15,18 @@
 // needs never grows with it, and each range advances at least Bd - split_cost:
 // the smallest budget that places all the work in P ranges -- what the host's
 // binary search finds -- lies in [ceil(W / P), ceil(W / P) + split_cost],
-// W = S_batch. One wavefront per candidate walks the ranges (the sequence
-// holding E found by a ballot over the prefix sums); the rows, their first
-// piece indices, the piece counts and the checksums then follow from the range
-// starts in parallel. (The tile scheduler of the wmrh.cn FlashMLA深度解析
-// page, "计算流水线设计", spreads requests and blocks over the SMs; this
-// cost model and layout are this library's own.)
+// W = S_batch. Between snaps the walk is arithmetic: from a sequence start S_e
+// the range starts are S_e + k (Bd - split_cost) until a range end falls
+// within split_cost of a later sequence start S_a, where the walk snaps to
+// S_a. So, per candidate budget, every sequence start gets its run (the number
+// of range starts before the next snap, and the sequence it snaps to) in
+// parallel; the number of ranges is the sum of the runs along the chain of
+// snaps from sequence 0, found by pointer jumping; and once the budget is
+// chosen, every range start follows at once by binary lifting over that chain.
+// The rows, their first piece indices, the piece counts and the checksums then
+// follow from the range starts in parallel. (The tile scheduler of the wmrh.cn
+// FlashMLA深度解析 page, "计算流水线设计", spreads requests and blocks over
+// the SMs; this cost model and layout are this library's own.)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -32,21 +38,33 @@ namespace {
 
 constexpr int kSchedThreads = 1024;                 // 16 wavefronts
 constexpr int kSchedWaves = kSchedThreads / 64;
-constexpr int kSchedMaxBatch = 1023;                // prefix sums S[0..batch] in 16 chunks of 64 lanes
+constexpr int kSchedMaxBatch = 1023;                // one sequence per thread; node indices fit 11 bits
 constexpr int kSchedMaxParts = 1024;
-constexpr int kSchedChunks = (kSchedMaxBatch + 1) / 64;
 constexpr int kSchedMaxPages = 1 << 20;             // per sequence
 
-constexpr int kSnapTable = 1 << 16;                 // cost-line positions the snap table covers
+constexpr int kSchedNodes = kSchedMaxBatch + 1;    // sequence starts 0..batch-1 and the end (batch)
+constexpr int kSchedLevels = 11;                    // lifting levels: 2^10 >= kSchedNodes - 1 snaps
+// A jump word: (ranges up to the target, saturated at kJumpSat) << 11 | target node. Saturation
+// only marks a budget as infeasible: every count that matters is at most num_parts <= 1024.
+constexpr uint32_t kJumpSat = (1u << 21) - 1;
+__device__ __forceinline__ uint32_t jump_word(uint32_t ranges, uint32_t target) {
+  return (ranges < kJumpSat ? ranges : kJumpSat) << 11 | target;
+}
 
 struct SchedShared {
-  uint8_t snap[kSnapTable];                         // x - S_b if x in [S_b, S_b + split_cost] (b holding x), else 255
   int32_t npages[kSchedMaxBatch];
   int32_t S[kSchedMaxBatch + 1];                    // cost-line start of each sequence; S[batch] = W
-  int32_t V[kSchedWaves][kSchedMaxParts + 1];       // range starts of each candidate budget, then W
   int32_t scan[kSchedThreads];
-  int32_t ok[kSchedWaves];
-  int32_t nranges[kSchedWaves];
+  int32_t nranges[kSchedWaves];                     // ranges each candidate budget needs
+  int32_t V[kSchedMaxParts + 1];                    // range starts of the chosen budget, then W
+  uint32_t run0[kSchedWaves][kSchedNodes];          // per candidate: each sequence start's run (jump word)
+  union {
+    uint32_t jump[kSchedWaves][kSchedNodes];        // per candidate: pointer jumping over the runs
+    struct {
+      int16_t up[kSchedLevels][kSchedNodes];        // the node 2^k snaps ahead (batch: the end)
+      int32_t cnt[kSchedLevels][kSchedNodes];       // ranges from a node up to that one
+    } lift;
+  };
 };
 
 // Inclusive scan of one value per thread (every thread of the workgroup calls
@@ -73,79 +91,72 @@ __device__ __forceinline__ int block_scan(int32_t* buf, int x) {
   return before + x;
 }
 
-// The same walk with the snap table (cost lines of up to kSnapTable
-// positions), one candidate budget per lane of wavefront 0: lane c walks
-// budget lo + c with its own LDS byte reads, so all candidates advance
-// together and a step is one LDS read and a few vector instructions.
-__device__ __forceinline__ void walk_candidates_table(SchedShared& sh, int W, int lo, int split_cost, int num_parts) {
-  const int lane = threadIdx.x & 63;
-  if (lane > split_cost) return;
-  const int bd = lo + lane;
-  int32_t* vout = sh.V[lane];
-  int v = 0, p = 0;
-  bool ok = bd > split_cost;
-  while (ok && v < W) {
-    if (p == num_parts) {
-      ok = false;
-      break;
-    }
-    const int E = v + bd;
-    const int d = sh.snap[E < W ? E : 0];           // issued before the store below: they overlap
-    vout[p] = v;
-    const int nv = E >= W ? W : (d <= split_cost ? E - d : E - split_cost);
-    if (nv <= v) {
-      ok = false;
-      break;
-    }
-    v = nv;
-    ++p;
+// max { b < batch : S[b] <= x } for x in [S[lo], W), searching b in [lo, batch - 1]
+__device__ __forceinline__ int seq_holding(const int32_t* S, int batch, int lo, int x) {
+  int a = lo, z = batch - 1;
+  while (a < z) {
+    const int m = (a + z + 1) >> 1;
+    if (S[m] <= x) a = m; else z = m - 1;
   }
-  sh.ok[lane] = ok ? 1 : 0;
-  sh.nranges[lane] = p;
-  vout[p] = W;
+  return a;
 }
 
-template <int NC>
-__device__ __forceinline__ void walk_candidate(SchedShared& sh, int batch, int W, int bd, int split_cost,
-                                               int num_parts) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int32_t sreg[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int i = 64 * c + lane;
-    sreg[c] = i <= batch ? sh.S[i] : 0x7FFFFFFF;
+// floor(x / d) for 0 <= x < 2^31, 1 <= d < 2^30, from a float reciprocal estimate
+// made exact by correction steps (unsigned products stay below 2^32)
+__device__ __forceinline__ uint32_t div_floor(uint32_t x, uint32_t d, float inv_d) {
+  uint32_t q = static_cast<uint32_t>(static_cast<float>(x) * inv_d);
+  while (q > 0 && q * d > x) --q;
+  while ((q + 1) * d <= x) ++q;
+  return q;
+}
+
+// The run of budget bd from the start of sequence e: K range starts S_e + k step
+// (step = bd - split_cost, k < K), then the snap to the start of sequence nx, or
+// the end of the work (nx = batch). e = batch (the end): no range.
+__device__ __forceinline__ void run_of(const int32_t* S, int batch, int W, int bd, int split_cost, int e, int& K,
+                                       int& nx) {
+  K = 0;
+  nx = batch;
+  if (e >= batch) return;
+  const int step = bd - split_cost;
+  const float inv_step = 1.f / static_cast<float>(step);
+  const int E0 = S[e] + bd;                         // end of the run's first range
+  if (E0 >= W) {
+    K = 1;
+    return;
   }
-  bd = __builtin_amdgcn_readfirstlane(bd);
-  int32_t* vout = sh.V[wave];
-  int v = 0, p = 0;
-  bool ok = bd > split_cost;
-  while (ok && v < W) {
-    if (p == num_parts) {
-      ok = false;
-      break;
+  int a = seq_holding(S, batch, e, E0);
+  // region [sa, sa1) of sequence a holds E; sa2 is the boundary after it, read one step early
+  // (S[batch] = W closes the last region)
+  int sa = S[a], sa1 = S[a + 1], sa2 = S[min(a + 2, batch)];
+  int k = 0, E = E0;
+  for (;;) {
+    if (E - sa <= split_cost) {                     // the range ends too close to S_a: snap there
+      K = k + 1;
+      nx = a;
+      return;
     }
-    if (lane == 0) vout[p] = v;
-    const int E = v + bd;
-    int nv = E - split_cost;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64(sreg[c] >= E - split_cost && sreg[c] <= E);
-      const int idx = __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m | 1));
-      const int sv = __builtin_amdgcn_readlane(sreg[c], idx);
-      nv = m != 0 ? sv : nv;
+    // the first range whose end reaches sa1 (the next sequence start, or the end)
+    k += 1 + static_cast<int>(div_floor(static_cast<uint32_t>(sa1 - E - 1), static_cast<uint32_t>(step), inv_step));
+    E = E0 + k * step;
+    if (E >= W) {
+      K = k + 1;
+      return;
     }
-    nv = __builtin_amdgcn_readfirstlane(E >= W ? W : nv);
-    if (nv <= v) {                                // no progress (cannot happen when bd > split_cost)
-      ok = false;
-      break;
+    // the sequence holding E: step ahead a few regions, then search
+    int guard = 0;
+    do {
+      ++a;
+      sa = sa1;
+      sa1 = sa2;
+      sa2 = S[min(a + 2, batch)];
+    } while (sa1 <= E && ++guard < 4);
+    if (sa1 <= E) {
+      a = seq_holding(S, batch, a, E);
+      sa = S[a];
+      sa1 = S[a + 1];
+      sa2 = S[min(a + 2, batch)];
     }
-    v = nv;
-    ++p;
-  }
-  if (lane == 0) {
-    sh.ok[wave] = ok ? 1 : 0;
-    sh.nranges[wave] = p;
-    vout[p] = W;
   }
 }
 
@@ -186,31 +197,83 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(const int32_t* 
   const int W = sh.S[batch];
   const int lo = max(1, (W + num_parts - 1) / num_parts);
 
-  // ---- the snap table (short cost lines): positions within split_cost of a sequence start ----
-  const bool table = W <= kSnapTable;
-  if (table) {
-    for (int x = tid; x < W; x += kSchedThreads) sh.snap[x] = 255;
-    __syncthreads();
-    if (tid < batch) {
-      const int s0 = sh.S[tid], s1 = min(s0 + split_cost, sh.S[tid + 1] - 1);
-      for (int x = s0; x <= s1; ++x) sh.snap[x] = static_cast<uint8_t>(x - s0);
-    }
-    __syncthreads();
+  const int lane = tid & 63;
+  const int nodes = batch + 1;                      // the sequence starts and the end (node batch)
+
+  // ---- per candidate budget: the runs of every sequence start (all (candidate, sequence)
+  // pairs spread over the workgroup), then the ranges it needs -------------------------------
+  const int ncand = split_cost + 1;
+  for (int pr = tid; pr < ncand * nodes; pr += kSchedThreads) {
+    const int cc = pr / nodes, e = pr - cc * nodes;
+    const int bd = lo + cc;
+    int K = 0, nx = batch;
+    if (bd > split_cost) run_of(sh.S, batch, W, bd, split_cost, e, K, nx);
+    const uint32_t w = jump_word(static_cast<uint32_t>(K), static_cast<uint32_t>(nx));
+    sh.run0[cc][e] = w;
+    sh.jump[cc][e] = w;
   }
-  // ---- one candidate budget per wavefront: its range starts, and whether they place all ----
-  if (table) {
-    if (wave == 0) walk_candidates_table(sh, W, lo, split_cost, num_parts);
-  } else if (wave <= split_cost) {
-    if (batch < 4 * 64)
-      walk_candidate<4>(sh, batch, W, lo + wave, split_cost, num_parts);
-    else
-      walk_candidate<kSchedChunks>(sh, batch, W, lo + wave, split_cost, num_parts);
+  __syncthreads();
+  // Pointer jumping in place, one wavefront per candidate: a node's jump word is read and written
+  // whole, so every word is a valid jump at any time and the wavefront needs no barrier; a round
+  // at least doubles every jump, and no chain has more than batch snaps.
+  if (wave <= split_cost) {
+    const int bd = lo + wave;
+    uint32_t* const jw = sh.jump[wave];
+    int need = 0x7FFFFFFF;
+    if (bd > split_cost) {
+      for (int r = 0; (1 << r) <= batch; ++r)
+        for (int e = lane; e < nodes; e += 64) {
+          const uint32_t w = jw[e];
+          const uint32_t t = w & 2047u;
+          if (t != static_cast<uint32_t>(batch)) {
+            const uint32_t w2 = jw[t];
+            jw[e] = jump_word((w >> 11) + (w2 >> 11), w2 & 2047u);
+          }
+        }
+      const uint32_t w0 = jw[0];
+      if ((w0 & 2047u) == static_cast<uint32_t>(batch) && (w0 >> 11) < kJumpSat) need = static_cast<int>(w0 >> 11);
+    }
+    if (lane == 0) sh.nranges[wave] = need;
   }
   __syncthreads();
   int c = 0;
-  while (c < split_cost && sh.ok[c] == 0) ++c;      // c = split_cost is always feasible
-  const int32_t* V = sh.V[c];
-  const int n = sh.nranges[c];
+  while (c < split_cost && sh.nranges[c] > num_parts) ++c;   // c = split_cost is always feasible
+  const int step = lo + c - split_cost;
+  const int n = min(sh.nranges[c], num_parts);
+
+  // ---- the chosen budget: lifting tables over its chain of snaps, then every range start ----
+  // (a node's ranges to the end never exceed those from sequence 0: the walk is monotone)
+  int levels = 1;
+  while ((1 << levels) - 1 < batch) ++levels;       // 2^levels - 1 >= the snaps on the chain
+  for (int e = tid; e < nodes; e += kSchedThreads) {   // (every wavefront is past its jumping)
+    const uint32_t w = sh.run0[c][e];
+    sh.lift.up[0][e] = static_cast<int16_t>(w & 2047u);
+    sh.lift.cnt[0][e] = static_cast<int32_t>(w >> 11);
+  }
+  __syncthreads();
+  for (int k = 0; k + 1 < levels; ++k) {
+    for (int e = tid; e < nodes; e += kSchedThreads) {
+      const int u = sh.lift.up[k][e];
+      sh.lift.up[k + 1][e] = sh.lift.up[k][u];
+      sh.lift.cnt[k + 1][e] = sh.lift.cnt[k][e] + sh.lift.cnt[k][u];
+    }
+    __syncthreads();
+  }
+  for (int q = tid; q < n; q += kSchedThreads) {    // range q: in the run of the last chain node
+    int cur = 0, acc = 0;                           // whose first range is at or before q
+    for (int k = levels - 1; k >= 0; --k) {
+      const int u = sh.lift.up[k][cur];
+      const int cn = sh.lift.cnt[k][cur];
+      if (u != batch && acc + cn <= q) {
+        acc += cn;
+        cur = u;
+      }
+    }
+    sh.V[q] = sh.S[cur] + (q - acc) * step;
+  }
+  if (tid == 0) sh.V[n] = W;
+  __syncthreads();
+  const int32_t* V = sh.V;
 
   auto count_le = [&](int x) {                      // #{q in [0, n) : V[q] <= x}
     int a = 0, z = n;

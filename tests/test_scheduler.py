@@ -181,11 +181,13 @@ def test_lengths_beyond_the_block_table_are_rejected():
 
 
 def cost_line_schedule(L, split_cost, parts):
-    """The device scheduler's algorithm (scheduler_device.hip), in plain Python: on the cost
-    line where sequence b spans [S_b, S_b+1) with S_b+1 - S_b = split_cost + pages_b, a range
-    starting at V ends at E = V + budget and the next one starts at S_e if E - S_e <= split_cost
-    (e: the sequence holding E), else at E - split_cost; the budget is the smallest in
-    [ceil(W / P), ceil(W / P) + split_cost] that places all the work."""
+    """The cost-line form of the greedy fill that the device scheduler (scheduler_device.hip)
+    builds on, in plain Python: on the cost line where sequence b spans [S_b, S_b+1) with
+    S_b+1 - S_b = split_cost + pages_b, a range starting at V ends at E = V + budget and the next
+    one starts at S_e if E - S_e <= split_cost (e: the sequence holding E), else at
+    E - split_cost; the budget is the smallest in [ceil(W / P), ceil(W / P) + split_cost] that
+    places all the work. The device computes the same range starts in parallel
+    (parallel_range_starts below); the rows, piece indices and counts follow as here."""
     import bisect
     B = len(L)
     npg = [(int(x) + 63) // 64 for x in L]
@@ -256,3 +258,121 @@ def test_cost_line_algorithm_matches_the_greedy_scheduler():
         meta, splits = schedule(L, M=M, parts=P)
         m2, s2 = cost_line_schedule(L, 8 if M > 64 else 3, P)
         assert np.array_equal(meta, m2) and np.array_equal(splits, s2), (B, M, P)
+
+
+def run_table(S, W, bd, split_cost):
+    """Runs of the cost-line walk with budget bd (the device scheduler's first step): from the
+    start S_e of sequence e the range starts are S_e + k (bd - split_cost) until the end E of a
+    range falls within split_cost of a later sequence start S_a (the walk snaps to S_a: the next
+    run starts there) or reaches W. Returns, per sequence e, the number of range starts of the run
+    and the sequence it snaps to (len(S) - 1 = the end)."""
+    B = len(S) - 1
+    step = bd - split_cost
+    K, nx = [0] * (B + 1), [B] * (B + 1)
+    for e in range(B):
+        E0 = S[e] + bd
+        if E0 >= W:
+            K[e], nx[e] = 1, B
+            continue
+        a = e
+        while a + 1 < B and S[a + 1] <= E0:
+            a += 1
+        k, E = 0, E0
+        while True:
+            if E - S[a] <= split_cost:                   # snap to the start of sequence a
+                K[e], nx[e] = k + 1, a
+                break
+            target = S[a + 1] if a + 1 < B else W        # the next start (or the end)
+            k = k + 1 + (target - E - 1) // step         # first k with E0 + k step >= target
+            E = E0 + k * step
+            if E >= W:
+                K[e], nx[e] = k + 1, B
+                break
+            a += 1
+            while a + 1 < B and S[a + 1] <= E:
+                a += 1
+    return K, nx
+
+
+def parallel_range_starts(L, split_cost, parts):
+    """The device scheduler's formulation: per candidate budget, the runs, then the number of
+    ranges as the sum of the run lengths along the chain of snaps from sequence 0 (pointer
+    jumping); the smallest feasible budget; then every range start at once by binary lifting
+    over the chain (range p lies in the run of the last chain node whose first range <= p)."""
+    B = len(L)
+    npg = [(int(x) + 63) // 64 for x in L]
+    S = [0]
+    for n in npg:
+        S.append(S[-1] + split_cost + n)
+    W = S[-1]
+    lo = max(1, -(-W // parts))
+    for c in range(split_cost + 1):
+        bd = lo + c
+        if bd <= split_cost:
+            continue
+        K, nx = run_table(S, W, bd, split_cost)
+        nxt, tot = list(nx), list(K)
+        for _ in range(max(1, B.bit_length()) + 1):      # pointer jumping: tot[e] = ranges from e to the end
+            nxt, tot = [nxt[nxt[e]] for e in range(B + 1)], [tot[e] + tot[nxt[e]] for e in range(B + 1)]
+        if tot[0] <= parts:
+            break
+    n = tot[0]
+    up, cnt = [list(nx)], [list(K)]                      # lifting tables: 2^k snaps ahead, ranges covered
+    for _ in range(max(1, B.bit_length())):
+        u, t = up[-1], cnt[-1]
+        up.append([u[u[e]] for e in range(B + 1)])
+        cnt.append([t[e] + t[u[e]] for e in range(B + 1)])
+    V = []
+    for p in range(n):
+        cur, acc = 0, 0
+        for k in reversed(range(len(up))):
+            if up[k][cur] != B and acc + cnt[k][cur] <= p:
+                acc += cnt[k][cur]
+                cur = up[k][cur]
+        V.append(S[cur] + (p - acc) * (bd - split_cost))
+    return bd, V + [W]
+
+
+def test_parallel_formulation_matches_the_walk():
+    # the device scheduler's parallel form (runs, pointer jumping, lifting) gives the walk's ranges
+    import bisect
+    rng = np.random.default_rng(33)
+    for trial in range(400):
+        B = int(rng.integers(1, 300))
+        kind = trial % 4
+        if kind == 0:
+            L = rng.integers(0, 5000, size=B)
+        elif kind == 1:
+            L = rng.integers(0, 200, size=B)
+        elif kind == 2:
+            L = np.full(B, int(rng.integers(0, 9000)))
+        else:
+            L = rng.integers(256, 1025, size=B)
+            L[rng.integers(0, B)] = 32768
+        if rng.random() < 0.2:
+            L[rng.random(B) < 0.3] = 0
+        sc = int(rng.choice([1, 3, 8, 15]))
+        P = int(rng.choice([1, 2, 3, 7, 64, 128, 256, 1024]))
+        npg = [(int(x) + 63) // 64 for x in L]
+        S = [0]
+        for n in npg:
+            S.append(S[-1] + sc + n)
+        W = S[-1]
+        lo = max(1, -(-W // P))
+        for c in range(sc + 1):                          # the walk, as in cost_line_schedule
+            bd, v, V, ok = lo + c, 0, [], True
+            while v < W:
+                if len(V) == P or bd <= sc:
+                    ok = False
+                    break
+                V.append(v)
+                E = v + bd
+                if E >= W:
+                    v = W
+                else:
+                    e = bisect.bisect_right(S, E) - 1
+                    v = S[e] if E - S[e] <= sc else E - sc
+            if ok:
+                break
+        bd2, V2 = parallel_range_starts(L, sc, P)
+        assert (bd2, V2) == (bd, V + [W]), (trial, B, sc, P)
