@@ -81,6 +81,45 @@ def test_decode_with_device_metadata_is_bitwise_equal(name):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("h_kv", [2, 4])
+def test_device_metadata_equals_host_with_several_kv_heads(h_kv):
+    # with several KV heads the default range count shrinks (the grid holds every KV head of a
+    # range) and the runs of the device scheduler get longer
+    rng = np.random.default_rng(77 + h_kv)
+    for trial in range(40):
+        B = int(rng.integers(1, 400))
+        L = rng.integers(0, 6000, size=B) if trial % 2 == 0 else np.full(B, int(rng.integers(1, 9000)))
+        M = int(rng.choice([16, 64, 128, 256]))
+        fmt = "fp8" if trial % 3 == 0 else "bf16"
+        _same(L, M, h_kv, fmt, 0, f"h_kv={h_kv} trial {trial}: B={B} M={M} {fmt}")
+
+
+@pytest.mark.parametrize("fmt,h_q", [("bf16", 256), ("fp8", 32)])
+def test_decode_with_device_metadata_two_kv_heads(fmt, h_q):
+    # two KV heads (128 and 16 rows per head): the decode with device metadata gives the bits of
+    # the decode with host metadata, and matches the oracle
+    import oracle
+    import paged_mla_decode_amd as mla
+    w = make_workload(name="dev_hkv2", batch=6, s_q=1, h_q=h_q, h_kv=2, seqlens=[3000, 64, 1, 700, 5000, 129],
+                      kv_format=fmt, seed=17)
+    q, kv, bt, L = w.q.to(DEV), w.kvcache.to(DEV), w.block_table.to(DEV), w.cache_seqlens.to(DEV)
+    mh, sh = mla.mla_get_metadata(w.cache_seqlens, w.heads_per_kv, 2, kv_format=fmt, device=DEV)
+    md, sd = mla.mla_get_metadata_device(L, w.heads_per_kv, 2, kv_format=fmt)
+    hint = int(getattr(sh, "_mla_max_splits", 0))
+    o1, l1 = mla.MlaDecoder(q, kv, bt, L, 512, mh, sh, w.causal, max_splits=hint).run()
+    o2, l2 = mla.MlaDecoder(q, kv, bt, L, 512, md, sd, w.causal, max_splits=hint).run()
+    torch.cuda.synchronize()
+    print(f"[sched] dev_hkv2 {fmt} h_q={h_q}", flush=True)
+    assert torch.equal(md.cpu(), mh.cpu()) and torch.equal(sd.cpu(), sh.cpu())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    O_ref, L_ref = oracle.mla_decode_workload(w)
+    O = o2.float().cpu().numpy().astype(np.float64)
+    LS = l2.cpu().numpy().astype(np.float64)
+    tol = 1e-2 if fmt == "bf16" else 3e-2
+    assert np.all(np.isfinite(O)) and float(np.max(np.abs(O - O_ref))) <= tol
+    assert float(np.max(np.abs(LS - L_ref))) <= 1e-3
+
+
 def test_device_metadata_for_lengths_past_its_limit_is_empty():
     # more than 2^20 pages in one sequence: every range empty and no pieces (the decode then
     # reports every sequence as NaN) -- the host scheduler has no such limit
